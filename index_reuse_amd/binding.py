@@ -1,0 +1,274 @@
+"""ctypes binding of libsparse_attn.so.
+
+Argument marshalling only: tensors become device pointers inside the C
+descriptors of ``include/sparse_attn.h`` and every computation runs in the
+library's HIP kernels.  torch provides device memory and the current stream.
+There is no fallback: if the library is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
+
+SA_F32, SA_BF16, SA_FP8_E4M3, SA_FP4_E2M1 = 0, 1, 2, 3
+SA_OP_INDEX_SCORE, SA_OP_TOPK_SELECT, SA_OP_ATTN_GATHER_FWD = 0, 1, 2
+
+_P = ctypes.c_void_p
+_i32, _i64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+
+
+class sa_cache(ctypes.Structure):
+    _fields_ = [("data", _P), ("scale", _P), ("block_table", _P), ("page_size", _i32),
+                ("max_pages", _i32), ("heads", _i32), ("width", _i32), ("row_stride", _i64),
+                ("scale_stride", _i64), ("dtype", _i32), ("reserved", _i32)]
+
+
+class sa_rows(ctypes.Structure):
+    _fields_ = [("n_rows", _i32), ("n_seqs", _i32), ("seq_of_row", _P), ("pos_of_row", _P),
+                ("seq_len", _P), ("stride", _i32), ("window", _i32)]
+
+
+class sa_index_desc(ctypes.Structure):
+    _fields_ = [("rows", sa_rows), ("q", _P), ("w", _P), ("k", sa_cache), ("n_heads", _i32),
+                ("dim", _i32), ("cand", _P), ("cand_count", _P), ("cand_stride", _i32),
+                ("reserved", _i32), ("scores", _P), ("score_stride", _i64)]
+
+
+class sa_topk_desc(ctypes.Structure):
+    _fields_ = [("rows", sa_rows), ("scores", _P), ("score_stride", _i64), ("cand", _P),
+                ("cand_count", _P), ("cand_stride", _i32), ("k", _i32), ("idx", _P),
+                ("count", _P), ("idx_stride", _i32), ("block", _i32), ("max_blocks", _i32),
+                ("pool_stride", _i32), ("pool", _P), ("pool_count", _P)]
+
+
+class sa_attn_desc(ctypes.Structure):
+    _fields_ = [("rows", sa_rows), ("n_qsets", _i32), ("n_heads_q", _i32), ("q", _P),
+                ("q_dtype", _i32), ("d_v", _i32), ("k", sa_cache), ("v", sa_cache),
+                ("v_from_k", _i32), ("idx_stride", _i32), ("idx", _P), ("count", _P),
+                ("scale", _f32), ("o_dtype", _i32), ("o", _P), ("lse", _P)]
+
+
+EXPORTS = ("sparse_index_score", "sparse_topk_select", "sparse_attn_gather_fwd",
+           "sa_workspace_size", "sa_last_error", "sa_abi_version")
+
+_lib = None
+
+
+class SAError(RuntimeError):
+    pass
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (after torch, so that it binds to the HIP runtime
+    torch already mapped).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise SAError("libsparse_attn.so not built: run `python -m index_reuse_amd.build` "
+                      "(or __graft_entry__.build())")
+    L = ctypes.CDLL(path)
+    for name in ("sparse_index_score", "sparse_topk_select", "sparse_attn_gather_fwd"):
+        getattr(L, name).restype = _i32
+    L.sparse_index_score.argtypes = [ctypes.POINTER(sa_index_desc), _P, ctypes.c_size_t, _P]
+    L.sparse_topk_select.argtypes = [ctypes.POINTER(sa_topk_desc), _P, ctypes.c_size_t, _P]
+    L.sparse_attn_gather_fwd.argtypes = [ctypes.POINTER(sa_attn_desc), _P, ctypes.c_size_t, _P]
+    L.sa_workspace_size.restype = ctypes.c_size_t
+    L.sa_workspace_size.argtypes = [_i32, _P]
+    L.sa_last_error.restype = ctypes.c_char_p
+    L.sa_abi_version.restype = _i32
+    _lib = L
+    return L
+
+
+def abi_version() -> int:
+    return int(load().sa_abi_version())
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load().sa_last_error().decode(errors="replace")
+        raise SAError("status %d: %s" % (status, msg))
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SA_F32
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return SA_FP8_E4M3
+    raise SAError("unsupported dtype %s" % t.dtype)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# Python-side views of the descriptor parts
+# ---------------------------------------------------------------------------
+
+
+@dataclass
+class Rows:
+    seq_of_row: torch.Tensor  # int32 [R]
+    pos_of_row: torch.Tensor  # int32 [R]
+    seq_len: torch.Tensor     # int32 [B]
+    stride: int = 1
+    window: int = 0
+
+    def c(self) -> sa_rows:
+        return sa_rows(int(self.seq_of_row.numel()), int(self.seq_len.numel()),
+                       _ptr(self.seq_of_row), _ptr(self.pos_of_row), _ptr(self.seq_len),
+                       int(self.stride), int(self.window))
+
+
+@dataclass
+class Cache:
+    """A paged cache: ``pool`` is [n_pages, page_size, heads, width] (or
+    [n_seqs, cap, heads, width] with ``block_table=None``); FP4 pools hold
+    bytes [.., width/2] with ``scale`` [.., width/16]."""
+
+    pool: torch.Tensor
+    block_table: Optional[torch.Tensor]
+    heads: int
+    width: int
+    fp4: bool = False
+    scale: Optional[torch.Tensor] = None
+
+    def c(self) -> sa_cache:
+        p = self.pool
+        page_size = int(p.shape[1])
+        if self.block_table is not None:
+            max_pages = int(self.block_table.shape[1])
+        else:
+            max_pages = 1
+        row_stride = p.stride(1) * p.element_size()
+        dtype = SA_FP4_E2M1 if self.fp4 else _dt(p)
+        scale_stride = 0
+        if self.fp4:
+            scale_stride = self.scale.stride(1) * self.scale.element_size()
+        return sa_cache(_ptr(p), _ptr(self.scale), _ptr(self.block_table), page_size, max_pages,
+                        int(self.heads), int(self.width), row_stride, scale_stride, dtype, 0)
+
+
+def _cache_struct(c: Cache) -> sa_cache:
+    return c.c()
+
+
+_ws_cache = {}
+
+
+def workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    """A cached device workspace of at least ``nbytes`` bytes."""
+    if nbytes == 0:
+        return None
+    key = torch.device(device).index
+    t = _ws_cache.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _ws_cache[key] = t
+    return t
+
+
+# ---------------------------------------------------------------------------
+# Entry points
+# ---------------------------------------------------------------------------
+
+
+def index_desc(rows: Rows, q, w, k: Cache, scores, cand=None, cand_count=None) -> sa_index_desc:
+    return sa_index_desc(rows.c(), _ptr(q), _ptr(w), k.c(), int(q.shape[1]), int(q.shape[2]),
+                         _ptr(cand), _ptr(cand_count), 0 if cand is None else int(cand.stride(0)),
+                         0, _ptr(scores), int(scores.stride(0)))
+
+
+def index_score(rows: Rows, q: torch.Tensor, w: torch.Tensor, k: Cache,
+                scores: Optional[torch.Tensor] = None, n_slots: Optional[int] = None,
+                cand: Optional[torch.Tensor] = None, cand_count: Optional[torch.Tensor] = None):
+    """Indexer scores [R, S] float32 (see sparse_index_score)."""
+    L = load()
+    if scores is None:
+        S = int(cand.shape[1]) if cand is not None else int(n_slots)
+        scores = torch.empty(int(q.shape[0]), S, dtype=torch.float32, device=q.device)
+    d = index_desc(rows, q, w, k, scores, cand, cand_count)
+    _check(L.sparse_index_score(ctypes.byref(d), None, 0, _stream()))
+    return scores
+
+
+def topk_desc(rows: Rows, scores, k: int, idx, count, cand=None, cand_count=None, block=0,
+              max_blocks=0, pool=None, pool_count=None) -> sa_topk_desc:
+    return sa_topk_desc(rows.c(), _ptr(scores), int(scores.stride(0)), _ptr(cand), _ptr(cand_count),
+                        0 if cand is None else int(cand.stride(0)), int(k), _ptr(idx), _ptr(count),
+                        0 if idx is None else int(idx.stride(0)), int(block), int(max_blocks),
+                        0 if pool is None else int(pool.stride(0)), _ptr(pool), _ptr(pool_count))
+
+
+def topk_select(rows: Rows, scores: torch.Tensor, k: int, cand=None, cand_count=None,
+                block: int = 0, max_blocks: int = 0, idx=None, count=None, pool=None,
+                pool_count=None):
+    """Window + top-k (and optionally the block-max pool).  Returns
+    (idx, count) or (idx, count, pool, pool_count)."""
+    L = load()
+    R, dev = int(scores.shape[0]), scores.device
+    if k > 0 and idx is None:
+        idx = torch.empty(R, k, dtype=torch.int32, device=dev)
+        count = torch.empty(R, dtype=torch.int32, device=dev)
+    if block > 0 and pool is None:
+        pool = torch.empty(R, max_blocks * block, dtype=torch.int32, device=dev)
+        pool_count = torch.empty(R, dtype=torch.int32, device=dev)
+    d = topk_desc(rows, scores, k, idx, count, cand, cand_count, block, max_blocks, pool,
+                  pool_count)
+    _check(L.sparse_topk_select(ctypes.byref(d), None, 0, _stream()))
+    if block > 0:
+        return idx, count, pool, pool_count
+    return idx, count
+
+
+def attn_desc(rows: Rows, q, k: Cache, v: Optional[Cache], idx, count, o, lse=None,
+              scale: Optional[float] = None, d_v: Optional[int] = None) -> sa_attn_desc:
+    n_qsets, R, hq, dqk = (int(x) for x in q.shape)
+    if d_v is None:
+        d_v = v.width if v is not None else k.width
+    if scale is None:
+        scale = dqk ** -0.5
+    vc = v.c() if v is not None else sa_cache()
+    return sa_attn_desc(rows.c(), n_qsets, hq, _ptr(q), _dt(q), int(d_v), k.c(), vc,
+                        1 if v is None else 0, 0 if idx is None else int(idx.stride(0)), _ptr(idx),
+                        _ptr(count), float(scale), _dt(o), _ptr(o), _ptr(lse))
+
+
+def attn_gather_fwd(rows: Rows, q: torch.Tensor, k: Cache, v: Optional[Cache] = None,
+                    idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
+                    scale: Optional[float] = None, d_v: Optional[int] = None,
+                    o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    out_dtype=None, want_lse: bool = True):
+    """Joint-softmax gather attention.  ``v=None`` means V is the first d_v
+    channels of the K row.  Returns (o, lse)."""
+    L = load()
+    n_qsets, R, hq, dqk = (int(x) for x in q.shape)
+    if d_v is None:
+        d_v = v.width if v is not None else k.width
+    if o is None:
+        o = torch.empty(n_qsets, R, hq, d_v, dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(n_qsets, R, hq, dtype=torch.float32, device=q.device)
+    d = attn_desc(rows, q, k, v, idx, count, o, lse, scale, d_v)
+    need = int(L.sa_workspace_size(SA_OP_ATTN_GATHER_FWD, ctypes.byref(d)))
+    if need == ctypes.c_size_t(-1).value:
+        _check(-2)
+    ws = workspace(need, q.device)
+    _check(L.sparse_attn_gather_fwd(ctypes.byref(d), _ptr(ws), need, _stream()))
+    return o, lse

@@ -1,0 +1,508 @@
+// Gather attention with one joint softmax over the forced window plus the
+// selected entries, on gfx950.
+//
+// ("HySparse2", section 7.2: window and selected positions come from one KV
+// cache and share one softmax normalisation; section 5: the SA layers reuse
+// the FA layer's KV and indices with their own queries.  "Lecture 10",
+// section 5.1: in MQA mode one latent entry serves every query head, so a
+// gathered entry must be shared by all heads to be worth its bytes.)
+//
+// Work decomposition (BF16 / FP4 KV): one workgroup per (query row, KV head,
+// entry split, query-row tile group).  All query heads of the KV group and
+// all query sets are stacked into Mq = n_qsets * (Hq / Hkv) MFMA rows, so
+// every gathered K/V row is read from HBM once per call and reused by every
+// head and query set.  Per 32-entry tile:
+//   1. the workgroup gathers the 32 K (and V) rows through the block table
+//      into LDS (FP4 rows are dequantised exactly to bf16 on the way);
+//   2. each wave computes S^T = K . Q^T for its 16 query rows with
+//      v_mfma_f32_16x16x32_bf16 (entries on M, query rows on N), so each lane
+//      ends up holding 8 logits of ONE query row;
+//   3. online softmax in fp32 (exp2 domain), per query row;
+//   4. O += P . V with the contraction order permuted so that the lane's 8
+//      probabilities are directly its A operand; the V operand is built from
+//      16-byte LDS reads by an in-register 8x8 bf16 transpose (v_perm), with
+//      output columns interleaved so each lane owns 8 contiguous channels.
+// Long entry lists are split across workgroups; a combine kernel merges the
+// (max, sum, unnormalised O) partials.  F32 inputs use a plain VALU kernel.
+#include "kernels.hpp"
+
+namespace sa {
+
+namespace {
+
+constexpr int kTile = 32;   // entries per tile
+constexpr int kMaxW = 8;    // waves per workgroup (query-row tiles of 16)
+
+enum { KV_SEPARATE = 0, KV_SHARED = 1, KV_FP4 = 2 };
+
+__device__ __forceinline__ uint32_t lo16x2(uint32_t a, uint32_t b) {
+  return (a & 0xFFFFu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xFFFF0000u);
+}
+
+// Dequantise 32 FP4 channels (16 code bytes, 2 E4M3 scales) into 16 packed
+// bf16 pairs.  e2m1 * e4m3 has at most 6 significant bits, so the bf16 value
+// is exact and truncating the float is the exact conversion.
+__device__ __forceinline__ void fp4_dequant32(u32x4 codes, uint32_t s0, uint32_t s1,
+                                              uint32_t out[16]) {
+  const float f0 = e4m3_to_f32(s0), f1 = e4m3_to_f32(s1);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t word = codes[w];
+    const float sc = w < 2 ? f0 : f1;  // channels 8w..8w+7 -> scale (8w)/16
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t byte = (word >> (8 * p)) & 0xFFu;
+      const float lo = e2m1_to_f32(byte & 15u) * sc;
+      const float hi = e2m1_to_f32(byte >> 4) * sc;
+      out[w * 4 + p] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+    }
+  }
+}
+
+template <int DQK, int DV, int KV>
+struct AttnLds {
+  static constexpr int KROW = DQK + 8;  // bf16 elements per LDS row (padded)
+  static constexpr int VROW = DV + 8;
+  static constexpr bool HAS_V = KV == KV_SEPARATE;
+  uint16_t k[kTile * KROW];
+  uint16_t v[HAS_V ? kTile * VROW : 1];
+  int64_t slot[kTile];
+};
+
+template <int DQK, int DV, int KV>
+__global__ __launch_bounds__(64 * kMaxW) void attn_mfma(AttnArgs a, int per_split) {
+  using L = AttnLds<DQK, DV, KV>;
+  __shared__ __align__(16) L lds;
+  constexpr int KS = DQK / 32;           // k-steps of the S MFMA
+  constexpr int QV = DQK / 32;           // 16-byte q vectors per lane
+  constexpr int NJB = DV / 128;          // 128-channel blocks of V
+  constexpr int NT = DV / 16;            // N tiles of O
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int col = lane & 15, gq = lane >> 4;
+  const int sp = blockIdx.x;
+  const int r = blockIdx.y / a.hkv, g = blockIdx.y % a.hkv;
+  const int G = a.hq / a.hkv;
+  const int Mq = a.n_qsets * G;
+  const int qrow0 = (blockIdx.z * nw + wave) * 16;
+  const bool active = qrow0 < Mq;
+
+  const RowInfo ri = row_info(a.rows, r);
+  const int n_w = ri.n_avail - ri.win_lo;
+  const int cnt = (a.idx && ri.b >= 0) ? a.count[r] : 0;
+  const int n_e = ri.b < 0 ? 0 : n_w + cnt;
+  const int e0 = sp * per_split, e1 = min(n_e, e0 + per_split);
+  const int32_t* idx = a.idx ? a.idx + (int64_t)r * a.idx_stride : nullptr;
+
+  // Query rows of this wave as the B operand (query row = col).
+  u32x4 qv[QV];
+  {
+    const int qr = qrow0 + col;
+    if (active && qr < Mq) {
+      const int set = qr / G, h = g * G + qr % G;
+      const u32x4* qp = reinterpret_cast<const u32x4*>(
+          reinterpret_cast<const uint16_t*>(a.q) +
+          (((int64_t)set * a.rows.n_rows + r) * a.hq + h) * DQK + gq * (DQK / 4));
+#pragma unroll
+      for (int i = 0; i < QV; ++i) qv[i] = qp[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < QV; ++i) qv[i] = u32x4{0, 0, 0, 0};
+    }
+  }
+
+  f32x4 O[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_huge_valf(), l_run = 0.0f;
+
+  for (int tb = e0; tb < e1; tb += kTile) {
+    const int n_t = min(kTile, e1 - tb);
+    // 1. slots of this tile's entries
+    if (threadIdx.x < kTile) {
+      int64_t slot = -1;
+      const int i = tb + threadIdx.x;
+      if ((int)threadIdx.x < n_t) {
+        const int pos = i < n_w ? ri.win_lo + i : idx[i - n_w];
+        if (pos >= 0) slot = cache_slot(a.k, ri.b, pos);
+      }
+      lds.slot[threadIdx.x] = slot;
+    }
+    __syncthreads();
+    // 2. gather K (and V) rows into LDS
+    if constexpr (KV == KV_FP4) {
+      constexpr int CH = DQK / 32;  // 16-byte code chunks per row
+      for (int c = threadIdx.x; c < kTile * CH; c += blockDim.x) {
+        const int e = c / CH, part = c % CH;
+        const int64_t slot = lds.slot[e];
+        uint32_t vals[16];
+        if (slot >= 0) {
+          const u32x4 codes = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+              a.k.data + slot * a.k.row_stride + g * (DQK / 2) + part * 16));
+          const uint8_t* sp8 = a.k.scale + slot * a.k.scale_stride + g * (DQK / 16) + part * 2;
+          fp4_dequant32(codes, sp8[0], sp8[1], vals);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) vals[i] = 0u;
+        }
+        u32x4* dst = reinterpret_cast<u32x4*>(&lds.k[e * L::KROW + part * 32]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = u32x4{vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]};
+      }
+    } else {
+      constexpr int CH = DQK / 8;
+      for (int c = threadIdx.x; c < kTile * CH; c += blockDim.x) {
+        const int e = c / CH, part = c % CH;
+        const int64_t slot = lds.slot[e];
+        u32x4 val = u32x4{0, 0, 0, 0};
+        if (slot >= 0)
+          val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+              a.k.data + slot * a.k.row_stride + g * (DQK * 2) + part * 16));
+        *reinterpret_cast<u32x4*>(&lds.k[e * L::KROW + part * 8]) = val;
+      }
+      if constexpr (KV == KV_SEPARATE) {
+        constexpr int CV = DV / 8;
+        for (int c = threadIdx.x; c < kTile * CV; c += blockDim.x) {
+          const int e = c / CV, part = c % CV;
+          const int64_t slot = lds.slot[e];
+          u32x4 val = u32x4{0, 0, 0, 0};
+          if (slot >= 0)
+            val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                a.v.data + slot * a.v.row_stride + g * (DV * 2) + part * 16));
+          *reinterpret_cast<u32x4*>(&lds.v[e * L::VROW + part * 8]) = val;
+        }
+      }
+    }
+    __syncthreads();
+
+    if (active) {
+      // 3. S^T tile: entries (M) x query rows (N)
+      f32x4 s[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const uint16_t* krow = &lds.k[(mt * 16 + col) * L::KROW + gq * (DQK / 4)];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 av = *reinterpret_cast<const u32x4*>(krow + ks * 8);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                        __builtin_bit_cast(bf16x8, qv[ks]), acc,
+                                                        0, 0, 0);
+        }
+        s[mt] = acc;
+      }
+      // mask and scale: lane holds entries mt*16 + 4*gq + i for query row col
+      float tmax = -__builtin_huge_valf();
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = mt * 16 + 4 * gq + i;
+          const bool ok = e < n_t && lds.slot[e] >= 0;
+          const float x = ok ? s[mt][i] * a.scale_log2 : -__builtin_huge_valf();
+          s[mt][i] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run, tmax);
+      float alpha = 1.0f;
+      float psum = 0.0f;
+      float p[2][4];
+      if (m_new == -__builtin_huge_valf()) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[mt][i] = 0.0f;
+      } else {
+        alpha = exp2f(m_run - m_new);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[mt][i] = exp2f(s[mt][i] - m_new);
+            psum += p[mt][i];
+          }
+      }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      // rescale O: its rows are 4*gq + i; query row x's statistics sit in lane x
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * gq + i, 64);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[t][i] *= al[i];
+
+      // 4. P as the A operand: k-slot 8*gq + i <-> entry (i<4 ? 4gq+i : 16+4gq+i-4)
+      u32x4 pa;
+      pa[0] = pack_bf16x2(p[0][0], p[0][1]);
+      pa[1] = pack_bf16x2(p[0][2], p[0][3]);
+      pa[2] = pack_bf16x2(p[1][0], p[1][1]);
+      pa[3] = pack_bf16x2(p[1][2], p[1][3]);
+      const bf16x8 pab = __builtin_bit_cast(bf16x8, pa);
+      const uint16_t* vbase = KV == KV_SEPARATE ? lds.v : lds.k;
+      constexpr int VR = KV == KV_SEPARATE ? L::VROW : L::KROW;
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        u32x4 R[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int e = i < 4 ? 4 * gq + i : 16 + 4 * gq + (i - 4);
+          R[i] = *reinterpret_cast<const u32x4*>(vbase + e * VR + jb * 128 + col * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          u32x4 b;
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            b[qd] = (j & 1) ? hi16x2(R[2 * qd][j >> 1], R[2 * qd + 1][j >> 1])
+                            : lo16x2(R[2 * qd][j >> 1], R[2 * qd + 1][j >> 1]);
+          O[jb * 8 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              pab, __builtin_bit_cast(bf16x8, b), O[jb * 8 + j], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!active) return;
+  // Output: lane holds O[row 4*gq + i][channel 128*jb + 8*col + j] in O[8jb+j][i].
+  float lrow[4], mrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lrow[i] = __shfl(l_run, 4 * gq + i, 64);
+    mrow[i] = __shfl(m_run, 4 * gq + i, 64);
+  }
+  const int R = a.rows.n_rows;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qr = qrow0 + 4 * gq + i;
+    if (qr >= Mq) continue;
+    const int set = qr / G, h = g * G + qr % G;
+    const int64_t orow = ((int64_t)set * R + r) * a.hq + h;
+    if (a.n_split == 1) {
+      const float inv = lrow[i] > 0.0f ? 1.0f / lrow[i] : 0.0f;
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        const int c0 = jb * 128 + col * 8;
+        if (a.o_dtype == 1) {
+          u32x4 pk;
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            pk[qd] = pack_bf16x2(O[jb * 8 + 2 * qd][i] * inv, O[jb * 8 + 2 * qd + 1][i] * inv);
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.o) + orow * DV + c0) = pk;
+        } else {
+          float* op = reinterpret_cast<float*>(a.o) + orow * DV + c0;
+          f32x4 v0 = {O[jb * 8 + 0][i] * inv, O[jb * 8 + 1][i] * inv, O[jb * 8 + 2][i] * inv,
+                      O[jb * 8 + 3][i] * inv};
+          f32x4 v1 = {O[jb * 8 + 4][i] * inv, O[jb * 8 + 5][i] * inv, O[jb * 8 + 6][i] * inv,
+                      O[jb * 8 + 7][i] * inv};
+          reinterpret_cast<f32x4*>(op)[0] = v0;
+          reinterpret_cast<f32x4*>(op)[1] = v1;
+        }
+      }
+      if (a.lse && col == 0)
+        a.lse[orow] = lrow[i] > 0.0f ? (mrow[i] + __log2f(lrow[i])) * 0.6931471805599453f
+                                     : -__builtin_huge_valf();
+    } else {
+      const int64_t nrows = (int64_t)a.n_qsets * R * a.hq;
+      float* po = a.part + ((int64_t)sp * nrows + orow) * DV;
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        float* op = po + jb * 128 + col * 8;
+        f32x4 v0 = {O[jb * 8 + 0][i], O[jb * 8 + 1][i], O[jb * 8 + 2][i], O[jb * 8 + 3][i]};
+        f32x4 v1 = {O[jb * 8 + 4][i], O[jb * 8 + 5][i], O[jb * 8 + 6][i], O[jb * 8 + 7][i]};
+        reinterpret_cast<f32x4*>(op)[0] = v0;
+        reinterpret_cast<f32x4*>(op)[1] = v1;
+      }
+      if (col == 0) {
+        float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 2;
+        ml[0] = mrow[i];
+        ml[1] = lrow[i];
+      }
+    }
+  }
+}
+
+// Merge split partials: o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i.
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nrows = (int64_t)a.n_qsets * a.rows.n_rows * a.hq;
+  if (row >= nrows) return;
+  const int DV = a.dv;
+  const float* ml = a.part + (int64_t)a.n_split * nrows * DV;
+  float M = -__builtin_huge_valf();
+  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, ml[((int64_t)s * nrows + row) * 2]);
+  float Lsum = 0.0f;
+  for (int s = 0; s < a.n_split; ++s) {
+    const float m = ml[((int64_t)s * nrows + row) * 2], l = ml[((int64_t)s * nrows + row) * 2 + 1];
+    if (l > 0.0f) Lsum += exp2f(m - M) * l;
+  }
+  const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+  for (int c = lane; c < DV; c += 64) {
+    float acc = 0.0f;
+    for (int s = 0; s < a.n_split; ++s) {
+      const float m = ml[((int64_t)s * nrows + row) * 2], l = ml[((int64_t)s * nrows + row) * 2 + 1];
+      if (l > 0.0f) acc += exp2f(m - M) * a.part[((int64_t)s * nrows + row) * DV + c];
+    }
+    acc *= inv;
+    if (a.o_dtype == 1)
+      reinterpret_cast<uint16_t*>(a.o)[row * DV + c] = (uint16_t)f32_to_bf16_bits(acc);
+    else
+      reinterpret_cast<float*>(a.o)[row * DV + c] = acc;
+  }
+  if (a.lse && lane == 0)
+    a.lse[row] = Lsum > 0.0f ? (M + __log2f(Lsum)) * 0.6931471805599453f : -__builtin_huge_valf();
+}
+
+// F32 path: one wave per (row, KV head, query set, query head); entries in
+// chunks of 64 (one per lane), online softmax, lanes own output channels.
+constexpr int kF32MaxD = 256;
+__global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
+  __shared__ float qsh[4][kF32MaxD * 4];
+  __shared__ float psh[4][64];
+  __shared__ int64_t ssh[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
+  const int G = a.hq / a.hkv;
+  const int qr = blockIdx.y * 4 + wave;
+  if (qr >= a.n_qsets * G) return;
+  const int set = qr / G, h = g * G + qr % G;
+  const int R = a.rows.n_rows;
+  const int64_t orow = ((int64_t)set * R + r) * a.hq + h;
+  const RowInfo ri = row_info(a.rows, r);
+  const int n_w = ri.n_avail - ri.win_lo;
+  const int cnt = (a.idx && ri.b >= 0) ? a.count[r] : 0;
+  const int n_e = ri.b < 0 ? 0 : n_w + cnt;
+  const int32_t* idx = a.idx ? a.idx + (int64_t)r * a.idx_stride : nullptr;
+  const float* q = reinterpret_cast<const float*>(a.q) + orow * a.dqk;
+  float* qs = qsh[wave];
+  for (int c = lane; c < a.dqk; c += 64) qs[c] = q[c];
+  float m_run = -__builtin_huge_valf(), l_run = 0.0f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const char* vdata = a.kv_kind == KV_SEPARATE ? a.v.data : a.k.data;
+  const int64_t vstride = a.kv_kind == KV_SEPARATE ? a.v.row_stride : a.k.row_stride;
+  const int vhead_w = a.kv_kind == KV_SEPARATE ? a.dv : a.dqk;
+  for (int cb = 0; cb < n_e; cb += 64) {
+    const int i = cb + lane;
+    float x = -__builtin_huge_valf();
+    int64_t slot = -1;
+    if (i < n_e) {
+      const int pos = i < n_w ? ri.win_lo + i : idx[i - n_w];
+      if (pos >= 0) {
+        slot = cache_slot(a.k, ri.b, pos);
+        const float* kr = reinterpret_cast<const float*>(a.k.data + slot * a.k.row_stride) + g * a.dqk;
+        float d = 0.0f;
+        for (int c = 0; c < a.dqk; ++c) d = fmaf(qs[c], kr[c], d);
+        x = d * a.scale_log2;
+      }
+    }
+    const float m_new = fmaxf(m_run, wave_max(x));
+    float p = 0.0f, alpha = 1.0f;
+    if (m_new != -__builtin_huge_valf()) {
+      p = exp2f(x - m_new);
+      alpha = exp2f(m_run - m_new);
+    }
+    l_run = l_run * alpha + wave_sum(p);
+    m_run = m_new;
+    psh[wave][lane] = p;
+    ssh[wave][lane] = slot;
+    __builtin_amdgcn_wave_barrier();
+    const int ne = min(64, n_e - cb);
+    for (int k = 0; k < 4; ++k) acc[k] *= alpha;
+    for (int e = 0; e < ne; ++e) {
+      const int64_t sl = ssh[wave][e];
+      if (sl < 0) continue;
+      const float pe = psh[wave][e];
+      const float* vr = reinterpret_cast<const float*>(vdata + sl * vstride) + g * vhead_w;
+      for (int k = 0; k < 4; ++k) {
+        const int c = lane + 64 * k;
+        if (c < a.dv) acc[k] = fmaf(pe, vr[c], acc[k]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  for (int k = 0; k < 4; ++k) {
+    const int c = lane + 64 * k;
+    if (c >= a.dv) continue;
+    if (a.o_dtype == 1)
+      reinterpret_cast<uint16_t*>(a.o)[orow * a.dv + c] = (uint16_t)f32_to_bf16_bits(acc[k] * inv);
+    else
+      reinterpret_cast<float*>(a.o)[orow * a.dv + c] = acc[k] * inv;
+  }
+  if (a.lse && lane == 0)
+    a.lse[orow] = l_run > 0.0f ? (m_run + __log2f(l_run)) * 0.6931471805599453f
+                               : -__builtin_huge_valf();
+}
+
+template <int DQK, int DV, int KV>
+hipError_t launch_mfma_attn(const AttnArgs& a, hipStream_t s) {
+  const int G = a.hq / a.hkv;
+  const int tiles = (a.n_qsets * G + 15) / 16;
+  const int nw = tiles < kMaxW ? tiles : kMaxW;
+  const int groups = (tiles + nw - 1) / nw;
+  const int per = ((a.max_entries + a.n_split - 1) / a.n_split + kTile - 1) / kTile * kTile;
+  dim3 grid(a.n_split, a.rows.n_rows * a.hkv, groups);
+  hipLaunchKernelGGL((attn_mfma<DQK, DV, KV>), grid, dim3(64 * nw), 0, s, a, per);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split == 1) return e;
+  const int64_t nrows = (int64_t)a.n_qsets * a.rows.n_rows * a.hq;
+  hipLaunchKernelGGL(attn_combine, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Splits per row so that the grid covers the chip about twice; never below
+// one 32-entry tile per split.
+void attn_plan(AttnArgs& a) {
+  a.n_split = 1;
+  if (a.dtype == 0) return;
+  const int G = a.hq / a.hkv;
+  const int tiles = (a.n_qsets * G + 15) / 16;
+  const int nw = tiles < kMaxW ? tiles : kMaxW;
+  const int64_t base = (int64_t)a.rows.n_rows * a.hkv * ((tiles + nw - 1) / nw);
+  const int max_split = (a.max_entries + kTile - 1) / kTile;
+  int ns = 1;
+  while (ns < max_split && base * ns < 512) ++ns;
+  a.n_split = ns < 1 ? 1 : ns;
+}
+
+size_t attn_workspace_bytes(const AttnArgs& a) {
+  if (a.n_split <= 1) return 0;
+  const int64_t nrows = (int64_t)a.n_qsets * a.rows.n_rows * a.hq;
+  return (size_t)a.n_split * nrows * (a.dv + 2) * sizeof(float);
+}
+
+hipError_t launch_attn_gather(const AttnArgs& a, hipStream_t s) {
+  if (a.rows.n_rows == 0) return hipSuccess;
+  if (a.dtype == 0) {
+    const int G = a.hq / a.hkv;
+    dim3 grid(a.rows.n_rows * a.hkv, (a.n_qsets * G + 3) / 4);
+    hipLaunchKernelGGL(attn_f32, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  if (a.kv_kind == KV_SEPARATE) {
+    if (a.dqk == 128 && a.dv == 128) return launch_mfma_attn<128, 128, KV_SEPARATE>(a, s);
+    if (a.dqk == 256 && a.dv == 256) return launch_mfma_attn<256, 256, KV_SEPARATE>(a, s);
+  } else if (a.kv_kind == KV_SHARED) {
+    if (a.dqk == 576 && a.dv == 512) return launch_mfma_attn<576, 512, KV_SHARED>(a, s);
+    if (a.dqk == 512 && a.dv == 512) return launch_mfma_attn<512, 512, KV_SHARED>(a, s);
+    if (a.dqk == 128 && a.dv == 128) return launch_mfma_attn<128, 128, KV_SHARED>(a, s);
+  } else if (a.kv_kind == KV_FP4) {
+    if (a.dqk == 512 && a.dv == 512) return launch_mfma_attn<512, 512, KV_FP4>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sa

@@ -1,0 +1,110 @@
+"""Host-side drivers that chain the three entry points into one step of a
+workload.  Every call launches HIP kernels on the current stream; nothing here
+computes on the CPU.
+
+Layer-group semantics ("CSA, HCA and CSA2" page, section 3.1): a Full layer
+scores every visible entry and selects; a Reindex layer rescores only the
+block-max candidate pool with its own query and selects again; a Reuse layer
+runs no indexer at all and passes an existing index tensor to attention.
+HySparse2's FA + SA group ("HySparse2" page, section 5) is one index tensor
+shared by every query set of the group.
+
+A step object allocates all outputs and scratch once, so ``run()`` launches
+kernels only (and can be captured in a HIP graph).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional
+
+import torch
+
+from .binding import Cache, Rows, attn_gather_fwd, index_score, topk_select
+
+
+def _cache(c, heads, width, fp4=False) -> Cache:
+    return Cache(c.pool, c.block_table, heads, width, fp4=fp4, scale=c.scale)
+
+
+@dataclass
+class StepOutputs:
+    scores: List[torch.Tensor]
+    idx: List[torch.Tensor]
+    count: List[torch.Tensor]
+    pool: Optional[torch.Tensor]
+    pool_count: Optional[torch.Tensor]
+    o: List[torch.Tensor]
+    lse: List[torch.Tensor]
+
+
+class Step:
+    """One pass of the hot path over a problem instance.
+
+    Workloads without a block pool: score (full domain) -> window + top-k ->
+    one attention call for all query sets.  Workloads with a block pool
+    (CSA2): Full score -> top-k + pool -> Reindex score over the pool ->
+    top-k inside the pool -> attention with the Full indices (Full query) and
+    with the Reindex indices (Reindex query + Reuse queries, fused)."""
+
+    def __init__(self, prob, scores_slots: Optional[int] = None):
+        wl = prob.wl
+        self.prob = prob
+        self.wl = wl
+        dev = prob.seq_of_row.device
+        R = prob.n_rows
+        self.rows = Rows(prob.seq_of_row, prob.pos_of_row, prob.seq_len, wl.stride, wl.window)
+        self.kidx = _cache(prob.kidx, 1, wl.idx_dim)
+        fp4 = wl.kv_mode == "fp4"
+        self.k = _cache(prob.k, wl.hkv, wl.dqk, fp4=fp4)
+        self.v = _cache(prob.v, wl.hkv, wl.dv) if prob.v is not None else None
+        self.S = scores_slots or wl.n_entries_cap
+        f32 = torch.float32
+        i32 = torch.int32
+        self.scores = [torch.empty(R, self.S, dtype=f32, device=dev)]
+        self.idx = [torch.empty(R, wl.k, dtype=i32, device=dev)]
+        self.count = [torch.empty(R, dtype=i32, device=dev)]
+        self.pool = self.pool_count = None
+        if wl.block:
+            P = wl.max_blocks * wl.block
+            self.pool = torch.empty(R, P, dtype=i32, device=dev)
+            self.pool_count = torch.empty(R, dtype=i32, device=dev)
+            self.scores.append(torch.empty(R, P, dtype=f32, device=dev))
+            self.idx.append(torch.empty(R, wl.k, dtype=i32, device=dev))
+            self.count.append(torch.empty(R, dtype=i32, device=dev))
+        self.o, self.lse = [], []
+        for q in prob.q:
+            self.o.append(torch.empty(q.shape[0], R, wl.hq, wl.dv, dtype=q.dtype, device=dev))
+            self.lse.append(torch.empty(q.shape[0], R, wl.hq, dtype=f32, device=dev))
+        self.scale = wl.dqk ** -0.5
+
+    def run_index(self):
+        p, wl = self.prob, self.wl
+        index_score(self.rows, p.idx_q[0], p.idx_w[0], self.kidx, scores=self.scores[0])
+        if not wl.block:
+            topk_select(self.rows, self.scores[0], wl.k, idx=self.idx[0], count=self.count[0])
+            return
+        topk_select(self.rows, self.scores[0], wl.k, block=wl.block, max_blocks=wl.max_blocks,
+                    idx=self.idx[0], count=self.count[0], pool=self.pool,
+                    pool_count=self.pool_count)
+        index_score(self.rows, p.idx_q[1], p.idx_w[1], self.kidx, scores=self.scores[1],
+                    cand=self.pool, cand_count=self.pool_count)
+        topk_select(self.rows, self.scores[1], wl.k, cand=self.pool, cand_count=self.pool_count,
+                    idx=self.idx[1], count=self.count[1])
+
+    def run_attention(self, idx=None, count=None):
+        """Attention for every call; ``idx``/``count`` (lists) override the
+        step's own index tensors (used to feed externally chosen indices)."""
+        p = self.prob
+        idx = idx if idx is not None else self.idx
+        count = count if count is not None else self.count
+        for c, q in enumerate(p.q):
+            attn_gather_fwd(self.rows, q, self.k, self.v, idx=idx[c], count=count[c],
+                            scale=self.scale, d_v=self.wl.dv, o=self.o[c], lse=self.lse[c])
+
+    def run(self):
+        self.run_index()
+        self.run_attention()
+
+    def outputs(self) -> StepOutputs:
+        return StepOutputs(self.scores, self.idx, self.count, self.pool, self.pool_count, self.o,
+                           self.lse)

@@ -255,7 +255,8 @@ def make_problem(wl: Workload, device="cpu", integer=False, seed_base=None,
 
     ``integer=True`` gives the integer-valued variant: indexer q, k and w are
     uniform integers in [-4, 4] (every score then is an exact integer in
-    float32), and attention inputs are integers too.  ``rows`` restricts the
+    float32, so selections can be compared bit for bit); attention inputs stay
+    N(0, 1).  ``rows`` restricts the
     query rows of a prefill workload to the listed positions of sequence 0.
     """
     base = 1000 * (wl.cfg_id + 1) if seed_base is None else seed_base
@@ -300,20 +301,20 @@ def make_problem(wl: Workload, device="cpu", integer=False, seed_base=None,
     for call in range(n_calls):
         sets = wl.n_qsets if call == 0 else 1 + wl.n_reuse
         q.append(_draw((sets, R, wl.hq, wl.dqk), base + 4 + 10 * call, device, wl.attn_dtype,
-                       integer))
+                       False))
     lead = (n_pages, wl.page_size) if wl.page_size else (B, cap)
     if wl.kv_mode == "fp4":
-        x = _draw(lead + (wl.hkv, wl.dqk), base + 5, device, torch.float32, integer)
+        x = _draw(lead + (wl.hkv, wl.dqk), base + 5, device, torch.float32, False)
         codes, scales = fp4_encode(x)
         del x
         kc = Cache(codes, bt, wl.page_size, scale=scales)
         vc = None
     else:
-        kc = Cache(_draw(lead + (wl.hkv, wl.dqk), base + 5, device, wl.attn_dtype, integer), bt,
+        kc = Cache(_draw(lead + (wl.hkv, wl.dqk), base + 5, device, wl.attn_dtype, False), bt,
                    wl.page_size)
         vc = None
         if wl.kv_mode == "separate":
-            vc = Cache(_draw(lead + (wl.hkv, wl.dv), base + 6, device, wl.attn_dtype, integer), bt,
+            vc = Cache(_draw(lead + (wl.hkv, wl.dv), base + 6, device, wl.attn_dtype, False), bt,
                        wl.page_size)
     return Problem(wl, integer, seq_of_row.to(device), pos_of_row.to(device), seq_len.to(device),
                    idx_q, idx_w, kidx, q, kc, vc)

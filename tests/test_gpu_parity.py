@@ -1,0 +1,250 @@
+"""GPU parity: every entry point of the HIP library against the fp64 oracle on
+seeded inputs of each workload's shape family, at oracle-friendly sizes that
+still span several tiles, pages and splits, with ragged and degenerate rows.
+
+Index sets are bit-exact on integer-valued inputs; on float inputs only
+boundary swaps within the fp32 error bound are allowed.  Attention is checked
+given identical (oracle-chosen) indices: max-abs 1e-2 / rel-L2 5e-3 for bf16
+and FP4 (after the same exact dequantisation), 1e-5 / 1e-6 for fp32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import index_reuse_amd
+
+    index_reuse_amd.load()
+    return "cuda"
+
+
+def _cases():
+    hs2 = synth.HYSPARSE2.replace(n_seqs=7, seq_lens_override=(2500, 1151, 1152, 1153, 100, 1, 1280))
+    csa = synth.CSA.replace(n_seqs=4, seq_len=8192, tail_variant=True)
+    csa2 = synth.CSA2.replace(n_seqs=2, seq_lens_override=(20000, 16389))
+    tiny = synth.TINY
+    return {
+        "tiny": (tiny, False),
+        "tiny_int": (tiny, True),
+        "hysparse2": (hs2, False),
+        "hysparse2_int": (hs2, True),
+        "csa": (csa, False),
+        "csa_int": (csa, True),
+        "csa2": (csa2, False),
+        "csa2_int": (csa2, True),
+    }
+
+
+CASES = _cases()
+DSA_ROWS = [0, 1, 2, 63, 64, 100, 2046, 2047, 2048, 2049, 3000, 4095]
+
+
+def _problem(name):
+    wl, integer = CASES[name]
+    return wl, integer, synth.make_problem(wl, device="cpu", integer=integer)
+
+
+def _step(prob, dev):
+    from index_reuse_amd.pipeline import Step
+
+    p = H.move(prob, dev)
+    return p, Step(p)
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_index_and_select(name, dev):
+    wl, integer, prob = _problem(name)
+    _flush("case %s R=%d" % (name, prob.n_rows))
+    p, step = _step(prob, dev)
+    step.run_index()
+    torch.cuda.synchronize()
+    sc = H.oracle_scores(prob, 0)
+    g = step.scores[0].cpu().double().numpy()
+    valid = ~np.isnan(sc)
+    tau = None if integer else H.fp32_score_bound(prob, 0)
+    if integer:
+        assert np.array_equal(g[valid], sc[valid])
+    else:
+        err = np.abs(g - np.nan_to_num(sc))
+        assert np.all(err[valid] <= np.broadcast_to(tau[:, None], sc.shape)[valid])
+    if not wl.block:
+        idx, cnt = H.oracle_select(prob, sc, wl.k)
+        H.check_indices(step.idx[0].cpu(), step.count[0].cpu(), idx, cnt, sc, tau)
+        return
+    idx, cnt, pool, pc = H.oracle_select(prob, sc, wl.k, block=wl.block, max_blocks=wl.max_blocks)
+    H.check_indices(step.idx[0].cpu(), step.count[0].cpu(), idx, cnt, sc, tau)
+    gpool, gpc = step.pool.cpu().numpy(), step.pool_count.cpu().numpy()
+    if integer:
+        assert np.array_equal(gpc, pc)
+        assert np.array_equal(gpool, pool)
+    same = [r for r in range(prob.n_rows) if np.array_equal(gpool[r], pool[r])]
+    assert len(same) >= (prob.n_rows if integer else 1)
+    # Reindex over the (identical) pool with the second query
+    rs = H.oracle_scores(prob, 1, cand=pool, cand_count=pc)
+    gr = step.scores[1].cpu().double().numpy()
+    for r in same:
+        v = ~np.isnan(rs[r])
+        if integer:
+            assert np.array_equal(gr[r, v], rs[r, v])
+    ridx, rcnt = H.oracle_select(prob, rs, wl.k, cand=pool, cand_count=pc)
+    tau1 = None if integer else H.fp32_score_bound(prob, 1)
+    H.check_indices(step.idx[1].cpu(), step.count[1].cpu(), ridx, rcnt, rs, tau1, rows=same,
+                    positions=pool)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_attention_given_oracle_indices(name, dev):
+    wl, integer, prob = _problem(name)
+    _flush("case %s R=%d" % (name, prob.n_rows))
+    p, step = _step(prob, dev)
+    sc = H.oracle_scores(prob, 0)
+    if wl.block:
+        idx, cnt, pool, pc = H.oracle_select(prob, sc, wl.k, block=wl.block,
+                                             max_blocks=wl.max_blocks)
+        rs = H.oracle_scores(prob, 1, cand=pool, cand_count=pc)
+        ridx, rcnt = H.oracle_select(prob, rs, wl.k, cand=pool, cand_count=pc)
+        idxs, cnts = [idx, ridx], [cnt, rcnt]
+    else:
+        idx, cnt = H.oracle_select(prob, sc, wl.k)
+        idxs, cnts = [idx], [cnt]
+    tidx = [torch.from_numpy(np.ascontiguousarray(i)).to(dev) for i in idxs]
+    tcnt = [torch.from_numpy(np.ascontiguousarray(c)).to(dev) for c in cnts]
+    step.run_attention(idx=tidx, count=tcnt)
+    torch.cuda.synchronize()
+    for c in range(len(prob.q)):
+        o_ref, l_ref = H.oracle_attention(prob, c, idxs[c], cnts[c])
+        H.check_outputs(step.o[c], o_ref, step.lse[c], l_ref, wl.attn_dtype,
+                        what="%s call %d" % (name, c))
+
+
+def test_dsa_rows_fp8_latent(dev):
+    """DSA-shaped prefill rows (FP8 indexer 64x128, top-2048, latent 576 with
+    V = first 512, 128 heads) on a 4096-token sequence; rows straddle the
+    point where the budget stops covering the whole causal prefix."""
+    for integer in (True, False):
+        wl = synth.DSA.replace(seq_len=4096)
+        prob = synth.make_problem(wl, device="cpu", integer=integer, rows=DSA_ROWS)
+        _flush("case dsa integer=%s" % integer)
+        p, step = _step(prob, dev)
+        step.run_index()
+        torch.cuda.synchronize()
+        sc = H.oracle_scores(prob, 0)
+        g = step.scores[0].cpu().double().numpy()
+        valid = ~np.isnan(sc)
+        if integer:
+            assert np.array_equal(g[valid], sc[valid])
+            tau = None
+        else:
+            tau = H.fp32_score_bound(prob, 0)
+        idx, cnt = H.oracle_select(prob, sc, wl.k)
+        assert list(cnt) == [min(2048, t + 1) for t in DSA_ROWS]
+        H.check_indices(step.idx[0].cpu(), step.count[0].cpu(), idx, cnt, sc, tau)
+        step.run_attention(idx=[torch.from_numpy(idx).to(dev)], count=[torch.from_numpy(cnt).to(dev)])
+        torch.cuda.synchronize()
+        o_ref, l_ref = H.oracle_attention(prob, 0, idx, cnt)
+        H.check_outputs(step.o[0], o_ref, step.lse[0], l_ref, torch.bfloat16, what="dsa")
+
+
+def test_select_exact_on_given_scores(dev):
+    """Selection alone on generated scores with heavy ties and signed zeros
+    (token, candidate and pool modes) is bit-exact."""
+    from index_reuse_amd import Rows, topk_select
+
+    import oracle
+
+    R, S = 24, 5000
+    scores = synth.small_ints((R, S), seed=77, lo=-3, hi=3)
+    scores[scores == 0] = -0.0
+    scores[:, ::7] = 0.0
+    scores[3] = 1.0  # one row of all-equal scores
+    so = torch.zeros(R, dtype=torch.int32)
+    po = torch.tensor([S - 1 - 37 * r for r in range(R)], dtype=torch.int32)
+    sl = torch.tensor([S], dtype=torch.int32)
+    for window, k in ((0, 1), (16, 700), (100, 4096), (3, 4999)):
+        rows = Rows(so.to(dev), po.to(dev), sl.to(dev), 1, window)
+        gi, gc, gp, gpc = topk_select(rows, scores.to(dev), k, block=8, max_blocks=100)
+        oi, oc, op, opc = oracle.topk_select(so, po, sl, 1, window, scores.double().numpy(), k,
+                                             block=8, max_blocks=100)
+        torch.cuda.synchronize()
+        assert np.array_equal(gc.cpu().numpy(), oc)
+        assert np.array_equal(gi.cpu().numpy(), oi)
+        assert np.array_equal(gpc.cpu().numpy(), opc)
+        assert np.array_equal(gp.cpu().numpy(), op)
+    # candidate mode
+    P = 1500
+    cand = torch.full((R, P), -1, dtype=torch.int32)
+    cc = torch.zeros(R, dtype=torch.int32)
+    g = torch.Generator().manual_seed(5)
+    for r in range(R):
+        m = int(torch.randint(0, P + 1, (1,), generator=g))
+        cand[r, :m] = torch.randperm(S, generator=g)[:m].sort().values.to(torch.int32)
+        cc[r] = m
+    cs = scores[:, :P].contiguous()
+    rows = Rows(so.to(dev), po.to(dev), sl.to(dev), 1, 10)
+    gi, gc = topk_select(rows, cs.to(dev), 300, cand=cand.to(dev), cand_count=cc.to(dev))
+    oi, oc = oracle.topk_select(so, po, sl, 1, 10, cs.double().numpy(), 300, cand=cand,
+                                cand_count=cc)
+    torch.cuda.synchronize()
+    assert np.array_equal(gc.cpu().numpy(), oc)
+    assert np.array_equal(gi.cpu().numpy(), oi)
+
+
+def test_deterministic_and_reuse(dev):
+    """Two runs are bitwise identical; one fused call over all query sets
+    equals one call per set (index reuse changes nothing numerically)."""
+    from index_reuse_amd import attn_gather_fwd
+
+    wl, integer, prob = _problem("hysparse2")
+    p, step = _step(prob, dev)
+    step.run()
+    torch.cuda.synchronize()
+    first = [t.clone() for t in step.o] + [step.idx[0].clone()]
+    step.run()
+    torch.cuda.synchronize()
+    for a, b in zip(first, [t for t in step.o] + [step.idx[0]]):
+        assert torch.equal(a, b)
+    q = p.q[0]
+    for s in range(q.shape[0]):
+        o1, l1 = attn_gather_fwd(step.rows, q[s:s + 1].contiguous(), step.k, step.v,
+                                 idx=step.idx[0], count=step.count[0], scale=step.scale)
+        torch.cuda.synchronize()
+        ref = step.o[0][s:s + 1].float()
+        assert (o1.float() - ref).abs().max().item() <= 1e-2
+
+
+def test_padding_rows_and_empty(dev):
+    """Padding rows (negative sequence) and rows whose window covers their
+    whole domain give count 0, o = 0 and lse = -inf."""
+    wl = synth.HYSPARSE2.replace(n_seqs=2, seq_lens_override=(300, 50))
+    prob = synth.make_problem(wl, device="cpu")
+    prob.seq_of_row = torch.tensor([0, -1, 1, 0], dtype=torch.int32)
+    prob.pos_of_row = torch.tensor([299, 10, 49, -1], dtype=torch.int32)
+    for layer in range(len(prob.idx_q)):
+        prob.idx_q[layer] = torch.cat([prob.idx_q[layer]] * 2)
+        prob.idx_w[layer] = torch.cat([prob.idx_w[layer]] * 2)
+    prob.q = [torch.cat([q, q], dim=1) for q in prob.q]
+    p, step = _step(prob, dev)
+    step.run()
+    torch.cuda.synchronize()
+    cnt = step.count[0].cpu().tolist()
+    assert cnt == [172, 0, 0, 0]
+    o = step.o[0].float().cpu()
+    lse = step.lse[0].cpu()
+    for r in (1, 3):
+        assert torch.all(o[:, r] == 0) and torch.all(torch.isneginf(lse[:, r]))
+    sc = H.oracle_scores(prob, 0)
+    idx, c = H.oracle_select(prob, sc, wl.k)
+    o_ref, l_ref = H.oracle_attention(prob, 0, idx, c)
+    H.check_outputs(step.o[0], o_ref, step.lse[0], l_ref, torch.bfloat16, what="padding")
