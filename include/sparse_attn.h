@@ -177,7 +177,8 @@ typedef struct {
  * (score descending, index ascending; -0 == +0) are written ASCENDING to
  * idx[r][0 .. count[r]), and idx[r][count[r] .. k) = -1.
  *
- * Pool mode (block > 1, full mode only) ["CSA, HCA and CSA2", section 3.2]:
+ * Pool mode (pool != NULL, block >= 1, max_blocks <= 2048, full-domain scores
+ * only) ["CSA, HCA and CSA2", section 3.2]:
  * every aligned block j of `block` entries gets beta_j = the max score over
  * its visible members (window included); the first min(max_blocks, #blocks)
  * blocks in the order (beta descending, j ascending) are kept, and their

@@ -231,7 +231,11 @@ def topk_select(rows: Rows, scores: torch.Tensor, k: int, cand=None, cand_count=
         pool_count = torch.empty(R, dtype=torch.int32, device=dev)
     d = topk_desc(rows, scores, k, idx, count, cand, cand_count, block, max_blocks, pool,
                   pool_count)
-    _check(L.sparse_topk_select(ctypes.byref(d), None, 0, _stream()))
+    need = int(L.sa_workspace_size(SA_OP_TOPK_SELECT, ctypes.byref(d)))
+    if need == ctypes.c_size_t(-1).value:
+        _check(-2)
+    ws = workspace(need, scores.device)
+    _check(L.sparse_topk_select(ctypes.byref(d), _ptr(ws), need, _stream()))
     if block > 0:
         return idx, count, pool, pool_count
     return idx, count
@@ -272,3 +276,51 @@ def attn_gather_fwd(rows: Rows, q: torch.Tensor, k: Cache, v: Optional[Cache] = 
     ws = workspace(need, q.device)
     _check(L.sparse_attn_gather_fwd(ctypes.byref(d), _ptr(ws), need, _stream()))
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Prepared calls: descriptor and workspace built once, launch-only __call__
+# ---------------------------------------------------------------------------
+
+
+class Prepared:
+    """A validated entry-point call whose descriptor (and workspace) are kept,
+    so that each launch costs one ctypes call.  Every tensor the descriptor
+    points to must stay alive as long as this object."""
+
+    def __init__(self, fn_name: str, desc, op: int, device, keep=()):
+        L = load()
+        self.fn = getattr(L, fn_name)
+        self.desc = desc
+        self.ref = ctypes.byref(desc)
+        need = int(L.sa_workspace_size(op, self.ref))
+        if need == ctypes.c_size_t(-1).value:
+            _check(-2)
+        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device) if need else None
+        self.ws_ptr = _ptr(self.ws)
+        self.need = need
+        self.keep = keep
+
+    def __call__(self, stream=None):
+        _check(self.fn(self.ref, self.ws_ptr, self.need, _stream() if stream is None else stream))
+
+
+def prepare_index_score(rows: Rows, q, w, k: Cache, scores, cand=None, cand_count=None):
+    d = index_desc(rows, q, w, k, scores, cand, cand_count)
+    return Prepared("sparse_index_score", d, SA_OP_INDEX_SCORE, q.device,
+                    keep=(rows, q, w, k, scores, cand, cand_count))
+
+
+def prepare_topk_select(rows: Rows, scores, k, idx, count, cand=None, cand_count=None, block=0,
+                        max_blocks=0, pool=None, pool_count=None):
+    d = topk_desc(rows, scores, k, idx, count, cand, cand_count, block, max_blocks, pool,
+                  pool_count)
+    return Prepared("sparse_topk_select", d, SA_OP_TOPK_SELECT, scores.device,
+                    keep=(rows, scores, idx, count, cand, cand_count, pool, pool_count))
+
+
+def prepare_attn_gather_fwd(rows: Rows, q, k: Cache, v: Optional[Cache], idx, count, o, lse=None,
+                            scale=None, d_v=None):
+    d = attn_desc(rows, q, k, v, idx, count, o, lse, scale, d_v)
+    return Prepared("sparse_attn_gather_fwd", d, SA_OP_ATTN_GATHER_FWD, q.device,
+                    keep=(rows, q, k, v, idx, count, o, lse))

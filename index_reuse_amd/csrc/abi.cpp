@@ -173,6 +173,7 @@ sa_status validate_topk(const sa_topk_desc* d, sa::SelectArgs* out) {
           "%s: block and max_blocks must be >= 1", op);
     CHECK((int64_t)d->pool_stride >= (int64_t)d->max_blocks * d->block, SA_ERR_SHAPE,
           "%s: pool_stride < max_blocks * block", op);
+    CHECK(d->max_blocks <= 2048, SA_ERR_UNSUPPORTED, "%s: at most 2048 pool blocks", op);
   }
   if (out) {
     out->rows = to_dev(d->rows);
@@ -191,6 +192,8 @@ sa_status validate_topk(const sa_topk_desc* d, sa::SelectArgs* out) {
     out->pool = d->pool;
     out->pool_count = d->pool_count;
     out->max_elems = d->cand ? d->cand_stride : (int32_t)d->score_stride;
+    out->beta = nullptr;
+    out->beta_stride = pool ? ((d->score_stride + d->block - 1) / d->block + 63) / 64 * 64 : 0;
   }
   return SA_OK;
 }
@@ -239,6 +242,8 @@ sa_status validate_attn(const sa_attn_desc* d, sa::AttnArgs* out) {
     CHECK(d->k.scale, SA_ERR_NULL, "%s: FP4 k needs k.scale", op);
     CHECK(d->k.scale_stride >= (int64_t)hkv * dqk / 16, SA_ERR_SHAPE, "%s: k.scale_stride too small",
           op);
+    CHECK(d->k.scale_stride % 2 == 0 && ((uintptr_t)d->k.scale & 1u) == 0, SA_ERR_SHAPE,
+          "%s: k.scale and k.scale_stride must be 2-byte aligned", op);
   } else {
     st = check_cache(d->k, op, "k", (int64_t)hkv * dqk * elem_bytes(cdt));
     if (st) return st;
@@ -296,11 +301,17 @@ sa_status sparse_index_score(const sa_index_desc* desc, void* ws, size_t ws_byte
 }
 
 sa_status sparse_topk_select(const sa_topk_desc* desc, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   sa::SelectArgs a;
   sa_status st = validate_topk(desc, &a);
   if (st || desc->rows.n_rows == 0) return st;
+  const size_t need = sa::topk_workspace_bytes(a);
+  if (need) {
+    CHECK(ws && ws_bytes >= need, SA_ERR_WORKSPACE,
+          "sparse_topk_select: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    CHECK(((uintptr_t)ws & 255u) == 0, SA_ERR_WORKSPACE,
+          "sparse_topk_select: workspace must be 256-byte aligned");
+    a.beta = reinterpret_cast<float*>(ws);
+  }
   return hip_status(sa::launch_topk_select(a, (hipStream_t)stream), "sparse_topk_select");
 }
 
@@ -324,8 +335,13 @@ size_t sa_workspace_size(int32_t op, const void* desc) {
   switch (op) {
     case SA_OP_INDEX_SCORE:
       return validate_index(reinterpret_cast<const sa_index_desc*>(desc), nullptr) ? (size_t)-1 : 0;
-    case SA_OP_TOPK_SELECT:
-      return validate_topk(reinterpret_cast<const sa_topk_desc*>(desc), nullptr) ? (size_t)-1 : 0;
+    case SA_OP_TOPK_SELECT: {
+      const sa_topk_desc* d = reinterpret_cast<const sa_topk_desc*>(desc);
+      sa::SelectArgs a;
+      if (validate_topk(d, &a)) return (size_t)-1;
+      if (d->rows.n_rows == 0) return 0;
+      return sa::topk_workspace_bytes(a);
+    }
     case SA_OP_ATTN_GATHER_FWD: {
       const sa_attn_desc* d = reinterpret_cast<const sa_attn_desc*>(desc);
       sa::AttnArgs a;

@@ -31,7 +31,6 @@ namespace sa {
 namespace {
 
 constexpr int kTile = 32;   // entries per tile
-constexpr int kMaxW = 8;    // waves per workgroup (query-row tiles of 16)
 
 enum { KV_SEPARATE = 0, KV_SHARED = 1, KV_FP4 = 2 };
 
@@ -62,33 +61,52 @@ __device__ __forceinline__ void fp4_dequant32(u32x4 codes, uint32_t s0, uint32_t
   }
 }
 
+constexpr int kNW = 4;           // waves per workgroup (one per SIMD)
+constexpr int kMaxEntries = 2048;  // entries per workgroup (slot table size)
+
 template <int DQK, int DV, int KV>
 struct AttnLds {
   static constexpr int KROW = DQK + 8;  // bf16 elements per LDS row (padded)
   static constexpr int VROW = DV + 8;
   static constexpr bool HAS_V = KV == KV_SEPARATE;
-  uint16_t k[kTile * KROW];
-  uint16_t v[HAS_V ? kTile * VROW : 1];
-  int64_t slot[kTile];
+  uint16_t k[2][kTile * KROW];
+  uint16_t v[2][HAS_V ? kTile * VROW : 1];
+  int32_t slot[kMaxEntries];  // cache slot of every entry of the range (-1: none)
 };
 
+// Per-thread share of one tile of gathered rows, held in registers between
+// the global load and the LDS store (the prefetch ring).
 template <int DQK, int DV, int KV>
-__global__ __launch_bounds__(64 * kMaxW) void attn_mfma(AttnArgs a, int per_split) {
-  using L = AttnLds<DQK, DV, KV>;
-  __shared__ __align__(16) L lds;
-  constexpr int KS = DQK / 32;           // k-steps of the S MFMA
-  constexpr int QV = DQK / 32;           // 16-byte q vectors per lane
-  constexpr int NJB = DV / 128;          // 128-channel blocks of V
-  constexpr int NT = DV / 16;            // N tiles of O
+struct TileRegs {
+  static constexpr bool FP4 = KV == KV_FP4;
+  static constexpr int CPR_K = FP4 ? DQK / 32 : DQK / 8;  // 16-byte chunks per K row
+  static constexpr int CPR_V = KV == KV_SEPARATE ? DV / 8 : 0;
+  static constexpr int C_K = kTile * CPR_K;
+  static constexpr int C_ALL = C_K + kTile * CPR_V;
+  static constexpr int U = (C_ALL + 64 * kNW - 1) / (64 * kNW);
+  u32x4 v[U];
+  uint32_t sc[FP4 ? U : 1];  // FP4: the two E4M3 scales of each 32-channel chunk
+};
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
+template <int DQK, int DV, int KV, int D>
+__global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_split) {
+  using L = AttnLds<DQK, DV, KV>;
+  using T = TileRegs<DQK, DV, KV>;
+  __shared__ __align__(16) L lds;
+  constexpr int KS = DQK / 32;   // k-steps of the S MFMA
+  constexpr int QV = DQK / 32;   // 16-byte q vectors per lane
+  constexpr int NJB = DV / 128;  // 128-channel blocks of V
+  constexpr int NT = DV / 16;    // N tiles of O
+  constexpr int NTH = 64 * kNW;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, gq = lane >> 4;
   const int sp = blockIdx.x;
   const int r = blockIdx.y / a.hkv, g = blockIdx.y % a.hkv;
   const int G = a.hq / a.hkv;
   const int Mq = a.n_qsets * G;
-  const int qrow0 = (blockIdx.z * nw + wave) * 16;
+  const int qrow0 = (blockIdx.z * kNW + wave) * 16;
   const bool active = qrow0 < Mq;
 
   const RowInfo ri = row_info(a.rows, r);
@@ -96,7 +114,21 @@ __global__ __launch_bounds__(64 * kMaxW) void attn_mfma(AttnArgs a, int per_spli
   const int cnt = (a.idx && ri.b >= 0) ? a.count[r] : 0;
   const int n_e = ri.b < 0 ? 0 : n_w + cnt;
   const int e0 = sp * per_split, e1 = min(n_e, e0 + per_split);
+  const int ne = max(0, e1 - e0);
+  const int ntiles = (ne + kTile - 1) / kTile;
   const int32_t* idx = a.idx ? a.idx + (int64_t)r * a.idx_stride : nullptr;
+
+  // Cache slot of every entry of this range, once: the window entries, then
+  // the selected ones, through the block table.  Padding to whole tiles is -1.
+  for (int i = tid; i < ntiles * kTile; i += NTH) {
+    int slot = -1;
+    if (i < ne) {
+      const int e = e0 + i;
+      const int pos = e < n_w ? ri.win_lo + e : idx[e - n_w];
+      if (pos >= 0) slot = (int)cache_slot(a.k, ri.b, pos);
+    }
+    lds.slot[i] = slot;
+  }
 
   // Query rows of this wave as the B operand (query row = col).
   u32x4 qv[QV];
@@ -114,163 +146,179 @@ __global__ __launch_bounds__(64 * kMaxW) void attn_mfma(AttnArgs a, int per_spli
       for (int i = 0; i < QV; ++i) qv[i] = u32x4{0, 0, 0, 0};
     }
   }
+  __syncthreads();
+
+  // Issue the global loads of tile t into registers.
+  auto load_tile = [&](int t, T& regs) {
+#pragma unroll
+    for (int u = 0; u < T::U; ++u) {
+      const int c = tid + NTH * u;
+      u32x4 val = u32x4{0, 0, 0, 0};
+      uint32_t scl = 0u;
+      if (c < T::C_ALL) {
+        const bool is_k = c < T::C_K;
+        const int cc = is_k ? c : c - T::C_K;
+        const int cpr = is_k ? T::CPR_K : T::CPR_V;
+        const int e = cc / cpr, part = cc % cpr;
+        const int slot = lds.slot[t * kTile + e];
+        if (slot >= 0) {
+          if constexpr (T::FP4) {
+            val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                a.k.data + (int64_t)slot * a.k.row_stride + g * (DQK / 2) + part * 16));
+            scl = *reinterpret_cast<const uint16_t*>(a.k.scale + (int64_t)slot * a.k.scale_stride +
+                                                     g * (DQK / 16) + part * 2);
+          } else if (is_k) {
+            val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                a.k.data + (int64_t)slot * a.k.row_stride + g * (DQK * 2) + part * 16));
+          } else {
+            val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                a.v.data + (int64_t)slot * a.v.row_stride + g * (DV * 2) + part * 16));
+          }
+        }
+      }
+      regs.v[u] = val;
+      if constexpr (T::FP4) regs.sc[u] = scl;
+    }
+  };
+  // Store a tile's registers into LDS buffer `buf` (FP4 is dequantised here).
+  auto store_tile = [&](const T& regs, int buf) {
+#pragma unroll
+    for (int u = 0; u < T::U; ++u) {
+      const int c = tid + NTH * u;
+      if (c >= T::C_ALL) continue;
+      if constexpr (T::FP4) {
+        const int e = c / T::CPR_K, part = c % T::CPR_K;
+        uint32_t vals[16];
+        fp4_dequant32(regs.v[u], regs.sc[u] & 0xFFu, regs.sc[u] >> 8, vals);
+        u32x4* dst = reinterpret_cast<u32x4*>(&lds.k[buf][e * L::KROW + part * 32]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[i] = u32x4{vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]};
+      } else if (c < T::C_K) {
+        const int e = c / T::CPR_K, part = c % T::CPR_K;
+        *reinterpret_cast<u32x4*>(&lds.k[buf][e * L::KROW + part * 8]) = regs.v[u];
+      } else {
+        const int cc = c - T::C_K;
+        const int e = cc / T::CPR_V, part = cc % T::CPR_V;
+        *reinterpret_cast<u32x4*>(&lds.v[buf][e * L::VROW + part * 8]) = regs.v[u];
+      }
+    }
+  };
 
   f32x4 O[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_huge_valf(), l_run = 0.0f;
 
-  for (int tb = e0; tb < e1; tb += kTile) {
-    const int n_t = min(kTile, e1 - tb);
-    // 1. slots of this tile's entries
-    if (threadIdx.x < kTile) {
-      int64_t slot = -1;
-      const int i = tb + threadIdx.x;
-      if ((int)threadIdx.x < n_t) {
-        const int pos = i < n_w ? ri.win_lo + i : idx[i - n_w];
-        if (pos >= 0) slot = cache_slot(a.k, ri.b, pos);
+  auto compute = [&](int buf, int t) {
+    const uint16_t* kb = lds.k[buf];
+    // S^T tile: entries (M) x query rows (N)
+    f32x4 s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* krow = kb + (mt * 16 + col) * L::KROW + gq * (DQK / 4);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(krow + ks * 8);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                      __builtin_bit_cast(bf16x8, qv[ks]), acc, 0,
+                                                      0, 0);
       }
-      lds.slot[threadIdx.x] = slot;
+      s[mt] = acc;
     }
-    __syncthreads();
-    // 2. gather K (and V) rows into LDS
-    if constexpr (KV == KV_FP4) {
-      constexpr int CH = DQK / 32;  // 16-byte code chunks per row
-      for (int c = threadIdx.x; c < kTile * CH; c += blockDim.x) {
-        const int e = c / CH, part = c % CH;
-        const int64_t slot = lds.slot[e];
-        uint32_t vals[16];
-        if (slot >= 0) {
-          const u32x4 codes = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-              a.k.data + slot * a.k.row_stride + g * (DQK / 2) + part * 16));
-          const uint8_t* sp8 = a.k.scale + slot * a.k.scale_stride + g * (DQK / 16) + part * 2;
-          fp4_dequant32(codes, sp8[0], sp8[1], vals);
-        } else {
+    // mask and scale: lane holds entries mt*16 + 4*gq + i for query row col
+    float tmax = -__builtin_huge_valf();
 #pragma unroll
-          for (int i = 0; i < 16; ++i) vals[i] = 0u;
-        }
-        u32x4* dst = reinterpret_cast<u32x4*>(&lds.k[e * L::KROW + part * 32]);
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = u32x4{vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]};
+      for (int i = 0; i < 4; ++i) {
+        const int e = mt * 16 + 4 * gq + i;
+        const bool ok = lds.slot[t * kTile + e] >= 0;
+        const float x = ok ? s[mt][i] * a.scale_log2 : -__builtin_huge_valf();
+        s[mt][i] = x;
+        tmax = fmaxf(tmax, x);
       }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    float alpha = 1.0f;
+    float psum = 0.0f;
+    float p[2][4];
+    if (m_new == -__builtin_huge_valf()) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[mt][i] = 0.0f;
     } else {
-      constexpr int CH = DQK / 8;
-      for (int c = threadIdx.x; c < kTile * CH; c += blockDim.x) {
-        const int e = c / CH, part = c % CH;
-        const int64_t slot = lds.slot[e];
-        u32x4 val = u32x4{0, 0, 0, 0};
-        if (slot >= 0)
-          val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-              a.k.data + slot * a.k.row_stride + g * (DQK * 2) + part * 16));
-        *reinterpret_cast<u32x4*>(&lds.k[e * L::KROW + part * 8]) = val;
-      }
-      if constexpr (KV == KV_SEPARATE) {
-        constexpr int CV = DV / 8;
-        for (int c = threadIdx.x; c < kTile * CV; c += blockDim.x) {
-          const int e = c / CV, part = c % CV;
-          const int64_t slot = lds.slot[e];
-          u32x4 val = u32x4{0, 0, 0, 0};
-          if (slot >= 0)
-            val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                a.v.data + slot * a.v.row_stride + g * (DV * 2) + part * 16));
-          *reinterpret_cast<u32x4*>(&lds.v[e * L::VROW + part * 8]) = val;
-        }
-      }
-    }
-    __syncthreads();
-
-    if (active) {
-      // 3. S^T tile: entries (M) x query rows (N)
-      f32x4 s[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* krow = &lds.k[(mt * 16 + col) * L::KROW + gq * (DQK / 4)];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 av = *reinterpret_cast<const u32x4*>(krow + ks * 8);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                        __builtin_bit_cast(bf16x8, qv[ks]), acc,
-                                                        0, 0, 0);
-        }
-        s[mt] = acc;
-      }
-      // mask and scale: lane holds entries mt*16 + 4*gq + i for query row col
-      float tmax = -__builtin_huge_valf();
+      alpha = exp2f(m_run - m_new);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int e = mt * 16 + 4 * gq + i;
-          const bool ok = e < n_t && lds.slot[e] >= 0;
-          const float x = ok ? s[mt][i] * a.scale_log2 : -__builtin_huge_valf();
-          s[mt][i] = x;
-          tmax = fmaxf(tmax, x);
+          p[mt][i] = exp2f(s[mt][i] - m_new);
+          psum += p[mt][i];
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      float alpha = 1.0f;
-      float psum = 0.0f;
-      float p[2][4];
-      if (m_new == -__builtin_huge_valf()) {
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    // rescale O: its rows are 4*gq + i; query row x's statistics sit in lane x
+    float al[4];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * gq + i, 64);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[mt][i] = 0.0f;
-      } else {
-        alpha = exp2f(m_run - m_new);
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[mt][i] = exp2f(s[mt][i] - m_new);
-            psum += p[mt][i];
-          }
-      }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      // rescale O: its rows are 4*gq + i; query row x's statistics sit in lane x
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * gq + i, 64);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) O[t][i] *= al[i];
+      for (int i = 0; i < 4; ++i) O[tt][i] *= al[i];
 
-      // 4. P as the A operand: k-slot 8*gq + i <-> entry (i<4 ? 4gq+i : 16+4gq+i-4)
-      u32x4 pa;
-      pa[0] = pack_bf16x2(p[0][0], p[0][1]);
-      pa[1] = pack_bf16x2(p[0][2], p[0][3]);
-      pa[2] = pack_bf16x2(p[1][0], p[1][1]);
-      pa[3] = pack_bf16x2(p[1][2], p[1][3]);
-      const bf16x8 pab = __builtin_bit_cast(bf16x8, pa);
-      const uint16_t* vbase = KV == KV_SEPARATE ? lds.v : lds.k;
-      constexpr int VR = KV == KV_SEPARATE ? L::VROW : L::KROW;
+    // P as the A operand: k-slot 8*gq + i <-> entry (i<4 ? 4gq+i : 16+4gq+i-4)
+    u32x4 pa;
+    pa[0] = pack_bf16x2(p[0][0], p[0][1]);
+    pa[1] = pack_bf16x2(p[0][2], p[0][3]);
+    pa[2] = pack_bf16x2(p[1][0], p[1][1]);
+    pa[3] = pack_bf16x2(p[1][2], p[1][3]);
+    const bf16x8 pab = __builtin_bit_cast(bf16x8, pa);
+    const uint16_t* vbase = KV == KV_SEPARATE ? lds.v[buf] : kb;
+    constexpr int VR = KV == KV_SEPARATE ? L::VROW : L::KROW;
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        u32x4 R[8];
+    for (int jb = 0; jb < NJB; ++jb) {
+      u32x4 R[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int e = i < 4 ? 4 * gq + i : 16 + 4 * gq + (i - 4);
-          R[i] = *reinterpret_cast<const u32x4*>(vbase + e * VR + jb * 128 + col * 8);
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int e = i < 4 ? 4 * gq + i : 16 + 4 * gq + (i - 4);
+        R[i] = *reinterpret_cast<const u32x4*>(vbase + e * VR + jb * 128 + col * 8);
+      }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          u32x4 b;
+      for (int j = 0; j < 8; ++j) {
+        u32x4 b;
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-            b[qd] = (j & 1) ? hi16x2(R[2 * qd][j >> 1], R[2 * qd + 1][j >> 1])
-                            : lo16x2(R[2 * qd][j >> 1], R[2 * qd + 1][j >> 1]);
-          O[jb * 8 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              pab, __builtin_bit_cast(bf16x8, b), O[jb * 8 + j], 0, 0, 0);
-        }
+        for (int qd = 0; qd < 4; ++qd)
+          b[qd] = (j & 1) ? hi16x2(R[2 * qd][j >> 1], R[2 * qd + 1][j >> 1])
+                          : lo16x2(R[2 * qd][j >> 1], R[2 * qd + 1][j >> 1]);
+        O[jb * 8 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            pab, __builtin_bit_cast(bf16x8, b), O[jb * 8 + j], 0, 0, 0);
       }
     }
-    __syncthreads();
+  };
+
+  // Prefetch ring: tile t's rows are loaded D tiles ahead of their use.
+  T ring[D];
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (u < ntiles) load_tile(u, ring[u]);
+  for (int tb = 0; tb < ntiles; tb += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int t = tb + u;
+      if (t < ntiles) {
+        store_tile(ring[u], t & 1);
+        __syncthreads();
+        if (t + D < ntiles) load_tile(t + D, ring[u]);
+        if (active) compute(t & 1, t);
+      }
+    }
   }
 
   if (!active) return;
@@ -445,15 +493,14 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
                                : -__builtin_huge_valf();
 }
 
-template <int DQK, int DV, int KV>
+template <int DQK, int DV, int KV, int D>
 hipError_t launch_mfma_attn(const AttnArgs& a, hipStream_t s) {
   const int G = a.hq / a.hkv;
   const int tiles = (a.n_qsets * G + 15) / 16;
-  const int nw = tiles < kMaxW ? tiles : kMaxW;
-  const int groups = (tiles + nw - 1) / nw;
+  const int groups = (tiles + kNW - 1) / kNW;
   const int per = ((a.max_entries + a.n_split - 1) / a.n_split + kTile - 1) / kTile * kTile;
   dim3 grid(a.n_split, a.rows.n_rows * a.hkv, groups);
-  hipLaunchKernelGGL((attn_mfma<DQK, DV, KV>), grid, dim3(64 * nw), 0, s, a, per);
+  hipLaunchKernelGGL((attn_mfma<DQK, DV, KV, D>), grid, dim3(64 * kNW), 0, s, a, per);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const int64_t nrows = (int64_t)a.n_qsets * a.rows.n_rows * a.hq;
@@ -470,11 +517,13 @@ void attn_plan(AttnArgs& a) {
   if (a.dtype == 0) return;
   const int G = a.hq / a.hkv;
   const int tiles = (a.n_qsets * G + 15) / 16;
-  const int nw = tiles < kMaxW ? tiles : kMaxW;
-  const int64_t base = (int64_t)a.rows.n_rows * a.hkv * ((tiles + nw - 1) / nw);
+  const int64_t base = (int64_t)a.rows.n_rows * a.hkv * ((tiles + kNW - 1) / kNW);
   const int max_split = (a.max_entries + kTile - 1) / kTile;
-  int ns = 1;
-  while (ns < max_split && base * ns < 512) ++ns;
+  // enough entry ranges to occupy the chip, each within the slot table
+  int ns = (a.max_entries + kMaxEntries - 1) / kMaxEntries;
+  // wide value rows make split partials expensive: stop earlier
+  const int cap = a.dv >= 512 ? 4 : max_split;
+  while (ns < max_split && ns < cap && base * ns < 256) ++ns;
   a.n_split = ns < 1 ? 1 : ns;
 }
 
@@ -493,14 +542,14 @@ hipError_t launch_attn_gather(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.kv_kind == KV_SEPARATE) {
-    if (a.dqk == 128 && a.dv == 128) return launch_mfma_attn<128, 128, KV_SEPARATE>(a, s);
-    if (a.dqk == 256 && a.dv == 256) return launch_mfma_attn<256, 256, KV_SEPARATE>(a, s);
+    if (a.dqk == 128 && a.dv == 128) return launch_mfma_attn<128, 128, KV_SEPARATE, 4>(a, s);
+    if (a.dqk == 256 && a.dv == 256) return launch_mfma_attn<256, 256, KV_SEPARATE, 2>(a, s);
   } else if (a.kv_kind == KV_SHARED) {
-    if (a.dqk == 576 && a.dv == 512) return launch_mfma_attn<576, 512, KV_SHARED>(a, s);
-    if (a.dqk == 512 && a.dv == 512) return launch_mfma_attn<512, 512, KV_SHARED>(a, s);
-    if (a.dqk == 128 && a.dv == 128) return launch_mfma_attn<128, 128, KV_SHARED>(a, s);
+    if (a.dqk == 576 && a.dv == 512) return launch_mfma_attn<576, 512, KV_SHARED, 2>(a, s);
+    if (a.dqk == 512 && a.dv == 512) return launch_mfma_attn<512, 512, KV_SHARED, 2>(a, s);
+    if (a.dqk == 128 && a.dv == 128) return launch_mfma_attn<128, 128, KV_SHARED, 4>(a, s);
   } else if (a.kv_kind == KV_FP4) {
-    if (a.dqk == 512 && a.dv == 512) return launch_mfma_attn<512, 512, KV_FP4>(a, s);
+    if (a.dqk == 512 && a.dv == 512) return launch_mfma_attn<512, 512, KV_FP4, 4>(a, s);
   }
   return hipErrorInvalidValue;
 }

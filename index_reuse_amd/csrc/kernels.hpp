@@ -45,7 +45,10 @@ struct SelectArgs {
   int32_t* pool;
   int32_t* pool_count;
   int32_t max_elems;  // upper bound on elements per row (picks the block size)
+  float* beta;        // pool mode: block maxima [R][beta_stride] (workspace)
+  int64_t beta_stride;
 };
+size_t topk_workspace_bytes(const SelectArgs& a);
 hipError_t launch_topk_select(const SelectArgs& a, hipStream_t s);
 
 // --------------------------------------------------------------- attention

@@ -19,7 +19,8 @@ from typing import List, Optional
 
 import torch
 
-from .binding import Cache, Rows, attn_gather_fwd, index_score, topk_select
+from .binding import (Cache, Rows, attn_gather_fwd, index_score, prepare_attn_gather_fwd,
+                      prepare_index_score, prepare_topk_select, topk_select)
 
 
 def _cache(c, heads, width, fp4=False) -> Cache:
@@ -76,6 +77,36 @@ class Step:
             self.o.append(torch.empty(q.shape[0], R, wl.hq, wl.dv, dtype=q.dtype, device=dev))
             self.lse.append(torch.empty(q.shape[0], R, wl.hq, dtype=f32, device=dev))
         self.scale = wl.dqk ** -0.5
+        self._prepared = None
+
+    def prepare(self):
+        """Build the launch-only call list of one step (index calls, then
+        attention calls); returns [(name, callable), ...]."""
+        if self._prepared is not None:
+            return self._prepared
+        p, wl = self.prob, self.wl
+        calls = [("index_score", prepare_index_score(self.rows, p.idx_q[0], p.idx_w[0], self.kidx,
+                                                     self.scores[0]))]
+        if not wl.block:
+            calls.append(("topk_select", prepare_topk_select(self.rows, self.scores[0], wl.k,
+                                                             self.idx[0], self.count[0])))
+        else:
+            calls.append(("topk_select", prepare_topk_select(
+                self.rows, self.scores[0], wl.k, self.idx[0], self.count[0], block=wl.block,
+                max_blocks=wl.max_blocks, pool=self.pool, pool_count=self.pool_count)))
+            calls.append(("index_score_reindex", prepare_index_score(
+                self.rows, p.idx_q[1], p.idx_w[1], self.kidx, self.scores[1], cand=self.pool,
+                cand_count=self.pool_count)))
+            calls.append(("topk_select_reindex", prepare_topk_select(
+                self.rows, self.scores[1], wl.k, self.idx[1], self.count[1], cand=self.pool,
+                cand_count=self.pool_count)))
+        for c, q in enumerate(p.q):
+            calls.append(("attn_gather_fwd" + ("" if c == 0 else "_%d" % c),
+                          prepare_attn_gather_fwd(self.rows, q, self.k, self.v, self.idx[c],
+                                                  self.count[c], self.o[c], self.lse[c],
+                                                  self.scale, wl.dv)))
+        self._prepared = calls
+        return calls
 
     def run_index(self):
         p, wl = self.prob, self.wl

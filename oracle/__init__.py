@@ -110,14 +110,14 @@ def _ptr(a: np.ndarray):
 
 def unpage(pool: torch.Tensor, block_table, page_size: int, n_seqs: int, cap: int) -> torch.Tensor:
     """Logical view [n_seqs, cap, ...] of a paged pool (CPU copy)."""
-    pool = pool.detach().cpu()
+    pool = pool.detach()
     if block_table is None:
-        return pool[:n_seqs, :cap].contiguous()
-    bt = block_table.detach().cpu().long()
+        return pool[:n_seqs, :cap].cpu().contiguous()
+    bt = block_table.detach().to(pool.device).long()
     pages = -(-cap // page_size)
     out = pool[bt[:n_seqs, :pages]]  # [n_seqs, pages, page_size, ...]
     out = out.reshape(n_seqs, pages * page_size, *pool.shape[2:])
-    return out[:, :cap].contiguous()
+    return out[:, :cap].cpu().contiguous()
 
 
 def n_avail(seq_of_row, pos_of_row, seq_len, stride: int) -> np.ndarray:
