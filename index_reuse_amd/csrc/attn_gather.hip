@@ -18,10 +18,12 @@
 //      v_mfma_f32_16x16x32_bf16 (entries on M, query rows on N), so each lane
 //      ends up holding 8 logits of ONE query row;
 //   3. online softmax in fp32 (exp2 domain), per query row;
-//   4. O += P . V with the contraction order permuted so that the lane's 8
-//      probabilities are directly its A operand; the V operand is built from
-//      16-byte LDS reads by an in-register 8x8 bf16 transpose (v_perm), with
-//      output columns interleaved so each lane owns 8 contiguous channels.
+//   4. O^T += V^T . P^T with the contraction order permuted so that the
+//      lane's 8 probabilities are directly its B operand; the V^T operand is
+//      built from 16-byte LDS reads by an in-register 8x8 bf16 transpose
+//      (v_perm).  O^T keeps each lane on one query row, so the online-softmax
+//      rescale and the final normalisation need no cross-lane traffic;
+//      row statistics are reduced with the gfx950 lane-swap instructions.
 // Long entry lists are split across workgroups; a combine kernel merges the
 // (max, sum, unnormalised O) partials.  F32 inputs use a plain VALU kernel.
 #include "kernels.hpp"
@@ -71,7 +73,7 @@ struct AttnLds {
   static constexpr bool HAS_V = KV == KV_SEPARATE;
   uint16_t k[2][kTile * KROW];
   uint16_t v[2][HAS_V ? kTile * VROW : 1];
-  int32_t slot[kMaxEntries];  // cache slot of every entry of the range (-1: none)
+  int32_t slot[kMaxEntries + 8 * kTile];  // cache slot of every entry (-1: none)
 };
 
 // Per-thread share of one tile of gathered rows, held in registers between
@@ -119,8 +121,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_spl
   const int32_t* idx = a.idx ? a.idx + (int64_t)r * a.idx_stride : nullptr;
 
   // Cache slot of every entry of this range, once: the window entries, then
-  // the selected ones, through the block table.  Padding to whole tiles is -1.
-  for (int i = tid; i < ntiles * kTile; i += NTH) {
+  // the selected ones, through the block table.  Padding to whole tiles, and
+  // the D tiles past the end that the prefetch ring reads, are -1.
+  for (int i = tid; i < (ntiles + D) * kTile; i += NTH) {
     int slot = -1;
     if (i < ne) {
       const int e = e0 + i;
@@ -148,59 +151,59 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_spl
   }
   __syncthreads();
 
-  // Issue the global loads of tile t into registers.
+  // Issue the global loads of tile t into registers.  Branch-free, so the
+  // compiler can keep D tiles of loads in flight: an entry without a slot
+  // reads slot 0 (always backed by the cache) and is zeroed at store time.
   auto load_tile = [&](int t, T& regs) {
 #pragma unroll
     for (int u = 0; u < T::U; ++u) {
-      const int c = tid + NTH * u;
-      u32x4 val = u32x4{0, 0, 0, 0};
-      uint32_t scl = 0u;
-      if (c < T::C_ALL) {
-        const bool is_k = c < T::C_K;
-        const int cc = is_k ? c : c - T::C_K;
-        const int cpr = is_k ? T::CPR_K : T::CPR_V;
-        const int e = cc / cpr, part = cc % cpr;
-        const int slot = lds.slot[t * kTile + e];
-        if (slot >= 0) {
-          if constexpr (T::FP4) {
-            val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                a.k.data + (int64_t)slot * a.k.row_stride + g * (DQK / 2) + part * 16));
-            scl = *reinterpret_cast<const uint16_t*>(a.k.scale + (int64_t)slot * a.k.scale_stride +
-                                                     g * (DQK / 16) + part * 2);
-          } else if (is_k) {
-            val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                a.k.data + (int64_t)slot * a.k.row_stride + g * (DQK * 2) + part * 16));
-          } else {
-            val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                a.v.data + (int64_t)slot * a.v.row_stride + g * (DV * 2) + part * 16));
-          }
-        }
+      int c = tid + NTH * u;
+      if (T::C_ALL % NTH != 0) c = min(c, T::C_ALL - 1);
+      const bool is_k = c < T::C_K;
+      const int cc = is_k ? c : c - T::C_K;
+      const int cpr = is_k ? T::CPR_K : T::CPR_V;
+      const int e = cc / cpr, part = cc % cpr;
+      const int64_t slot = max(lds.slot[t * kTile + e], 0);
+      if constexpr (T::FP4) {
+        regs.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            a.k.data + slot * a.k.row_stride + g * (DQK / 2) + part * 16));
+        regs.sc[u] = *reinterpret_cast<const uint16_t*>(a.k.scale + slot * a.k.scale_stride +
+                                                        g * (DQK / 16) + part * 2);
+      } else {
+        const char* base = is_k ? a.k.data + slot * a.k.row_stride + g * (DQK * 2)
+                                : a.v.data + slot * a.v.row_stride + g * (DV * 2);
+        regs.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + part * 16));
       }
-      regs.v[u] = val;
-      if constexpr (T::FP4) regs.sc[u] = scl;
     }
   };
-  // Store a tile's registers into LDS buffer `buf` (FP4 is dequantised here).
-  auto store_tile = [&](const T& regs, int buf) {
+  // Store tile t's registers into LDS buffer `buf` (FP4 is dequantised here);
+  // rows of entries without a slot become zeros.
+  auto store_tile = [&](const T& regs, int buf, int t) {
 #pragma unroll
     for (int u = 0; u < T::U; ++u) {
       const int c = tid + NTH * u;
-      if (c >= T::C_ALL) continue;
+      if (T::C_ALL % NTH != 0 && c >= T::C_ALL) continue;
       if constexpr (T::FP4) {
         const int e = c / T::CPR_K, part = c % T::CPR_K;
+        const bool ok = lds.slot[t * kTile + e] >= 0;
         uint32_t vals[16];
         fp4_dequant32(regs.v[u], regs.sc[u] & 0xFFu, regs.sc[u] >> 8, vals);
         u32x4* dst = reinterpret_cast<u32x4*>(&lds.k[buf][e * L::KROW + part * 32]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          dst[i] = u32x4{vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]};
+          dst[i] = ok ? u32x4{vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]}
+                      : u32x4{0, 0, 0, 0};
       } else if (c < T::C_K) {
         const int e = c / T::CPR_K, part = c % T::CPR_K;
-        *reinterpret_cast<u32x4*>(&lds.k[buf][e * L::KROW + part * 8]) = regs.v[u];
+        const bool ok = lds.slot[t * kTile + e] >= 0;
+        *reinterpret_cast<u32x4*>(&lds.k[buf][e * L::KROW + part * 8]) =
+            ok ? regs.v[u] : u32x4{0, 0, 0, 0};
       } else {
         const int cc = c - T::C_K;
         const int e = cc / T::CPR_V, part = cc % T::CPR_V;
-        *reinterpret_cast<u32x4*>(&lds.v[buf][e * L::VROW + part * 8]) = regs.v[u];
+        const bool ok = lds.slot[t * kTile + e] >= 0;
+        *reinterpret_cast<u32x4*>(&lds.v[buf][e * L::VROW + part * 8]) =
+            ok ? regs.v[u] : u32x4{0, 0, 0, 0};
       }
     }
   };
@@ -239,8 +242,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_spl
         s[mt][i] = x;
         tmax = fmaxf(tmax, x);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = xor16_32_max(tmax);
     const float m_new = fmaxf(m_run, tmax);
     float alpha = 1.0f;
     float psum = 0.0f;
@@ -260,20 +262,16 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_spl
           psum += p[mt][i];
         }
     }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
+    psum = xor16_32_sum(psum);
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    // rescale O: its rows are 4*gq + i; query row x's statistics sit in lane x
-    float al[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * gq + i, 64);
+    // O^T holds only this lane's query row (col): the rescale is lane-local
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) O[tt][i] *= al[i];
+      for (int i = 0; i < 4; ++i) O[tt][i] *= alpha;
 
-    // P as the A operand: k-slot 8*gq + i <-> entry (i<4 ? 4gq+i : 16+4gq+i-4)
+    // P^T as the B operand: k-slot 8*gq + i <-> entry (i<4 ? 4gq+i : 16+4gq+i-4)
     u32x4 pa;
     pa[0] = pack_bf16x2(p[0][0], p[0][1]);
     pa[1] = pack_bf16x2(p[0][2], p[0][3]);
@@ -284,6 +282,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_spl
     constexpr int VR = KV == KV_SEPARATE ? L::VROW : L::KROW;
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
+      // V^T as the A operand: lane col takes channels 128jb + 8col + j of the
+      // 8 entries of its k-slots (an 8x8 bf16 transpose in registers), so
+      // M-tile 8jb + j row m is channel 128jb + 8m + j.
       u32x4 R[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -298,49 +299,52 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_spl
           b[qd] = (j & 1) ? hi16x2(R[2 * qd][j >> 1], R[2 * qd + 1][j >> 1])
                           : lo16x2(R[2 * qd][j >> 1], R[2 * qd + 1][j >> 1]);
         O[jb * 8 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            pab, __builtin_bit_cast(bf16x8, b), O[jb * 8 + j], 0, 0, 0);
+            __builtin_bit_cast(bf16x8, b), pab, O[jb * 8 + j], 0, 0, 0);
       }
     }
   };
 
-  // Prefetch ring: tile t's rows are loaded D tiles ahead of their use.
+  // Prefetch ring: tile t's rows are loaded D tiles ahead of their use.  Full
+  // groups of D tiles run without guards (D is even, so the LDS buffer of
+  // each unrolled step is static); the last partial group is guarded.
+  static_assert(D % 2 == 0, "prefetch depth must be even");
   T ring[D];
 #pragma unroll
-  for (int u = 0; u < D; ++u)
-    if (u < ntiles) load_tile(u, ring[u]);
-  for (int tb = 0; tb < ntiles; tb += D) {
+  for (int u = 0; u < D; ++u) load_tile(u, ring[u]);
+  int t0 = 0;
+  for (; t0 + D <= ntiles; t0 += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      const int t = tb + u;
-      if (t < ntiles) {
-        store_tile(ring[u], t & 1);
-        __syncthreads();
-        if (t + D < ntiles) load_tile(t + D, ring[u]);
-        if (active) compute(t & 1, t);
-      }
+      store_tile(ring[u], u & 1, t0 + u);
+      __syncthreads();
+      load_tile(t0 + u + D, ring[u]);
+      if (active) compute(u & 1, t0 + u);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    if (t0 + u < ntiles) {
+      store_tile(ring[u], u & 1, t0 + u);
+      __syncthreads();
+      if (active) compute(u & 1, t0 + u);
     }
   }
 
   if (!active) return;
-  // Output: lane holds O[row 4*gq + i][channel 128*jb + 8*col + j] in O[8jb+j][i].
-  float lrow[4], mrow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lrow[i] = __shfl(l_run, 4 * gq + i, 64);
-    mrow[i] = __shfl(m_run, 4 * gq + i, 64);
-  }
+  // Output: lane holds O^T for query row qrow0 + col: O[8jb + j][i] is channel
+  // 128jb + 8(4gq + i) + j, so each (jb, i) is 8 contiguous channels.
+  const int qr = qrow0 + col;
+  if (qr >= Mq) return;
   const int R = a.rows.n_rows;
+  const int set = qr / G, h = g * G + qr % G;
+  const int64_t orow = ((int64_t)set * R + r) * a.hq + h;
+  if (a.n_split == 1) {
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int qr = qrow0 + 4 * gq + i;
-    if (qr >= Mq) continue;
-    const int set = qr / G, h = g * G + qr % G;
-    const int64_t orow = ((int64_t)set * R + r) * a.hq + h;
-    if (a.n_split == 1) {
-      const float inv = lrow[i] > 0.0f ? 1.0f / lrow[i] : 0.0f;
+    for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        const int c0 = jb * 128 + col * 8;
+      for (int i = 0; i < 4; ++i) {
+        const int c0 = jb * 128 + 32 * gq + 8 * i;
         if (a.o_dtype == 1) {
           u32x4 pk;
 #pragma unroll
@@ -357,25 +361,26 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_spl
           reinterpret_cast<f32x4*>(op)[1] = v1;
         }
       }
-      if (a.lse && col == 0)
-        a.lse[orow] = lrow[i] > 0.0f ? (mrow[i] + __log2f(lrow[i])) * 0.6931471805599453f
-                                     : -__builtin_huge_valf();
-    } else {
-      const int64_t nrows = (int64_t)a.n_qsets * R * a.hq;
-      float* po = a.part + ((int64_t)sp * nrows + orow) * DV;
+    if (a.lse && gq == 0)
+      a.lse[orow] = l_run > 0.0f ? (m_run + __log2f(l_run)) * 0.6931471805599453f
+                                 : -__builtin_huge_valf();
+  } else {
+    const int64_t nrows = (int64_t)a.n_qsets * R * a.hq;
+    float* po = a.part + ((int64_t)sp * nrows + orow) * DV;
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        float* op = po + jb * 128 + col * 8;
+    for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float* op = po + jb * 128 + 32 * gq + 8 * i;
         f32x4 v0 = {O[jb * 8 + 0][i], O[jb * 8 + 1][i], O[jb * 8 + 2][i], O[jb * 8 + 3][i]};
         f32x4 v1 = {O[jb * 8 + 4][i], O[jb * 8 + 5][i], O[jb * 8 + 6][i], O[jb * 8 + 7][i]};
         reinterpret_cast<f32x4*>(op)[0] = v0;
         reinterpret_cast<f32x4*>(op)[1] = v1;
       }
-      if (col == 0) {
-        float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 2;
-        ml[0] = mrow[i];
-        ml[1] = lrow[i];
-      }
+    if (gq == 0) {
+      float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 2;
+      ml[0] = m_run;
+      ml[1] = l_run;
     }
   }
 }

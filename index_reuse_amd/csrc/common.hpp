@@ -141,6 +141,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Butterfly reductions across the four 16-lane groups of a wave with the
+// gfx950 lane-swap VALU instructions (no LDS round trip): after the two
+// steps every lane holds the reduction over lanes {l, l^16, l^32, l^48}.
+__device__ __forceinline__ float xor16_32_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xor16_32_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 }  // namespace sa

@@ -134,8 +134,7 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
 #pragma unroll
         for (int i = 0; i < 4; ++i) part = fmaf(wv[mt][i], fmaxf(acc[i], 0.0f), part);
       }
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
+      part = xor16_32_sum(part);
       res[t] = valid ? part : -__builtin_huge_valf();
     }
     // lane l stores the result of slot base + l (tile l/16, column l%16)
