@@ -194,6 +194,11 @@ typedef struct {
  *   pool        [R][pool_stride] int32 out, pool_stride >= max_blocks*block;
  *               pool_count [R] out
  * Scores must not be NaN.
+ *
+ * Workspace: sa_workspace_size(SA_OP_TOPK_SELECT, desc) bytes that must be
+ * zero-filled before the first call and are not shared with other entry
+ * points; every call leaves its histogram area zero-filled again.  Calls that
+ * overlap in time need distinct workspaces.
  */
 typedef struct {
   sa_rows rows;

@@ -172,14 +172,17 @@ def _cache_struct(c: Cache) -> sa_cache:
 _ws_cache = {}
 
 
-def workspace(nbytes: int, device) -> Optional[torch.Tensor]:
-    """A cached device workspace of at least ``nbytes`` bytes."""
+def workspace(nbytes: int, device, op: int) -> Optional[torch.Tensor]:
+    """A cached, zero-filled-at-allocation device workspace of at least
+    ``nbytes`` bytes, private to entry point ``op`` (the selection keeps its
+    workspace zero-filled between calls; other ops leave scratch behind)."""
     if nbytes == 0:
         return None
-    key = torch.device(device).index
+    # the selection's layout depends on its descriptor: one buffer per size
+    key = (torch.device(device).index, op, nbytes if op == SA_OP_TOPK_SELECT else 0)
     t = _ws_cache.get(key)
     if t is None or t.numel() < nbytes:
-        t = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        t = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _ws_cache[key] = t
     return t
 
@@ -234,7 +237,7 @@ def topk_select(rows: Rows, scores: torch.Tensor, k: int, cand=None, cand_count=
     need = int(L.sa_workspace_size(SA_OP_TOPK_SELECT, ctypes.byref(d)))
     if need == ctypes.c_size_t(-1).value:
         _check(-2)
-    ws = workspace(need, scores.device)
+    ws = workspace(need, scores.device, SA_OP_TOPK_SELECT)
     _check(L.sparse_topk_select(ctypes.byref(d), _ptr(ws), need, _stream()))
     if block > 0:
         return idx, count, pool, pool_count
@@ -273,7 +276,7 @@ def attn_gather_fwd(rows: Rows, q: torch.Tensor, k: Cache, v: Optional[Cache] = 
     need = int(L.sa_workspace_size(SA_OP_ATTN_GATHER_FWD, ctypes.byref(d)))
     if need == ctypes.c_size_t(-1).value:
         _check(-2)
-    ws = workspace(need, q.device)
+    ws = workspace(need, q.device, SA_OP_ATTN_GATHER_FWD)
     _check(L.sparse_attn_gather_fwd(ctypes.byref(d), _ptr(ws), need, _stream()))
     return o, lse
 
@@ -296,7 +299,8 @@ class Prepared:
         need = int(L.sa_workspace_size(op, self.ref))
         if need == ctypes.c_size_t(-1).value:
             _check(-2)
-        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device) if need else None
+        # zero-filled: the selection requires it on first use
+        self.ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=device) if need else None
         self.ws_ptr = _ptr(self.ws)
         self.need = need
         self.keep = keep

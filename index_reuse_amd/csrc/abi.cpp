@@ -8,7 +8,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/sparse_attn.h"
+#include "sparse_attn.h"
 #include "kernels.hpp"
 
 namespace {
@@ -167,6 +167,8 @@ sa_status validate_topk(const sa_topk_desc* d, sa::SelectArgs* out) {
           "%s: need 1 <= cand_stride <= score_stride", op);
     CHECK(!pool, SA_ERR_UNSUPPORTED, "%s: the block pool needs full-domain scores", op);
   }
+  CHECK(d->score_stride <= (1 << 21), SA_ERR_UNSUPPORTED,
+        "%s: at most 2097152 elements per row", op);
   if (pool) {
     CHECK(d->pool_count, SA_ERR_NULL, "%s: pool_count is required with pool", op);
     CHECK(d->block >= 1 && d->max_blocks >= 1, SA_ERR_SHAPE,

@@ -7,19 +7,20 @@
 // scored by its maximum over visible members, the first max_blocks blocks in
 // (max desc, block asc) order are kept and their members form the pool.
 //
-// One workgroup per row.  Scores become order-preserving uint32 keys (-0
-// folded onto +0).  The kept set is {key > theta} plus the elements with
-// key == theta up to index jstar, where (theta, jstar) is the take-th element
-// of the total order.  It is found without sorting:
-//   1. each thread holds the keys of a contiguous index range in registers;
-//   2. a 2048-bin histogram linear in score over the row's [min, max] (a
-//      monotone map that spreads real score distributions over many bins and
-//      keeps LDS atomic contention low) locates the bin of the take-th key;
-//   3. the few elements of that bin are gathered into LDS and ranked exactly
-//      by (key desc, index asc); a crowded bin (heavy ties) falls back to an
-//      exact 8-bit radix refinement restricted to that bin;
-//   4. an ordered compaction (block prefix sums over the contiguous ranges)
-//      writes the kept indices ascending.
+// Scores become order-preserving uint32 keys (-0 folded onto +0).  The kept
+// set is {key > theta} plus the elements with key == theta up to index jstar,
+// where (theta, jstar) is the take-th element of the total order.  Decode
+// rows are few and long, so the per-element work is spread over chunks of
+// 2048 elements on many workgroups and only a small per-row step is serial:
+//   1. hist (chunks x rows): a histogram of the top 12 key bits of every
+//      chunk, merged into the row's histogram with global atomics;
+//   2. threshold (one workgroup per row): the bin of the take-th key; one
+//      light pass over the row counts, per chunk, the keys above that bin and
+//      gathers the bin's few keys into LDS; a second 12-bit level and an
+//      exact comparison rank give (theta, jstar); per-chunk kept counts give
+//      each chunk its output offset;
+//   3. emit (chunks x rows): each chunk writes its kept indices ascending at
+//      its offset (wave-contiguous segments, ballot ranks).
 // The output depends only on the total order, never on thread timing.
 #include "kernels.hpp"
 
@@ -27,389 +28,162 @@ namespace sa {
 
 namespace {
 
-constexpr int kBins = 2048;
-constexpr int kCap = 2048;      // LDS slots (threshold-bin elements, kept blocks)
-constexpr int kRankMax = 512;   // largest threshold bin ranked by direct comparison
+// ---------------------------------------------------------------- wave ops
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+// row_ror:1/2/4/8 reduce within 16-lane rows; the lane swaps combine rows
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp<0x121>(v));
+  v = max(v, dpp<0x122>(v));
+  v = max(v, dpp<0x124>(v));
+  v = max(v, dpp<0x128>(v));
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(a[0], a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(b[0], b[1]);
+}
+__device__ __forceinline__ int wave_sum_i32(int x) {
+  uint32_t v = (uint32_t)x;
+  v += dpp<0x121>(v);
+  v += dpp<0x122>(v);
+  v += dpp<0x124>(v);
+  v += dpp<0x128>(v);
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = a[0] + a[1];
+  auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (int)(b[0] + b[1]);
+}
+// inclusive prefix sum over the 64 lanes (a few calls per kernel)
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+__device__ __forceinline__ uint64_t lanes_below() {
+  const int lane = threadIdx.x & 63;
+  return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+// ------------------------------------------------------------------ layout
+constexpr int kL1Bits = 12;            // level-1 digit: key bits 31..20
+constexpr int kL1 = 1 << kL1Bits;      // level-1 bins
+constexpr int kL2 = 4096;              // level-2 bins: key bits 19..8
+constexpr int kCap1 = 8192;            // LDS slots for the level-1 bin's keys
+constexpr int kRankMax = 512;          // largest level-2 bin ranked by comparison
+constexpr int kChunk = 2048;           // elements per chunk workgroup
+constexpr int kChunkT = 256;           // threads per chunk workgroup
+constexpr int kTT = 1024;              // threads of the per-row threshold workgroup
+constexpr int kTW = kTT / 64;
+constexpr int kMaxChunks = 1024;       // chunks per row (2M elements)
+constexpr int kHistStride = kL1 + 64;  // per-row histogram words (+ valid count)
+constexpr int kThrWords = 8;           // per-row results: theta, jstar, take, extra
+
+enum { SRC_TOKEN_FULL = 0, SRC_TOKEN_CAND = 1, SRC_BLOCK = 2, SRC_POOL = 3 };
 
 // Float value of an order-preserving key (inverse of order_key).
 __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-enum { SRC_TOKEN_FULL = 0, SRC_TOKEN_CAND = 1, SRC_BLOCK = 2, SRC_POOL = 3 };
+// Workspace views (see topk_workspace_bytes).
+struct Ws {
+  uint32_t* hist;    // [R][kHistStride], zero on entry, left zero
+  uint32_t* thr;     // [R][kThrWords]
+  int32_t* offs;     // [R][chunk_stride] output offset of every chunk
+  float* beta;       // [R][beta_stride] block maxima (pool mode)
+  int64_t chunk_stride;
+};
 
+// ----------------------------------------------------------------- sources
 // The elements being ranked (KIND fixes how an element's key is formed).
 // key() == 0 marks an element that can never be kept: every real score maps
 // to a key >= order_key(-inf) > 0.
 template <int KIND>
 struct Src {
-  const float* sc;      // this row's scores
+  const float* sc;      // scores (block maxima for SRC_BLOCK)
   const int32_t* list;  // candidate list (SRC_TOKEN_CAND) or pool (SRC_POOL)
   int n;                // elements
   int win_lo;           // kept tokens must lie below this entry
-  int n_avail;
-  int block;
 
   __device__ __forceinline__ uint32_t key(int j) const {
-    if constexpr (KIND == SRC_TOKEN_FULL) {
+    if constexpr (KIND == SRC_TOKEN_FULL || KIND == SRC_BLOCK) {
       return order_key(sc[j]);
     } else if constexpr (KIND == SRC_TOKEN_CAND) {
       const int p = list[j];
       return (p >= 0 && p < win_lo) ? order_key(sc[j]) : 0u;
-    } else if constexpr (KIND == SRC_POOL) {
+    } else {
       const int p = list[j];
-      return (p >= 0 && p < win_lo) ? order_key(sc[p]) : 0u;
-    } else {  // SRC_BLOCK: sc holds the row's block maxima
-      return order_key(sc[j]);
+      const bool ok = p >= 0 && p < win_lo;
+      return ok ? order_key(sc[ok ? p : 0]) : 0u;
     }
+  }
+  // key(j) for any j >= 0, with key 0 past the end: the index is clamped so
+  // the loads are unconditional (branch-free code keeps them in flight
+  // together).  Needs n >= 1.
+  __device__ __forceinline__ uint32_t key_c(int j) const {
+    const int jc = min(j, n - 1);
+    uint32_t k;
+    if constexpr (KIND == SRC_TOKEN_FULL || KIND == SRC_BLOCK) {
+      k = order_key(sc[jc]);
+    } else if constexpr (KIND == SRC_TOKEN_CAND) {
+      const int p = list[jc];
+      const float x = sc[jc];
+      k = (p >= 0 && p < win_lo) ? order_key(x) : 0u;
+    } else {
+      const int p = list[jc];
+      const bool ok = p >= 0 && p < win_lo;
+      const float x = sc[ok ? p : 0];
+      k = ok ? order_key(x) : 0u;
+    }
+    return j < n ? k : 0u;
   }
   static constexpr bool may_be_invalid() {
     return KIND == SRC_TOKEN_CAND || KIND == SRC_POOL;
   }
-  // value written for a kept token element
   __device__ __forceinline__ int position(int j) const {
-    if constexpr (KIND == SRC_TOKEN_FULL) return j;
+    if constexpr (KIND == SRC_TOKEN_FULL || KIND == SRC_BLOCK) return j;
     else return list[j];
   }
 };
 
-template <int NT>
-struct Shared {
-  uint32_t hist[kBins];
-  uint32_t ckey[kCap];
-  int32_t cidx[kCap];
-  int cnt[NT];  // per (slot, wave) counts of an ordered pass (KPT * NT/64 <= NT)
-  int scan[NT / 64];
-  uint32_t u[8];
-};
-
-// Exclusive prefix sum over the workgroup; *total receives the sum.
-template <int NT>
-__device__ __forceinline__ int block_excl_scan(int v, int* total, int* sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
+template <int KIND>
+__device__ __forceinline__ Src<KIND> make_src(const SelectArgs& a, const Ws& ws, int r,
+                                              const RowInfo& ri) {
+  Src<KIND> s;
+  s.win_lo = ri.win_lo;
+  s.list = nullptr;
+  if constexpr (KIND == SRC_BLOCK) {
+    s.sc = ws.beta + (int64_t)r * a.beta_stride;
+    s.n = (ri.n_avail + a.block - 1) / a.block;
+    s.win_lo = ri.n_avail;
+  } else if constexpr (KIND == SRC_POOL) {
+    s.sc = a.scores + (int64_t)r * a.score_stride;
+    s.list = a.pool + (int64_t)r * a.pool_stride;
+    s.n = a.pool_count[r];
+  } else if constexpr (KIND == SRC_TOKEN_CAND) {
+    s.sc = a.scores + (int64_t)r * a.score_stride;
+    s.list = a.cand + (int64_t)r * a.cand_stride;
+    s.n = a.cand_count[r];
+  } else {
+    s.sc = a.scores + (int64_t)r * a.score_stride;
+    s.n = ri.win_lo;
   }
-  if (lane == 63) sh[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    int wv = lane < NT / 64 ? sh[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(wv, o, 64);
-      if (lane >= o) wv += y;
-    }
-    if (lane < NT / 64) sh[lane] = wv;
-  }
-  __syncthreads();
-  const int base = wave ? sh[wave - 1] : 0;
-  *total = sh[NT / 64 - 1];
-  __syncthreads();
-  return base + x - v;
+  return s;
 }
 
-template <int NT>
-__device__ __forceinline__ uint32_t block_reduce_max(uint32_t v, int* sh) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) sh[wave] = (int)v;
-  __syncthreads();
-  uint32_t r = 0;
-  for (int i = 0; i < NT / 64; ++i) r = max(r, (uint32_t)sh[i]);
-  __syncthreads();
-  return r;
+__device__ __forceinline__ bool kept(uint32_t theta, int jstar, uint32_t key, int j) {
+  return key != 0u && (key > theta || (key == theta && j <= jstar));
 }
 
-// One histogram increment per element, with a single atomic when the whole
-// wave hits one bin (massive ties).
-__device__ __forceinline__ void hist_add(uint32_t* hist, bool v, int bin) {
-  const uint64_t vm = __ballot(v);
-  if (vm == 0) return;
-  const int lead = __ffsll((unsigned long long)vm) - 1;
-  const int bl = __shfl(bin, lead, 64);
-  const uint64_t sm = __ballot(v && bin == bl);
-  if (sm == vm) {
-    if ((int)(threadIdx.x & 63) == lead) atomicAdd(&hist[bl], (uint32_t)__popcll(sm));
-  } else if (v) {
-    atomicAdd(&hist[bin], 1u);
-  }
-}
-
-struct Pick {
-  uint32_t theta;  // keep key > theta ...
-  int jstar;       // ... and key == theta with index <= jstar
-  int take;        // number kept
-};
-
-// Elements are striped over the workgroup: chunk c holds NT*KPT consecutive
-// elements and thread t owns elements c*NT*KPT + i*NT + t (i < KPT), so every
-// load instruction of a wave reads 64 consecutive scores.  When the row fits
-// in one chunk the keys stay in registers (kc[]); otherwise they are
-// recomputed from memory in every pass.
-template <int NT, int KPT, class S>
-struct Range {
-  int n, nchunks;
-  bool cached;
-  uint32_t kc[KPT];
-
-  __device__ __forceinline__ void init(const S& s) {
-    n = s.n;
-    nchunks = (n + NT * KPT - 1) / (NT * KPT);
-    cached = nchunks <= 1;
-    if (cached) {
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int j = i * NT + (int)threadIdx.x;
-        kc[i] = j < n ? s.key(j) : 0u;
-        // bound the loads in flight (a block key reads `block` scores)
-        if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-  // f(index, key, in_range) for every owned slot, in increasing index order
-  // per thread; the trip count is wave-uniform, so f may use wave collectives.
-  template <class F>
-  __device__ __forceinline__ void visit(const S& s, F f) const {
-    if (cached) {
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int j = i * NT + (int)threadIdx.x;
-        f(j, kc[i], j < n);
-      }
-    } else {
-      for (int c = 0; c < nchunks; ++c) {
-#pragma unroll 4
-        for (int i = 0; i < KPT; ++i) {
-          const int j = c * NT * KPT + i * NT + (int)threadIdx.x;
-          const bool in = j < n;
-          f(j, in ? s.key(j) : 0u, in);
-        }
-      }
-    }
-  }
-  // Calls emit(index, rank) for every owned element with sel(index, key)
-  // true, where rank is its position among all selected elements in
-  // increasing index order.  Returns the number selected.
-  template <class Sel, class Emit>
-  __device__ __forceinline__ int ordered(const S& s, Sel sel, Emit emit, int* cnt_lds,
-                                         int* scan_sh) const {
-    if (cached) return ordered_chunk<true>(s, 0, 0, sel, emit, cnt_lds, scan_sh);
-    int running = 0;
-    for (int c = 0; c < nchunks; ++c)
-      running = ordered_chunk<false>(s, c, running, sel, emit, cnt_lds, scan_sh);
-    return running;
-  }
-
-  template <bool CACHED, class Sel, class Emit>
-  __device__ __forceinline__ int ordered_chunk(const S& s, int c, int running, Sel sel,
-                                               Emit emit, int* cnt_lds, int* scan_sh) const {
-    constexpr int NW = NT / 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
-    uint32_t flags = 0u;  // selection bits of slots 0..31 (recomputed past 32)
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int j = c * NT * KPT + i * NT + (int)threadIdx.x;
-      const bool in = j < n;
-      uint32_t key;
-      if (CACHED)
-        key = kc[i];
-      else
-        key = in ? s.key(j) : 0u;
-      const bool me = in && sel(j, key);
-      if (i < 32 && me) flags |= 1u << i;
-      const uint64_t m = __ballot(me);
-      if (lane == 0) cnt_lds[i * NW + wave] = __popcll(m);
-    }
-    __syncthreads();
-    int total;
-    const int v = (int)threadIdx.x < KPT * NW ? cnt_lds[threadIdx.x] : 0;
-    const int ex = block_excl_scan<NT>(v, &total, scan_sh);
-    if ((int)threadIdx.x < KPT * NW) cnt_lds[threadIdx.x] = ex;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int j = c * NT * KPT + i * NT + (int)threadIdx.x;
-      bool me;
-      if (i < 32) {
-        me = (flags >> i) & 1u;
-      } else {
-        const bool in = j < n;
-        uint32_t key;
-        if (CACHED)
-          key = kc[i];
-        else
-          key = in ? s.key(j) : 0u;
-        me = in && sel(j, key);
-      }
-      const uint64_t m = __ballot(me);
-      if (me) emit(j, running + cnt_lds[i * NW + wave] + __popcll(m & below));
-    }
-    __syncthreads();
-    return running + total;
-  }
-};
-
-template <int NT, int KPT, class S>
-__device__ __forceinline__ Pick select_top(const S& s, const Range<NT, KPT, S>& rg, int k,
-                                          Shared<NT>& sh) {
-  Pick pk;
-  pk.theta = 0u;
-  pk.jstar = -1;
-  int n_valid = s.n;
-  if constexpr (S::may_be_invalid()) {
-    int c = 0;
-    rg.visit(s, [&](int, uint32_t key, bool in) { c += in && key != 0u; });
-    block_excl_scan<NT>(c, &n_valid, sh.scan);
-  }
-  pk.take = min(k, n_valid);
-  if (pk.take == 0 || pk.take == n_valid) return pk;  // none, or every valid element
-
-  // key range of the valid elements
-  uint32_t kmax = 0u, kmin_inv = 0u;  // max of key and of ~key over valid keys
-  rg.visit(s, [&](int, uint32_t key, bool in) {
-    if (in && key != 0u) {
-      kmax = max(kmax, key);
-      kmin_inv = max(kmin_inv, ~key);
-    }
-  });
-  kmax = block_reduce_max<NT>(kmax, sh.scan);
-  const uint32_t kmin = ~block_reduce_max<NT>(kmin_inv, sh.scan);
-  // Linear bins in score VALUE over [min, max]: x -> (x - min) * scale is
-  // monotone non-decreasing in floating point, so bins respect the order and
-  // equal scores share a bin.  (Bins linear in key space would put a range
-  // starting at 0 into a handful of bins.)  A non-finite span maps every
-  // element to bin 0 and the exact refinement below takes over.
-  const float xmin = key_value(kmin), xmax = key_value(kmax);
-  float span = xmax - xmin;
-  const float scale = (span > 0.0f && span < 3.0e38f) ? (float)kBins / span : 0.0f;
-  auto bin_of = [&](uint32_t key) {
-    const float t = (key_value(key) - xmin) * scale;
-    return min(kBins - 1, (int)t);
-  };
-
-  for (int i = threadIdx.x; i < kBins; i += NT) sh.hist[i] = 0u;
-  __syncthreads();
-  rg.visit(s, [&](int, uint32_t key, bool in) {
-    const bool v = in && key != 0u;
-    hist_add(sh.hist, v, v ? bin_of(key) : 0);
-  });
-  __syncthreads();
-
-  // Locate the bin holding the take-th key, scanning bins from the top.
-  constexpr int BPT = kBins / NT;
-  {
-    const int hi = kBins - (int)threadIdx.x * BPT;  // bins [hi - BPT, hi)
-    int mine = 0;
-#pragma unroll
-    for (int b = 0; b < BPT; ++b) mine += (int)sh.hist[hi - 1 - b];
-    int tot;
-    const int above = block_excl_scan<NT>(mine, &tot, sh.scan);
-    if (above < pk.take && pk.take <= above + mine) {
-      int acc = above;
-      for (int b = 0; b < BPT; ++b) {
-        const int c = (int)sh.hist[hi - 1 - b];
-        if (acc + c >= pk.take) {
-          sh.u[0] = (uint32_t)(hi - 1 - b);
-          sh.u[1] = (uint32_t)acc;
-          break;
-        }
-        acc += c;
-      }
-    }
-    __syncthreads();
-  }
-  const int bstar = (int)sh.u[0];
-  const int need = pk.take - (int)sh.u[1];  // rank (1-based) inside bin bstar
-  const int m = (int)sh.hist[bstar];
-
-  // Recompute bins from laundered copies of the map below, so the compiler
-  // does not keep every element's bin live across passes.
-  float scale_b = scale, xmin_b = xmin;
-  asm volatile("" : "+v"(scale_b), "+v"(xmin_b));
-  auto bin_again = [&](uint32_t key) {
-    const float t = (key_value(key) - xmin_b) * scale_b;
-    return min(kBins - 1, (int)t);
-  };
-  if (m <= kRankMax) {
-    // gather the bin's elements into LDS and rank them exactly
-    if (threadIdx.x == 0) sh.u[2] = 0u;
-    __syncthreads();
-    rg.visit(s, [&](int j, uint32_t key, bool in) {
-      if (in && key != 0u && bin_again(key) == bstar) {
-        const uint32_t slot = atomicAdd(&sh.u[2], 1u);
-        sh.ckey[slot] = key;
-        sh.cidx[slot] = j;
-      }
-    });
-    __syncthreads();
-    for (int i = threadIdx.x; i < m; i += NT) {
-      const uint32_t ki = sh.ckey[i];
-      const int ji = sh.cidx[i];
-      int rank = 0;
-      for (int l = 0; l < m; ++l) {
-        const uint32_t kl = sh.ckey[l];
-        rank += kl > ki || (kl == ki && sh.cidx[l] < ji);
-      }
-      if (rank == need - 1) {
-        sh.u[3] = ki;
-        sh.u[4] = (uint32_t)ji;
-      }
-    }
-    __syncthreads();
-    pk.theta = sh.u[3];
-    pk.jstar = (int)sh.u[4];
-    __syncthreads();
-    return pk;
-  }
-
-  // Crowded bin: exact 8-bit radix refinement restricted to it.
-  uint32_t prefix = 0u, pmask = 0u;
-  int remaining = need;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += NT) sh.hist[i] = 0u;
-    __syncthreads();
-    rg.visit(s, [&](int, uint32_t key, bool in) {
-      const bool v = in && key != 0u && bin_again(key) == bstar && (key & pmask) == prefix;
-      hist_add(sh.hist, v, v ? (int)((key >> shift) & 255u) : 0);
-    });
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int above = 0, d = 255;
-      for (; d > 0; --d) {
-        const int c = (int)sh.hist[d];
-        if (above + c >= remaining) break;
-        above += c;
-      }
-      sh.u[0] = (uint32_t)d;
-      sh.u[1] = (uint32_t)above;
-    }
-    __syncthreads();
-    remaining -= (int)sh.u[1];
-    prefix |= sh.u[0] << shift;
-    pmask |= 255u << shift;
-    __syncthreads();
-  }
-  pk.theta = prefix;
-  // the remaining-th element equal to theta, in index order
-  rg.ordered(
-      s, [&](int, uint32_t key) { return key == prefix; },
-      [&](int j, int rank) {
-        if (rank == remaining - 1) sh.u[4] = (uint32_t)j;
-      },
-      sh.cnt, sh.scan);
-  __syncthreads();
-  pk.jstar = (int)sh.u[4];
-  __syncthreads();
-  return pk;
-}
-
+// -------------------------------------------------------------- 1. hist
 // beta[r][j] = max of the visible scores of block j (one thread per block).
-__global__ __launch_bounds__(256) void block_max_kernel(SelectArgs a) {
+__global__ __launch_bounds__(256) void block_max_kernel(SelectArgs a, Ws ws) {
   const int r = blockIdx.y;
   const int j = blockIdx.x * 256 + threadIdx.x;
   const RowInfo ri = row_info(a.rows, r);
@@ -419,128 +193,494 @@ __global__ __launch_bounds__(256) void block_max_kernel(SelectArgs a) {
   const int lo = j * a.block, hi = min(lo + a.block, ri.n_avail);
   float m = sc[lo];
   for (int s = lo + 1; s < hi; ++s) m = fmaxf(m, sc[s]);
-  a.beta[(int64_t)r * a.beta_stride + j] = m;
+  ws.beta[(int64_t)r * a.beta_stride + j] = m;
 }
 
-// Block-max pool of one row per workgroup, ranking the block maxima.
-template <int NT, int KPT>
-__global__ __launch_bounds__(NT) void pool_select_kernel(SelectArgs a) {
-  __shared__ Shared<NT> sh;
-  using S = Src<SRC_BLOCK>;
-  const int r = blockIdx.x;
+// Level-1 histogram (key bits 31..20) of one chunk, merged into the row's.
+template <int KIND>
+__global__ __launch_bounds__(kChunkT) void hist_kernel(SelectArgs a, Ws ws) {
+  __shared__ uint32_t h[kL1];
+  __shared__ uint32_t nvalid;
+  const int r = blockIdx.y;
   const RowInfo ri = row_info(a.rows, r);
-  S s;
-  s.sc = a.beta + (int64_t)r * a.beta_stride;
-  s.list = nullptr;
-  s.n = (ri.n_avail + a.block - 1) / a.block;
-  s.win_lo = ri.win_lo;
-  s.n_avail = ri.n_avail;
-  s.block = a.block;
-  Range<NT, KPT, S> rg;
-  rg.init(s);
-  const Pick pk = select_top<NT, KPT>(s, rg, a.max_blocks, sh);
-  // kept blocks, ascending, into LDS (max_blocks <= kCap), then expanded
-  const int nsel = rg.ordered(
-      s,
-      [&](int j, uint32_t key) {
-        return pk.take > 0 && (key > pk.theta || (key == pk.theta && j <= pk.jstar));
-      },
-      [&](int j, int rank) { sh.cidx[rank] = j; }, sh.cnt, sh.scan);
+  const Src<KIND> s = make_src<KIND>(a, ws, r, ri);
+  const int j0 = blockIdx.x * kChunk;
+  if (j0 >= s.n) return;
+  for (int i = threadIdx.x; i < kL1; i += kChunkT) h[i] = 0u;
+  if (threadIdx.x == 0) nvalid = 0u;
   __syncthreads();
-  int32_t* out = a.pool + (int64_t)r * a.pool_stride;
-  const int bs = a.block;
-  // only the last block of the domain can be partial, and it is kept last
-  const int last_blk = s.n - 1;
-  const int deficit =
-      (nsel > 0 && sh.cidx[nsel - 1] == last_blk) ? (last_blk + 1) * bs - ri.n_avail : 0;
-  const int pool_n = nsel * bs - deficit;
-  for (int i = threadIdx.x; i < a.max_blocks * bs; i += NT)
-    out[i] = i < pool_n ? sh.cidx[i / bs] * bs + i % bs : -1;
-  if (threadIdx.x == 0) a.pool_count[r] = pool_n;
+  int valid = 0;
+  uint32_t keys[kChunk / kChunkT];
+#pragma unroll
+  for (int i = 0; i < kChunk / kChunkT; ++i) keys[i] = s.key_c(j0 + i * kChunkT + (int)threadIdx.x);
+#pragma unroll
+  for (int i = 0; i < kChunk / kChunkT; ++i) {
+    const uint32_t key = keys[i];
+    if (key) {
+      atomicAdd(&h[key >> (32 - kL1Bits)], 1u);
+      ++valid;
+    }
+  }
+  if (Src<KIND>::may_be_invalid()) {
+    valid = wave_sum_i32(valid);
+    if ((threadIdx.x & 63) == 0) atomicAdd(&nvalid, (uint32_t)valid);
+  }
+  __syncthreads();
+  uint32_t* gh = ws.hist + (int64_t)r * kHistStride;
+  for (int i = threadIdx.x; i < kL1; i += kChunkT)
+    if (h[i]) atomicAdd(&gh[i], h[i]);
+  if (Src<KIND>::may_be_invalid() && threadIdx.x == 0) atomicAdd(&gh[kL1], nvalid);
 }
 
-// Token top-k of one row per workgroup.  KIND = SRC_TOKEN_FULL (visible
-// entries outside the window), SRC_TOKEN_CAND (a candidate list) or SRC_POOL
-// (the block-max pool of the same scores: with no window and a pool of at
-// least k blocks the token top-k lies inside the pool -- a block ranked above
-// the block of a kept token has a maximum that itself ranks above that token,
-// so at most k-1 blocks rank above it -- and ranking only the pool gives the
-// same set).
-template <int KIND, int NT, int KPT>
-__global__ __launch_bounds__(NT) void token_select_kernel(SelectArgs a) {
-  __shared__ Shared<NT> sh;
-  using S = Src<KIND>;
+// --------------------------------------------------------- 2. threshold
+struct ThrShared {
+  uint32_t hist[kL2];
+  uint32_t ckey[kCap1];
+  int32_t cidx[kCap1];
+  int32_t ccnt[kMaxChunks];  // per-chunk counts
+  uint32_t wred[kTW];
+  uint32_t u[8];
+};
+
+// Locate, scanning bins from the top, the bin holding the rank-th (1-based)
+// element of a kL2-bin histogram in LDS; writes it and the count above it to
+// sh.u[0], sh.u[1].
+__device__ __forceinline__ void locate(const uint32_t* hist, int rank, ThrShared& sh) {
+  constexpr int BPT = kL2 / kTT;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int hi = kL2 - BPT * tid;
+  int c[BPT];
+  int mine = 0;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    c[q] = (int)hist[hi - 1 - q];
+    mine += c[q];
+  }
+  const int incl = wave_incl_scan(mine);
+  if (lane == 63) sh.wred[tid >> 6] = (uint32_t)incl;
+  __syncthreads();
+  int above = incl - mine;
+  for (int w = 0; w < (tid >> 6); ++w) above += (int)sh.wred[w];
+  if (above < rank && rank <= above + mine) {
+    int acc = above;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      if (acc + c[q] >= rank) {
+        sh.u[0] = (uint32_t)(hi - 1 - q);
+        sh.u[1] = (uint32_t)acc;
+        break;
+      }
+      acc += c[q];
+    }
+  }
+  __syncthreads();
+}
+
+// Per row: (theta, jstar, take) and the output offset of every chunk.
+// Element j of the row is visited by thread j % kTT (coalesced loads); its
+// chunk is j / kChunk.  Rows longer than kMaxCnt elements keep chunk counts
+// in LDS with atomics instead of registers.
+template <int KIND, int KPT>
+__global__ __launch_bounds__(kTT) void threshold_kernel(SelectArgs a, Ws ws, int kk) {
+  __shared__ ThrShared sh;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint64_t below = lanes_below();
   const int r = blockIdx.x;
   const RowInfo ri = row_info(a.rows, r);
-  S s;
-  s.sc = a.scores + (int64_t)r * a.score_stride;
-  s.win_lo = ri.win_lo;
-  s.n_avail = ri.n_avail;
-  s.block = 0;
-  if constexpr (KIND == SRC_POOL) {
-    s.list = a.pool + (int64_t)r * a.pool_stride;
-    s.n = a.pool_count[r];
-  } else if constexpr (KIND == SRC_TOKEN_CAND) {
-    s.list = a.cand + (int64_t)r * a.cand_stride;
-    s.n = a.cand_count[r];
-  } else {
-    s.list = nullptr;
-    s.n = ri.win_lo;
+  const Src<KIND> s = make_src<KIND>(a, ws, r, ri);
+  uint32_t* gh = ws.hist + (int64_t)r * kHistStride;
+  uint32_t* thr = ws.thr + (int64_t)r * kThrWords;
+  int32_t* offs = ws.offs + (int64_t)r * ws.chunk_stride;
+  const int n = s.n;
+  const int nch = (n + kChunk - 1) / kChunk;
+
+  for (int i = tid; i < kL1; i += kTT) sh.hist[i] = gh[i];
+  const int n_valid = Src<KIND>::may_be_invalid() ? (int)gh[kL1] : n;
+  __syncthreads();
+  for (int i = tid; i < kHistStride; i += kTT) gh[i] = 0u;  // leave it zero for the next call
+  const int take = min(kk, n_valid);
+
+  // How elements are kept: everything valid (mode 1), nothing (mode 0), or
+  // by threshold (mode 2).
+  int mode = take == 0 ? 0 : (take == n_valid ? 1 : 2);
+  uint32_t b1 = 0;
+  int need = 0;
+  if (mode == 2) {
+    locate(sh.hist, take, sh);
+    b1 = sh.u[0];
+    need = take - (int)sh.u[1];
   }
-  Range<NT, KPT, S> rg;
-  rg.init(s);
-  const Pick pk = select_top<NT, KPT>(s, rg, a.k, sh);
-  int32_t* out = a.idx + (int64_t)r * a.idx_stride;
-  rg.ordered(
-      s,
-      [&](int j, uint32_t key) {
-        return pk.take > 0 && key != 0u && (key > pk.theta || (key == pk.theta && j <= pk.jstar));
-      },
-      [&](int j, int rank) { out[rank] = s.position(j); }, sh.cnt, sh.scan);
-  for (int i = pk.take + threadIdx.x; i < a.k; i += NT) out[i] = -1;
-  if (threadIdx.x == 0) a.count[r] = pk.take;
+  const int m1 = mode == 2 ? (int)sh.hist[b1] : 0;
+  __syncthreads();
+
+  // One pass: per-chunk counts of certainly-kept (or valid) elements, and the
+  // level-1 bin's keys into LDS with a level-2 histogram.
+  for (int i = tid; i < nch; i += kTT) sh.ccnt[i] = 0;
+  for (int i = tid; i < kL2; i += kTT) sh.hist[i] = 0u;
+  if (tid == 0) sh.u[2] = 0u;
+  __syncthreads();
+  const bool gather = mode == 2 && m1 <= kCap1;
+  // Element j = it*kTT*KPT + i*kTT + tid: all KPT loads of a super-chunk are
+  // issued before any processing; chunk of slot i is it*KPT/2 + i/2.
+  constexpr int CPS = KPT / (kChunk / kTT);  // chunks per super-chunk
+  for (int it = 0; it * kTT * KPT < n; ++it) {
+    uint32_t kc[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) kc[i] = s.key_c(it * kTT * KPT + i * kTT + tid);
+    int cnt[CPS];
+#pragma unroll
+    for (int q = 0; q < CPS; ++q) cnt[q] = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const uint32_t key = kc[i];
+      const uint32_t d1 = key >> 20;
+      cnt[i / (kChunk / kTT)] += mode == 1 ? key != 0u : (mode == 2 && key != 0u && d1 > b1);
+    }
+#pragma unroll
+    for (int q = 0; q < CPS; ++q) {
+      const int c = it * CPS + q;
+      const int v = wave_sum_i32(cnt[q]);
+      if (lane == 0 && v && c < nch) atomicAdd(&sh.ccnt[c], v);
+    }
+    if (gather) {
+      // hit bits of this thread's slots, then one wave prefix for the LDS
+      // offsets; the (rare) hits are re-read from the cache to be stored
+      uint64_t hits = 0;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const uint32_t key = kc[i];
+        hits |= (uint64_t)(key != 0u && (key >> 20) == b1) << i;
+      }
+      const int nh = __popcll(hits);
+      const int incl = wave_incl_scan(nh);
+      const int wtot = __builtin_amdgcn_readlane(incl, 63);
+      uint32_t wbase = 0;
+      if (lane == 0 && wtot) wbase = atomicAdd(&sh.u[2], (uint32_t)wtot);
+      wbase = __builtin_amdgcn_readlane(wbase, 0);
+      uint32_t slot = wbase + (uint32_t)(incl - nh);
+      while (hits) {
+        const int i = __ffsll((unsigned long long)hits) - 1;
+        hits &= hits - 1;
+        const int j = it * kTT * KPT + i * kTT + tid;
+        const uint32_t key = s.key_c(j);
+        sh.ckey[slot] = key;
+        sh.cidx[slot] = j;
+        atomicAdd(&sh.hist[(key >> 8) & (kL2 - 1)], 1u);
+        ++slot;
+      }
+    }
+  }
+  __syncthreads();
+
+  uint32_t theta = 0u;
+  int jstar = -1;
+  if (mode == 2 && gather) {
+    locate(sh.hist, need, sh);
+    const uint32_t b2 = sh.u[0];
+    const int need2 = need - (int)sh.u[1];
+    const int m2 = (int)sh.hist[b2];
+    const uint32_t pre = (b1 << 20) | (b2 << 8);
+    __syncthreads();
+    if (m2 <= kRankMax) {
+      // compact the level-2 bin, rank it exactly by (key desc, index asc)
+      uint32_t* k2 = sh.hist;
+      int32_t* j2 = reinterpret_cast<int32_t*>(sh.hist + kRankMax);
+      if (tid == 0) sh.u[2] = 0u;
+      __syncthreads();
+      for (int b0 = 0; b0 < m1; b0 += kTT) {
+        const int i = b0 + tid;
+        const bool hit = i < m1 && (sh.ckey[i] & 0xFFFFFF00u) == pre;
+        const uint64_t mk = __ballot(hit);
+        if (mk) {
+          const int lead = __ffsll((unsigned long long)mk) - 1;
+          uint32_t sl = 0;
+          if (lane == lead) sl = atomicAdd(&sh.u[2], (uint32_t)__popcll(mk));
+          sl = __builtin_amdgcn_readlane(sl, lead);
+          if (hit) {
+            const uint32_t slot = sl + (uint32_t)__popcll(mk & below);
+            k2[slot] = sh.ckey[i];
+            j2[slot] = sh.cidx[i];
+          }
+        }
+      }
+      __syncthreads();
+      if (tid < m2) {
+        const uint32_t ki = k2[tid];
+        const int ji = j2[tid];
+        int rank = 0;
+        for (int l = 0; l < m2; ++l) {
+          const uint32_t kl = k2[l];
+          rank += kl > ki || (kl == ki && j2[l] < ji);
+        }
+        if (rank == need2 - 1) {
+          sh.u[3] = ki;
+          sh.u[4] = (uint32_t)ji;
+        }
+      }
+      __syncthreads();
+      theta = sh.u[3];
+      jstar = (int)sh.u[4];
+      __syncthreads();
+    } else {
+      // crowded level-2 bin: the last 8 bits by histogram over the LDS keys,
+      // then the need3-th tie by index (ties are few relative to the row)
+      for (int i = tid; i < 256; i += kTT) sh.hist[i] = 0u;
+      __syncthreads();
+      for (int i = tid; i < m1; i += kTT)
+        if ((sh.ckey[i] & 0xFFFFFF00u) == pre) atomicAdd(&sh.hist[sh.ckey[i] & 255u], 1u);
+      __syncthreads();
+      if (tid == 0) {
+        int above = 0, d = 255;
+        for (; d > 0; --d) {
+          const int c = (int)sh.hist[d];
+          if (above + c >= need2) break;
+          above += c;
+        }
+        sh.u[0] = (uint32_t)d;
+        sh.u[1] = (uint32_t)above;
+      }
+      __syncthreads();
+      theta = pre | sh.u[0];
+      const int need3 = need2 - (int)sh.u[1];
+      // the need3-th smallest index among keys == theta: count, per tie, the
+      // ties with a smaller index
+      for (int i = tid; i < m1; i += kTT) {
+        if (sh.ckey[i] != theta) continue;
+        const int ji = sh.cidx[i];
+        int rank = 0;
+        for (int l = 0; l < m1; ++l) rank += sh.ckey[l] == theta && sh.cidx[l] < ji;
+        if (rank == need3 - 1) sh.u[4] = (uint32_t)ji;
+      }
+      __syncthreads();
+      jstar = (int)sh.u[4];
+      __syncthreads();
+    }
+    // chunk counts of the kept keys inside the level-1 bin
+    for (int i = tid; i < m1; i += kTT) {
+      const int j = sh.cidx[i];
+      if (kept(theta, jstar, sh.ckey[i], j)) atomicAdd(&sh.ccnt[j / kChunk], 1);
+    }
+    __syncthreads();
+  } else if (mode == 2) {
+    // level-1 bin too crowded for LDS: resolve the remaining 20 key bits by
+    // radix passes over the row, then the tie by index, counting kept
+    // elements per chunk in the final pass
+    uint32_t prefix = b1 << 20, pmask = 0xFFF00000u;
+    int remaining = need;
+    const int shifts[3] = {12, 4, 0};
+    const int widths[3] = {8, 8, 4};
+    for (int p = 0; p < 3; ++p) {
+      const int shift = shifts[p];
+      const uint32_t dmask = (1u << widths[p]) - 1u;
+      for (int i = tid; i <= (int)dmask; i += kTT) sh.hist[i] = 0u;
+      __syncthreads();
+      for (int j = tid; j < n; j += kTT) {
+        const uint32_t key = s.key(j);
+        if (key != 0u && (key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int above = 0, d = (int)dmask;
+        for (; d > 0; --d) {
+          const int c = (int)sh.hist[d];
+          if (above + c >= remaining) break;
+          above += c;
+        }
+        sh.u[0] = (uint32_t)d;
+        sh.u[1] = (uint32_t)above;
+      }
+      __syncthreads();
+      remaining -= (int)sh.u[1];
+      prefix |= sh.u[0] << shift;
+      pmask |= dmask << shift;
+      __syncthreads();
+    }
+    theta = prefix;
+    // ties of theta in index order: per-chunk tie counts, then the chunk
+    // holding the remaining-th tie is scanned in order by one wave
+    for (int i = tid; i < nch; i += kTT) sh.hist[i] = 0u;
+    __syncthreads();
+    for (int j = tid; j < n; j += kTT)
+      if (s.key(j) == theta) atomicAdd(&sh.hist[j / kChunk], 1u);
+    __syncthreads();
+    if (tid < 64) {
+      int acc = 0, c = 0;
+      for (; c < nch; ++c) {
+        const int t = (int)sh.hist[c];
+        if (acc + t >= remaining) break;
+        acc += t;
+      }
+      // wave 0 walks chunk c in index order
+      int found = -1;
+      for (int j0 = c * kChunk; j0 < min(n, (c + 1) * kChunk) && found < 0; j0 += 64) {
+        const int j = j0 + lane;
+        const bool tie = j < n && s.key(j) == theta;
+        const uint64_t m = __ballot(tie);
+        const int cnt = __popcll(m);
+        if (acc + cnt >= remaining) {
+          const int want = remaining - acc;  // 1-based within this group
+          if (tie && (int)__popcll(m & below) == want - 1) sh.u[4] = (uint32_t)j;
+          found = 1;
+        }
+        acc += cnt;
+      }
+    }
+    __syncthreads();
+    jstar = (int)sh.u[4];
+    __syncthreads();
+    for (int j = tid; j < n; j += kTT) {
+      const uint32_t key = s.key(j);
+      if ((key >> 20) == b1 && kept(theta, jstar, key, j)) atomicAdd(&sh.ccnt[j / kChunk], 1);
+    }
+    __syncthreads();
+  }
+
+  // exclusive prefix of the chunk counts -> output offsets
+  if (tid < 64) {
+    int run = 0;
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+      const int c = c0 + lane;
+      const int v = c < nch ? sh.ccnt[c] : 0;
+      const int incl = wave_incl_scan(v);
+      if (c < nch) offs[c] = run + incl - v;
+      run += __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+  if (tid == 0) {
+    thr[0] = mode == 1 ? 0u : (mode == 0 ? 0xFFFFFFFFu : theta);
+    thr[1] = (uint32_t)(mode == 1 ? -1 : jstar);
+    thr[2] = (uint32_t)take;
+  }
 }
 
-template <int NT, int KPT>
-void launch_all(const SelectArgs& a, hipStream_t s) {
-  dim3 grid(a.rows.n_rows);
-  if (a.pool) {
-    dim3 g2((unsigned)((a.beta_stride + 255) / 256), a.rows.n_rows);
-    hipLaunchKernelGGL(block_max_kernel, g2, dim3(256), 0, s, a);
-    hipLaunchKernelGGL((pool_select_kernel<NT, KPT>), grid, dim3(NT), 0, s, a);
+// ------------------------------------------------------------- 3. emit
+// Each chunk writes its kept elements ascending at its offset.  Wave w owns
+// the contiguous quarter [w*512, (w+1)*512) of the chunk; lane l holds
+// elements q*64 + l, so in-wave order is (q, lane).
+template <int KIND>
+__global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int pool_mode) {
+  __shared__ int wtot[kChunkT / 64];
+  const int r = blockIdx.y, c = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t below = lanes_below();
+  const RowInfo ri = row_info(a.rows, r);
+  const Src<KIND> s = make_src<KIND>(a, ws, r, ri);
+  const uint32_t* thr = ws.thr + (int64_t)r * kThrWords;
+  const uint32_t theta = thr[0];
+  const int jstar = (int)thr[1];
+  const int take = (int)thr[2];
+  const int bs = a.block;
+  int32_t* out = pool_mode ? a.pool + (int64_t)r * a.pool_stride : a.idx + (int64_t)r * a.idx_stride;
+  if (c == 0) {
+    // padding and count (only the last kept block can be partial)
+    if (pool_mode) {
+      const int nb = s.n;
+      int pool_n = take * bs;
+      if (take > 0) {
+        const uint32_t klast = s.key(nb - 1);
+        if (kept(theta, jstar, klast, nb - 1)) pool_n -= nb * bs - ri.n_avail;
+      }
+      for (int i = pool_n + threadIdx.x; i < a.max_blocks * bs; i += kChunkT) out[i] = -1;
+      if (threadIdx.x == 0) a.pool_count[r] = pool_n;
+    } else {
+      for (int i = take + threadIdx.x; i < a.k; i += kChunkT) out[i] = -1;
+      if (threadIdx.x == 0) a.count[r] = take;
+    }
   }
-  if (a.k <= 0) return;
-  if (a.pool && a.rows.window == 0 && a.max_blocks >= a.k)
-    hipLaunchKernelGGL((token_select_kernel<SRC_POOL, NT, KPT>), grid, dim3(NT), 0, s, a);
-  else if (a.cand)
-    hipLaunchKernelGGL((token_select_kernel<SRC_TOKEN_CAND, NT, KPT>), grid, dim3(NT), 0, s, a);
+  const int j0 = c * kChunk;
+  if (take == 0 || j0 >= s.n) return;
+  constexpr int Q = kChunk / kChunkT;
+  uint32_t keys[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int j = j0 + wave * (kChunk / 4) + q * 64 + lane;
+    keys[q] = s.key_c(j);
+  }
+  uint32_t flags = 0u;
+  int tot = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int j = j0 + wave * (kChunk / 4) + q * 64 + lane;
+    const bool me = kept(theta, jstar, keys[q], j);
+    flags |= (uint32_t)me << q;
+    tot += __popcll(__ballot(me));
+  }
+  if (lane == 0) wtot[wave] = tot;
+  __syncthreads();
+  int base = ws.offs[(int64_t)r * ws.chunk_stride + c];
+  for (int w = 0; w < wave; ++w) base += wtot[w];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const bool me = (flags >> q) & 1u;
+    const uint64_t m = __ballot(me);
+    if (me) {
+      const int j = j0 + wave * (kChunk / 4) + q * 64 + lane;
+      const int rank = base + (int)__popcll(m & below);
+      if (pool_mode) {
+        const int lo = j * bs, mm = min(bs, ri.n_avail - lo);
+        for (int u = 0; u < mm; ++u) out[rank * bs + u] = lo + u;
+      } else {
+        out[rank] = s.position(j);
+      }
+    }
+    base += (int)__popcll(m);
+  }
+}
+
+template <int KIND>
+void run_select(const SelectArgs& a, const Ws& ws, int64_t max_n, int kk, int pool_mode,
+                hipStream_t st) {
+  const int R = a.rows.n_rows;
+  dim3 gc((unsigned)((max_n + kChunk - 1) / kChunk), R);
+  hipLaunchKernelGGL(hist_kernel<KIND>, gc, dim3(kChunkT), 0, st, a, ws);
+  if (max_n <= kTT * 32)
+    hipLaunchKernelGGL((threshold_kernel<KIND, 32>), dim3(R), dim3(kTT), 0, st, a, ws, kk);
   else
-    hipLaunchKernelGGL((token_select_kernel<SRC_TOKEN_FULL, NT, KPT>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((threshold_kernel<KIND, 64>), dim3(R), dim3(kTT), 0, st, a, ws, kk);
+  hipLaunchKernelGGL(emit_kernel<KIND>, gc, dim3(kChunkT), 0, st, a, ws, pool_mode);
+}
+
+int64_t chunk_stride(const SelectArgs& a) {
+  int64_t n = a.max_elems;
+  if (a.pool) n = max(n, a.beta_stride);
+  return ((n + kChunk - 1) / kChunk + 15) / 16 * 16;
 }
 
 }  // namespace
 
 size_t topk_workspace_bytes(const SelectArgs& a) {
-  if (!a.pool) return 0;
-  const int64_t nb = (a.score_stride + a.block - 1) / a.block;
-  const int64_t stride = (nb + 63) / 64 * 64;
-  return (size_t)a.rows.n_rows * stride * sizeof(float);
+  const int64_t R = a.rows.n_rows;
+  size_t b = (size_t)R * (kHistStride + kThrWords) * sizeof(uint32_t);
+  b += (size_t)R * chunk_stride(a) * sizeof(int32_t);
+  if (a.pool) b += (size_t)R * a.beta_stride * sizeof(float);
+  return b;
 }
 
-hipError_t launch_topk_select(const SelectArgs& a, hipStream_t s) {
+// Workspace: level-1 histograms [R][kHistStride] (zero on entry, left zero),
+// per-row thresholds, per-chunk offsets, then (pool mode) block maxima.
+hipError_t launch_topk_select(const SelectArgs& a, hipStream_t st) {
   if (a.rows.n_rows == 0) return hipSuccess;
-  int64_t n = a.max_elems;
+  const int64_t R = a.rows.n_rows;
+  Ws ws;
+  ws.hist = reinterpret_cast<uint32_t*>(a.beta);
+  ws.thr = ws.hist + R * kHistStride;
+  ws.chunk_stride = chunk_stride(a);
+  ws.offs = reinterpret_cast<int32_t*>(ws.thr + R * kThrWords);
+  ws.beta = reinterpret_cast<float*>(ws.offs + R * ws.chunk_stride);
+  if ((a.pool ? a.beta_stride : a.max_elems) > (int64_t)kChunk * kMaxChunks) return hipErrorInvalidValue;
   if (a.pool) {
-    const int64_t nb = a.beta_stride;
-    const int64_t pool_tokens = (int64_t)a.max_blocks * a.block;
-    n = nb;
-    if (a.k > 0 && a.rows.window == 0 && a.max_blocks >= a.k) n = nb > pool_tokens ? nb : pool_tokens;
-    else if (a.k > 0) n = n > a.max_elems ? n : a.max_elems;
+    dim3 g2((unsigned)((a.beta_stride + 255) / 256), a.rows.n_rows);
+    hipLaunchKernelGGL(block_max_kernel, g2, dim3(256), 0, st, a, ws);
+    run_select<SRC_BLOCK>(a, ws, a.beta_stride, a.max_blocks, 1, st);
   }
-  if (n <= 256 * 16)
-    launch_all<256, 16>(a, s);
-  else
-    launch_all<1024, 32>(a, s);
+  if (a.k > 0) {
+    if (a.pool && a.rows.window == 0 && a.max_blocks >= a.k)
+      run_select<SRC_POOL>(a, ws, (int64_t)a.max_blocks * a.block, a.k, 0, st);
+    else if (a.cand)
+      run_select<SRC_TOKEN_CAND>(a, ws, a.cand_stride, a.k, 0, st);
+    else
+      run_select<SRC_TOKEN_FULL>(a, ws, a.max_elems, a.k, 0, st);
+  }
   return hipGetLastError();
 }
 
