@@ -29,6 +29,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "index_reuse_amd", "csrc")
+# sources whose kernels each entry point launches (a traffic record is valid
+# only while their text is unchanged)
+CALL_SOURCES = {
+    "index_score": ("index_score.hip", "common.hpp", "kernels.hpp"),
+    "topk_select": ("topk_select.hip", "common.hpp", "kernels.hpp"),
+    "attn_gather_fwd": ("attn_gather.hip", "common.hpp", "kernels.hpp"),
+}
 METRIC = "sparse-attn decode queries/s & prefill rows/s at 1 GPU; % HBM/MFMA roofline"
 
 
@@ -90,11 +99,66 @@ def attention_flops(step, call=0) -> float:
     return 2.0 * n_e * sets * wl.hq * (wl.dqk + wl.dv)
 
 
-def cpu_baseline(step, n_rows: int):
-    """The fp64 oracle on the first ``n_rows`` decode rows of the same inputs
-    (whole step: score, select, attention for every query set)."""
-    import numpy as np
+def call_family(name: str) -> str:
+    for fam in CALL_SOURCES:
+        if name == fam or name.startswith(fam + "_"):
+            return fam
+    raise KeyError(name)
+
+
+def source_hash(fam: str) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in CALL_SOURCES[fam]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(fam: str, workload: str):
+    """HBM bytes per call from the committed counter summary
+    profiles/<call>_<workload>_traffic.txt (FETCH_SIZE and WRITE_SIZE per
+    dispatch, each scaled by the same counter's reading for a plain copy of
+    known size), or None when absent or taken on other kernel sources."""
+    path = os.path.join(PROFILES, "%s_%s_traffic.txt" % (fam, workload))
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("source_sha256") != source_hash(fam):
+        return None
+    try:
+        return float(rec["traffic_bytes"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibration_copy(mib: int):
+    """A plain device copy of known size (read mib MiB, write mib MiB), run
+    three times, so a counter run records what FETCH_SIZE / WRITE_SIZE read
+    for it."""
     import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def cpu_baseline(step, n_rows: int, min_seconds: float):
+    """The fp64 oracle on the first ``n_rows`` decode rows of the same inputs
+    (whole step: score, select, attention for every query set), repeated
+    until at least ``min_seconds`` of host time have elapsed."""
+    import numpy as np
 
     import oracle
 
@@ -118,19 +182,24 @@ def cpu_baseline(step, n_rows: int):
     q_idx = p.idx_q[0][rows].cpu()
     w = p.idx_w[0][rows].cpu()
     q = p.q[0][:, rows].cpu()
-    torch.cuda.synchronize()
+    scale = float(np.float32(wl.dqk ** -0.5))
+    reps = 0
     t0 = time.perf_counter()
-    sc = oracle.index_score(so, po, sl, wl.stride, q_idx, w, kl)
-    idx, cnt = oracle.topk_select(so, po, sl, wl.stride, wl.window, sc, wl.k)
-    oracle.attention(so, po, sl, wl.stride, wl.window, q, K, V, idx, cnt,
-                     scale=float(np.float32(wl.dqk ** -0.5)), v_from_k=V is None, dv=wl.dv)
-    dt = time.perf_counter() - t0
-    queries = n_rows * q.shape[0]
-    return {"value": queries / dt, "unit": "queries/s", "cores": oracle.num_threads(),
+    while True:
+        sc = oracle.index_score(so, po, sl, wl.stride, q_idx, w, kl)
+        idx, cnt = oracle.topk_select(so, po, sl, wl.stride, wl.window, sc, wl.k)
+        oracle.attention(so, po, sl, wl.stride, wl.window, q, K, V, idx, cnt,
+                         scale=scale, v_from_k=V is None, dv=wl.dv)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    queries = reps * n_rows * q.shape[0]
+    return {"value": round(queries / dt, 3), "unit": "queries/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "%d of %d decode rows (whole step: score %d entries/row, select, attention "
-                      "for %d query sets), %.1f s" % (n_rows, p.n_rows, int(sl.max()), q.shape[0],
-                                                      dt)}
+            "sample": "%d pass(es) over %d of %d decode rows of one replica (whole step: score "
+                      "%d entries/row, select, attention for %d query sets), %.1f s" % (
+                          reps, n_rows, p.n_rows, int(sl.max()) // wl.stride, q.shape[0], dt)}
 
 
 def main():
@@ -140,9 +209,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="hysparse2")
     ap.add_argument("--replicas", type=int, default=4)
-    ap.add_argument("--cpu-rows", type=int, default=4, help="decode rows for the oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="decode rows for the oracle baseline (default: all rows of a step)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum host time of the oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    ap.add_argument("--breakdown", action="store_true", help="also print per-call times")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run a plain copy of this size first (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -160,6 +233,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     index_reuse_amd.load()
     dev = torch.device("cuda:0")
+    if args.copy_mib > 0:
+        calibration_copy(args.copy_mib)
     wl = synth.WORKLOADS[args.workload]
     if wl.prefill:
         raise SystemExit("prefill workloads are benchmarked by their own script")
@@ -199,6 +274,7 @@ def main():
     step0 = steps[0]
     queries = step0.prob.n_rows * sum(q.shape[0] for q in step0.prob.q)
     dom = max(per_call, key=per_call.get)
+    traffic = recorded_traffic(call_family(dom), wl.name)
     bytes_dom = algorithmic_bytes(step0, dom)
     achieved = bytes_dom / (per_call[dom] * 1e-3) / 1e9
     kernels = {}
@@ -227,12 +303,14 @@ def main():
                    "page_size": wl.page_size, "replicas": args.replicas},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": None if traffic is None else int(traffic),
+                     "alg_bytes": int(bytes_dom)},
         "gpu_ms_per_step": round(gpu_ms_step, 5),
         "kernels": kernels,
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(step0, min(args.cpu_rows, step0.prob.n_rows))
+        n = args.cpu_rows if args.cpu_rows > 0 else step0.prob.n_rows
+        out["cpu_baseline"] = cpu_baseline(step0, min(n, step0.prob.n_rows), args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
