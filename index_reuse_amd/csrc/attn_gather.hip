@@ -11,19 +11,23 @@
 // entry split, query-row tile group).  All query heads of the KV group and
 // all query sets are stacked into Mq = n_qsets * (Hq / Hkv) MFMA rows, so
 // every gathered K/V row is read from HBM once per call and reused by every
-// head and query set.  Per 32-entry tile:
-//   1. the workgroup gathers the 32 K (and V) rows through the block table
+// head and query set.  Inside the workgroup, NG entry groups of W waves walk
+// disjoint 32-entry tiles of the entry list (several waves per SIMD hide
+// each other's latency) and merge their softmax states in LDS at the end.
+// Per tile:
+//   1. the workgroup gathers the K (and V) rows through the block table
 //      into LDS (FP4 rows are dequantised exactly to bf16 on the way);
 //   2. each wave computes S^T = K . Q^T for its 16 query rows with
 //      v_mfma_f32_16x16x32_bf16 (entries on M, query rows on N), so each lane
 //      ends up holding 8 logits of ONE query row;
-//   3. online softmax in fp32 (exp2 domain), per query row;
+//   3. softmax in fp32 (exp2 domain) against a per-row reference max that
+//      only moves when a tile exceeds it by 2^8 (lazy rescale);
 //   4. O^T += V^T . P^T with the contraction order permuted so that the
 //      lane's 8 probabilities are directly its B operand; the V^T operand is
 //      built from 16-byte LDS reads by an in-register 8x8 bf16 transpose
-//      (v_perm).  O^T keeps each lane on one query row, so the online-softmax
-//      rescale and the final normalisation need no cross-lane traffic;
-//      row statistics are reduced with the gfx950 lane-swap instructions.
+//      (v_perm).  O^T keeps each lane on one query row, so rescales and the
+//      final normalisation need no cross-lane traffic; row statistics are
+//      reduced with the gfx950 lane-swap instructions.
 // Long entry lists are split across workgroups; a combine kernel merges the
 // (max, sum, unnormalised O) partials.  F32 inputs use a plain VALU kernel.
 #include "kernels.hpp"
@@ -63,77 +67,75 @@ __device__ __forceinline__ void fp4_dequant32(u32x4 codes, uint32_t s0, uint32_t
   }
 }
 
-constexpr int kNW = 4;           // waves per workgroup (one per SIMD)
 constexpr int kMaxEntries = 2048;  // entries per workgroup (slot table size)
 
-template <int DQK, int DV, int KV>
+// Work shape of one workgroup: W waves per entry group, each owning one
+// 16-row query tile, and NG entry groups that walk disjoint tiles of the
+// entry list (group g takes tiles g, g + NG, ...).  The groups keep their
+// own softmax state and merge it in LDS at the end, so several waves per
+// SIMD hide each other's LDS and MFMA latency while every gathered row is
+// still read from HBM once per workgroup.
+template <int DQK, int DV, int KV, int W, int NG, int D>
 struct AttnLds {
   static constexpr int KROW = DQK + 8;  // bf16 elements per LDS row (padded)
   static constexpr int VROW = DV + 8;
   static constexpr bool HAS_V = KV == KV_SEPARATE;
-  uint16_t k[2][kTile * KROW];
-  uint16_t v[2][HAS_V ? kTile * VROW : 1];
-  int32_t slot[kMaxEntries + 8 * kTile];  // cache slot of every entry (-1: none)
+  static constexpr int NB = 2 * NG;     // tile buffers: double-buffered per group
+  static constexpr int SLOTS = kMaxEntries + (D + 1) * NG * kTile;
+  static constexpr int CSTRIDE = 36;    // floats per lane in the merge area
+  struct Tiles {
+    uint16_t k[NB][kTile * KROW];
+    uint16_t v[NB][HAS_V ? kTile * VROW : 1];
+  };
+  union {
+    Tiles t;
+    float comb[(NG > 1 ? NG - 1 : 1) * W * 64 * CSTRIDE];
+  } u;
+  float ml[NG][W][16][2];
+  int32_t first;        // first entry of the range with a slot
+  int32_t slot[SLOTS];  // cache slot of every entry (-1: none)
 };
 
-// Per-thread share of one tile of gathered rows, held in registers between
-// the global load and the LDS store (the prefetch ring).
-template <int DQK, int DV, int KV>
+// Per-thread share of one step (NG tiles) of gathered rows, held in
+// registers between the global load and the LDS store (the prefetch ring).
+template <int DQK, int DV, int KV, int NTH, int NG>
 struct TileRegs {
   static constexpr bool FP4 = KV == KV_FP4;
   static constexpr int CPR_K = FP4 ? DQK / 32 : DQK / 8;  // 16-byte chunks per K row
   static constexpr int CPR_V = KV == KV_SEPARATE ? DV / 8 : 0;
   static constexpr int C_K = kTile * CPR_K;
-  static constexpr int C_ALL = C_K + kTile * CPR_V;
-  static constexpr int U = (C_ALL + 64 * kNW - 1) / (64 * kNW);
+  static constexpr int C_ALL = C_K + kTile * CPR_V;      // chunks per tile
+  static constexpr int TOT = NG * C_ALL;                 // chunks per step
+  static constexpr int U = (TOT + NTH - 1) / NTH;
   u32x4 v[U];
   uint32_t sc[FP4 ? U : 1];  // FP4: the two E4M3 scales of each 32-channel chunk
 };
 
-template <int DQK, int DV, int KV, int D>
-__global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_split) {
-  using L = AttnLds<DQK, DV, KV>;
-  using T = TileRegs<DQK, DV, KV>;
+template <int DQK, int DV, int KV, int W, int NG, int D>
+__global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_split) {
+  constexpr int NTH = 64 * W * NG;
+  using L = AttnLds<DQK, DV, KV, W, NG, D>;
+  using T = TileRegs<DQK, DV, KV, NTH, NG>;
+  static_assert(sizeof(L) <= 160 * 1024, "LDS budget");
   __shared__ __align__(16) L lds;
   constexpr int KS = DQK / 32;   // k-steps of the S MFMA
   constexpr int QV = DQK / 32;   // 16-byte q vectors per lane
   constexpr int NJB = DV / 128;  // 128-channel blocks of V
   constexpr int NT = DV / 16;    // N tiles of O
-  constexpr int NTH = 64 * kNW;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int grp = wave / W, wq = wave - grp * W;
   const int col = lane & 15, gq = lane >> 4;
   const int sp = blockIdx.x;
   const int r = blockIdx.y / a.hkv, g = blockIdx.y % a.hkv;
   const int G = a.hq / a.hkv;
   const int Mq = a.n_qsets * G;
-  const int qrow0 = (blockIdx.z * kNW + wave) * 16;
+  const int qrow0 = (blockIdx.z * W + wq) * 16;
   const bool active = qrow0 < Mq;
 
-  const RowInfo ri = row_info(a.rows, r);
-  const int n_w = ri.n_avail - ri.win_lo;
-  const int cnt = (a.idx && ri.b >= 0) ? a.count[r] : 0;
-  const int n_e = ri.b < 0 ? 0 : n_w + cnt;
-  const int e0 = sp * per_split, e1 = min(n_e, e0 + per_split);
-  const int ne = max(0, e1 - e0);
-  const int ntiles = (ne + kTile - 1) / kTile;
-  const int32_t* idx = a.idx ? a.idx + (int64_t)r * a.idx_stride : nullptr;
-
-  // Cache slot of every entry of this range, once: the window entries, then
-  // the selected ones, through the block table.  Padding to whole tiles, and
-  // the D tiles past the end that the prefetch ring reads, are -1.
-  for (int i = tid; i < (ntiles + D) * kTile; i += NTH) {
-    int slot = -1;
-    if (i < ne) {
-      const int e = e0 + i;
-      const int pos = e < n_w ? ri.win_lo + e : idx[e - n_w];
-      if (pos >= 0) slot = (int)cache_slot(a.k, ri.b, pos);
-    }
-    lds.slot[i] = slot;
-  }
-
-  // Query rows of this wave as the B operand (query row = col).
+  // Query rows of this wave as the B operand (query row = col); issued first,
+  // they depend on nothing else.
   u32x4 qv[QV];
   {
     const int qr = qrow0 + col;
@@ -149,21 +151,84 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_spl
       for (int i = 0; i < QV; ++i) qv[i] = u32x4{0, 0, 0, 0};
     }
   }
-  __syncthreads();
 
-  // Issue the global loads of tile t into registers.  Branch-free, so the
-  // compiler can keep D tiles of loads in flight: an entry without a slot
+  // Entries of the row in this order: the selected ones (idx[0 .. count)),
+  // then the window.  Selected entries come first so that their index loads
+  // depend only on the row, not on the sequence length.
+  const int32_t* idx = a.idx ? a.idx + (int64_t)r * a.idx_stride : nullptr;
+  const int e0 = sp * per_split;
+  constexpr int PT = 4;  // table entries per thread per pass
+  int sel_pre[PT];
+#pragma unroll
+  for (int j = 0; j < PT; ++j)
+    sel_pre[j] = idx ? idx[min(e0 + j * NTH + tid, a.idx_stride - 1)] : -1;
+
+  const RowInfo ri = row_info(a.rows, r);
+  const int n_w = ri.n_avail - ri.win_lo;
+  const int cnt = (idx && ri.b >= 0) ? a.count[r] : 0;
+  const int n_e = ri.b < 0 ? 0 : n_w + cnt;
+  const int e1 = min(n_e, e0 + per_split);
+  const int ne = max(0, e1 - e0);
+  const int ntiles = (ne + kTile - 1) / kTile;
+  const int nsteps = (ntiles + NG - 1) / NG;
+
+  // Cache slot of every entry of this range, once, through the block table.
+  // Padding to whole steps, and the D steps past the end that the prefetch
+  // ring reads, are -1.  Loads are clamped rather than guarded so that a
+  // thread's loads all issue before the first wait.
+  if (tid == 0) lds.first = 0x7FFFFFFF;
+  __syncthreads();
+  {
+    const int n_tab = (nsteps + D) * NG * kTile;
+    for (int i0 = 0; i0 < n_tab; i0 += PT * NTH) {
+      int pos[PT];
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        const int i = i0 + j * NTH + tid;
+        const int e = e0 + i;
+        const int sel = i0 == 0 ? sel_pre[j] : (idx ? idx[min(e, a.idx_stride - 1)] : -1);
+        pos[j] = i < ne ? (e < cnt ? sel : ri.win_lo + (e - cnt)) : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        const int i = i0 + j * NTH + tid;
+        int slot = -1;
+        if (ri.b >= 0) {
+          const int sl = (int)cache_slot(a.k, ri.b, max(pos[j], 0));
+          slot = pos[j] >= 0 ? sl : -1;
+        }
+        if (i < n_tab) lds.slot[i] = slot;
+        // one LDS atomic per wave: the wave's lowest entry with a slot
+        const uint64_t has = __builtin_amdgcn_ballot_w64(slot >= 0);
+        if (has && lane == __builtin_ctzll(has)) atomicMin(&lds.first, i);
+      }
+    }
+  }
+  __syncthreads();
+  // Entries without a slot (tile padding, -1 indices) read the rows of the
+  // range's first real entry instead: finite data that the mask gives weight
+  // exactly 0.  A range with no real entry computes nothing.
+  const int first = lds.first;
+  const int nsteps_run = first < ne ? nsteps : 0;
+  const int64_t dummy = first < ne ? lds.slot[first] : 0;
+
+  // Chunk c of a step: tile c / C_ALL of the step, then K or V row part.
+  // Issue the global loads of step s into registers.  Branch-free, so the
+  // compiler can keep D steps of loads in flight: an entry without a slot
   // reads slot 0 (always backed by the cache) and is zeroed at store time.
-  auto load_tile = [&](int t, T& regs) {
+  auto load_step = [&](int s, T& regs) {
 #pragma unroll
     for (int u = 0; u < T::U; ++u) {
       int c = tid + NTH * u;
-      if (T::C_ALL % NTH != 0) c = min(c, T::C_ALL - 1);
-      const bool is_k = c < T::C_K;
-      const int cc = is_k ? c : c - T::C_K;
+      if (T::TOT % NTH != 0) c = min(c, T::TOT - 1);
+      const int gs = c / T::C_ALL;
+      const int cw = c - gs * T::C_ALL;
+      const bool is_k = cw < T::C_K;
+      const int cc = is_k ? cw : cw - T::C_K;
       const int cpr = is_k ? T::CPR_K : T::CPR_V;
       const int e = cc / cpr, part = cc % cpr;
-      const int64_t slot = max(lds.slot[t * kTile + e], 0);
+      const int sl = lds.slot[(s * NG + gs) * kTile + e];
+      const int64_t slot = sl >= 0 ? (int64_t)sl : dummy;
       if constexpr (T::FP4) {
         regs.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
             a.k.data + slot * a.k.row_stride + g * (DQK / 2) + part * 16));
@@ -176,34 +241,31 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_spl
       }
     }
   };
-  // Store tile t's registers into LDS buffer `buf` (FP4 is dequantised here);
-  // rows of entries without a slot become zeros.
-  auto store_tile = [&](const T& regs, int buf, int t) {
+  // Store step s's registers into LDS buffer set `sb` (FP4 is dequantised
+  // here).
+  auto store_step = [&](const T& regs, int sb) {
 #pragma unroll
     for (int u = 0; u < T::U; ++u) {
       const int c = tid + NTH * u;
-      if (T::C_ALL % NTH != 0 && c >= T::C_ALL) continue;
+      if (T::TOT % NTH != 0 && c >= T::TOT) continue;
+      const int gs = c / T::C_ALL;
+      const int cw = c - gs * T::C_ALL;
+      const int buf = sb * NG + gs;
       if constexpr (T::FP4) {
-        const int e = c / T::CPR_K, part = c % T::CPR_K;
-        const bool ok = lds.slot[t * kTile + e] >= 0;
+        const int e = cw / T::CPR_K, part = cw % T::CPR_K;
         uint32_t vals[16];
         fp4_dequant32(regs.v[u], regs.sc[u] & 0xFFu, regs.sc[u] >> 8, vals);
-        u32x4* dst = reinterpret_cast<u32x4*>(&lds.k[buf][e * L::KROW + part * 32]);
+        u32x4* dst = reinterpret_cast<u32x4*>(&lds.u.t.k[buf][e * L::KROW + part * 32]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          dst[i] = ok ? u32x4{vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]}
-                      : u32x4{0, 0, 0, 0};
-      } else if (c < T::C_K) {
-        const int e = c / T::CPR_K, part = c % T::CPR_K;
-        const bool ok = lds.slot[t * kTile + e] >= 0;
-        *reinterpret_cast<u32x4*>(&lds.k[buf][e * L::KROW + part * 8]) =
-            ok ? regs.v[u] : u32x4{0, 0, 0, 0};
+          dst[i] = u32x4{vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]};
+      } else if (cw < T::C_K) {
+        const int e = cw / T::CPR_K, part = cw % T::CPR_K;
+        *reinterpret_cast<u32x4*>(&lds.u.t.k[buf][e * L::KROW + part * 8]) = regs.v[u];
       } else {
-        const int cc = c - T::C_K;
+        const int cc = cw - T::C_K;
         const int e = cc / T::CPR_V, part = cc % T::CPR_V;
-        const bool ok = lds.slot[t * kTile + e] >= 0;
-        *reinterpret_cast<u32x4*>(&lds.v[buf][e * L::VROW + part * 8]) =
-            ok ? regs.v[u] : u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(&lds.u.t.v[buf][e * L::VROW + part * 8]) = regs.v[u];
       }
     }
   };
@@ -213,8 +275,9 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_spl
   for (int t = 0; t < NT; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_huge_valf(), l_run = 0.0f;
 
+  // One tile (LDS buffer `buf`, entry tile t) for this wave's query rows.
   auto compute = [&](int buf, int t) {
-    const uint16_t* kb = lds.k[buf];
+    const uint16_t* kb = lds.u.t.k[buf];
     // S^T tile: entries (M) x query rows (N)
     f32x4 s[2];
 #pragma unroll
@@ -243,33 +306,31 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_spl
         tmax = fmaxf(tmax, x);
       }
     tmax = xor16_32_max(tmax);
-    const float m_new = fmaxf(m_run, tmax);
-    float alpha = 1.0f;
+    // Lazy rescale: the reference max m_run only moves when some row's tile
+    // max exceeds it by more than 2^8 (in the exp2 domain), so most tiles
+    // leave O untouched; probabilities stay below 2^8 (exact bf16 range).
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + 8.0f)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = m_new == -__builtin_huge_valf() ? 1.0f : exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[tt][i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -__builtin_huge_valf() ? 0.0f : m_run;
     float psum = 0.0f;
     float p[2][4];
-    if (m_new == -__builtin_huge_valf()) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[mt][i] = 0.0f;
-    } else {
-      alpha = exp2f(m_run - m_new);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[mt][i] = exp2f(s[mt][i] - m_new);
-          psum += p[mt][i];
-        }
-    }
+      for (int i = 0; i < 4; ++i) {
+        p[mt][i] = exp2f(s[mt][i] - m_use);
+        psum += p[mt][i];
+      }
     psum = xor16_32_sum(psum);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // O^T holds only this lane's query row (col): the rescale is lane-local
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) O[tt][i] *= alpha;
+    l_run += psum;
 
     // P^T as the B operand: k-slot 8*gq + i <-> entry (i<4 ? 4gq+i : 16+4gq+i-4)
     u32x4 pa;
@@ -278,7 +339,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_spl
     pa[2] = pack_bf16x2(p[1][0], p[1][1]);
     pa[3] = pack_bf16x2(p[1][2], p[1][3]);
     const bf16x8 pab = __builtin_bit_cast(bf16x8, pa);
-    const uint16_t* vbase = KV == KV_SEPARATE ? lds.v[buf] : kb;
+    const uint16_t* vbase = KV == KV_SEPARATE ? lds.u.t.v[buf] : kb;
     constexpr int VR = KV == KV_SEPARATE ? L::VROW : L::KROW;
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
@@ -304,30 +365,74 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_mfma(AttnArgs a, int per_spl
     }
   };
 
-  // Prefetch ring: tile t's rows are loaded D tiles ahead of their use.  Full
-  // groups of D tiles run without guards (D is even, so the LDS buffer of
-  // each unrolled step is static); the last partial group is guarded.
-  static_assert(D % 2 == 0, "prefetch depth must be even");
+  // Prefetch ring: step s's rows are loaded D steps ahead of their use.
+  // Full groups of D steps run without guards (for even D the LDS buffer set
+  // of each unrolled step is static); the last partial group is guarded.
+  static_assert(D == 1 || D % 2 == 0, "prefetch depth must be 1 or even");
   T ring[D];
 #pragma unroll
-  for (int u = 0; u < D; ++u) load_tile(u, ring[u]);
-  int t0 = 0;
-  for (; t0 + D <= ntiles; t0 += D) {
+  for (int u = 0; u < D; ++u) load_step(u, ring[u]);
+  int s0 = 0;
+  for (; s0 + D <= nsteps_run; s0 += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      store_tile(ring[u], u & 1, t0 + u);
+      const int sb = D % 2 == 0 ? (u & 1) : ((s0 + u) & 1);
+      store_step(ring[u], sb);
       __syncthreads();
-      load_tile(t0 + u + D, ring[u]);
-      if (active) compute(u & 1, t0 + u);
+      load_step(s0 + u + D, ring[u]);
+      if (active) compute(sb * NG + grp, (s0 + u) * NG + grp);
     }
   }
 #pragma unroll
   for (int u = 0; u < D; ++u) {
-    if (t0 + u < ntiles) {
-      store_tile(ring[u], u & 1, t0 + u);
+    if (s0 + u < nsteps_run) {
+      const int sb = (s0 + u) & 1;
+      store_step(ring[u], sb);
       __syncthreads();
-      if (active) compute(u & 1, t0 + u);
+      if (active) compute(sb * NG + grp, (s0 + u) * NG + grp);
     }
+  }
+
+  // Merge the entry groups: every wave publishes (m, l, O^T) in LDS (same
+  // lane layout for every group), then group 0 rescales to the common max
+  // and sums.
+  if constexpr (NG > 1) {
+    static_assert(NJB == 1, "the group merge holds one 128-channel block");
+    __syncthreads();  // every tile buffer is free from here on
+    if (gq == 0) {
+      lds.ml[grp][wq][col][0] = m_run;
+      lds.ml[grp][wq][col][1] = l_run;
+    }
+    if (grp > 0) {
+      f32x4* dst = reinterpret_cast<f32x4*>(
+          &lds.u.comb[(((grp - 1) * W + wq) * 64 + lane) * L::CSTRIDE]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j] = O[j];
+    }
+    __syncthreads();
+    if (grp != 0) return;
+    float M = -__builtin_huge_valf();
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, lds.ml[gg][wq][col][0]);
+    float f[NG];
+    float Ls = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      const float m = lds.ml[gg][wq][col][0];
+      f[gg] = m == -__builtin_huge_valf() ? 0.0f : exp2f(m - M);
+      Ls += f[gg] * lds.ml[gg][wq][col][1];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) O[j] *= f[0];
+#pragma unroll
+    for (int gg = 1; gg < NG; ++gg) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(
+          &lds.u.comb[(((gg - 1) * W + wq) * 64 + lane) * L::CSTRIDE]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) O[j] += f[gg] * src[j];
+    }
+    m_run = M;
+    l_run = Ls;
   }
 
   if (!active) return;
@@ -498,19 +603,47 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
                                : -__builtin_huge_valf();
 }
 
-template <int DQK, int DV, int KV, int D>
+// Waves per entry group (one 16-row query tile each) and entry groups per
+// workgroup.  Decode with at most three query tiles per KV head (C2: 6 query
+// sets x 8 heads = 48 rows) runs 3 x 4 = 12 waves; other shapes 4 x NG.
+struct AttnShape {
+  int w, ng;
+};
+
+AttnShape attn_shape(const AttnArgs& a) {
+  const int tiles = (a.n_qsets * (a.hq / a.hkv) + 15) / 16;
+  if (a.kv_kind == KV_SEPARATE && a.dqk == 128 && tiles <= 3) return {3, 4};
+  if (a.kv_kind == KV_SHARED && a.dqk == 128 && tiles <= 3) return {3, 4};
+  if (a.dqk >= 256) return {4, 1};
+  return {4, 2};
+}
+
+template <int DQK, int DV, int KV, int W, int NG, int D>
 hipError_t launch_mfma_attn(const AttnArgs& a, hipStream_t s) {
   const int G = a.hq / a.hkv;
   const int tiles = (a.n_qsets * G + 15) / 16;
-  const int groups = (tiles + kNW - 1) / kNW;
+  const int groups = (tiles + W - 1) / W;
   const int per = ((a.max_entries + a.n_split - 1) / a.n_split + kTile - 1) / kTile * kTile;
   dim3 grid(a.n_split, a.rows.n_rows * a.hkv, groups);
-  hipLaunchKernelGGL((attn_mfma<DQK, DV, KV, D>), grid, dim3(64 * kNW), 0, s, a, per);
+  hipLaunchKernelGGL((attn_mfma<DQK, DV, KV, W, NG, D>), grid, dim3(64 * W * NG), 0, s, a, per);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const int64_t nrows = (int64_t)a.n_qsets * a.rows.n_rows * a.hq;
   hipLaunchKernelGGL(attn_combine, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <int DQK, int DV, int KV, int D>
+hipError_t launch_shaped(const AttnArgs& a, hipStream_t s) {
+  const AttnShape sh = attn_shape(a);
+  if (sh.w == 3 && sh.ng == 4) {
+    if constexpr (DQK == 128) return launch_mfma_attn<DQK, DV, KV, 3, 4, 1>(a, s);
+  } else if (sh.ng == 1) {
+    if constexpr (DQK >= 256) return launch_mfma_attn<DQK, DV, KV, 4, 1, D>(a, s);
+  } else {
+    if constexpr (DQK < 256) return launch_mfma_attn<DQK, DV, KV, 4, 2, D>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -522,7 +655,7 @@ void attn_plan(AttnArgs& a) {
   if (a.dtype == 0) return;
   const int G = a.hq / a.hkv;
   const int tiles = (a.n_qsets * G + 15) / 16;
-  const int64_t base = (int64_t)a.rows.n_rows * a.hkv * ((tiles + kNW - 1) / kNW);
+  const int64_t base = (int64_t)a.rows.n_rows * a.hkv * ((tiles + attn_shape(a).w - 1) / attn_shape(a).w);
   const int max_split = (a.max_entries + kTile - 1) / kTile;
   // enough entry ranges to occupy the chip, each within the slot table
   int ns = (a.max_entries + kMaxEntries - 1) / kMaxEntries;
@@ -547,14 +680,14 @@ hipError_t launch_attn_gather(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.kv_kind == KV_SEPARATE) {
-    if (a.dqk == 128 && a.dv == 128) return launch_mfma_attn<128, 128, KV_SEPARATE, 4>(a, s);
-    if (a.dqk == 256 && a.dv == 256) return launch_mfma_attn<256, 256, KV_SEPARATE, 2>(a, s);
+    if (a.dqk == 128 && a.dv == 128) return launch_shaped<128, 128, KV_SEPARATE, 2>(a, s);
+    if (a.dqk == 256 && a.dv == 256) return launch_shaped<256, 256, KV_SEPARATE, 2>(a, s);
   } else if (a.kv_kind == KV_SHARED) {
-    if (a.dqk == 576 && a.dv == 512) return launch_mfma_attn<576, 512, KV_SHARED, 2>(a, s);
-    if (a.dqk == 512 && a.dv == 512) return launch_mfma_attn<512, 512, KV_SHARED, 2>(a, s);
-    if (a.dqk == 128 && a.dv == 128) return launch_mfma_attn<128, 128, KV_SHARED, 4>(a, s);
+    if (a.dqk == 576 && a.dv == 512) return launch_shaped<576, 512, KV_SHARED, 2>(a, s);
+    if (a.dqk == 512 && a.dv == 512) return launch_shaped<512, 512, KV_SHARED, 2>(a, s);
+    if (a.dqk == 128 && a.dv == 128) return launch_shaped<128, 128, KV_SHARED, 2>(a, s);
   } else if (a.kv_kind == KV_FP4) {
-    if (a.dqk == 512 && a.dv == 512) return launch_mfma_attn<512, 512, KV_FP4, 4>(a, s);
+    if (a.dqk == 512 && a.dv == 512) return launch_shaped<512, 512, KV_FP4, 4>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -97,8 +97,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return u >> 16;
 }
 
+// Two floats -> packed bfloat16 pair (lo in the low half), round to nearest
+// even: one v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // OCP E4M3 (e4m3fn) byte -> float.  NaN codes are not expected in scales.
