@@ -59,8 +59,8 @@
  * ------------
  * Entry e of sequence b lives in page p = block_table[b * max_pages +
  * e / page_size] (or p = b * max_pages + e / page_size when block_table is
- * NULL) at slot u = p * page_size + e % page_size; its bytes start at
- * data + u * row_stride.  Every visible entry must be backed by the cache
+ * NULL) at slot u = p * page_size + e % page_size (u must be below 2^31);
+ * its bytes start at data + u * row_stride.  Every visible entry must be backed by the cache
  * (n_avail <= max_pages * page_size); the kernels do not check this.  Within a row, head h channel c is element
  * h * width + c ("Lecture 10", section 5.5: a sparse kernel fetches entries by
  * index, through the block table when paged; "HySparse2", section 7.2: no
@@ -114,8 +114,10 @@ typedef struct {
   int32_t max_pages;         /* pages per sequence in block_table             */
   int32_t heads;             /* heads per row                                 */
   int32_t width;             /* channels per head                             */
-  int64_t row_stride;        /* bytes between consecutive slots (16-B aligned)*/
-  int64_t scale_stride;      /* bytes between consecutive scale rows          */
+  int64_t row_stride;        /* bytes between consecutive slots (16-B aligned,
+                                below 2^31)                                    */
+  int64_t scale_stride;      /* bytes between consecutive scale rows (below
+                                2^31)                                          */
   int32_t dtype;             /* sa_dtype                                      */
   int32_t reserved;
 } sa_cache;

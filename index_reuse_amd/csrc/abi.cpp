@@ -69,6 +69,9 @@ sa_status check_cache(const sa_cache& c, const char* op, const char* name, int64
         (long long)min_row_bytes);
   CHECK(c.row_stride % 16 == 0 && aligned16(c.data), SA_ERR_SHAPE,
         "%s: %s.data and row_stride must be 16-byte aligned", op, name);
+  CHECK(c.row_stride < (int64_t(1) << 31) && c.scale_stride >= 0 &&
+            c.scale_stride < (int64_t(1) << 31),
+        SA_ERR_SHAPE, "%s: %s.row_stride and scale_stride must be below 2^31", op, name);
   return SA_OK;
 }
 

@@ -40,12 +40,20 @@ constexpr int kTile = 32;   // entries per tile
 
 enum { KV_SEPARATE = 0, KV_SHARED = 1, KV_FP4 = 2 };
 
+// Low (high) 16-bit halves of a and b packed as {a, b}: one v_perm_b32 each
+// (selector bytes 0-3 pick bytes of the second operand, 4-7 of the first).
 __device__ __forceinline__ uint32_t lo16x2(uint32_t a, uint32_t b) {
-  return (a & 0xFFFFu) | (b << 16);
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 __device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xFFFF0000u);
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
+
+// 2^x on the hardware exp unit (v_exp_f32): exact at 0, 0 at -inf; results
+// below 2^-126 flush to zero, which softmax weights can afford.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr int32_t kPadSlot = int32_t(0x80000000u);  // marks a padding entry
 
 // Dequantise 32 FP4 channels (16 code bytes, 2 E4M3 scales) into 16 packed
 // bf16 pairs.  e2m1 * e4m3 has at most 6 significant bits, so the bf16 value
@@ -205,12 +213,18 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
     }
   }
   __syncthreads();
-  // Entries without a slot (tile padding, -1 indices) read the rows of the
-  // range's first real entry instead: finite data that the mask gives weight
-  // exactly 0.  A range with no real entry computes nothing.
+  // A range with no real entry computes nothing.
   const int first = lds.first;
   const int nsteps_run = first < ne ? nsteps : 0;
-  const int64_t dummy = first < ne ? lds.slot[first] : 0;
+  {
+    // Padding entries read the range's first real entry: finite data that
+    // the mask gives weight exactly 0.  Bit 31 marks them.
+    const int dummy = first < ne ? lds.slot[first] : 0;
+    const int n_tab = (nsteps + D) * NG * kTile;
+    for (int i = tid; i < n_tab; i += NTH)
+      if (lds.slot[i] < 0) lds.slot[i] = dummy | kPadSlot;
+  }
+  __syncthreads();
 
   // Chunk c of a step: tile c / C_ALL of the step, then K or V row part.
   // Issue the global loads of step s into registers.  Branch-free, so the
@@ -227,16 +241,16 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
       const int cc = is_k ? cw : cw - T::C_K;
       const int cpr = is_k ? T::CPR_K : T::CPR_V;
       const int e = cc / cpr, part = cc % cpr;
-      const int sl = lds.slot[(s * NG + gs) * kTile + e];
-      const int64_t slot = sl >= 0 ? (int64_t)sl : dummy;
+      const uint32_t slot = (uint32_t)lds.slot[(s * NG + gs) * kTile + e] & 0x7FFFFFFFu;
       if constexpr (T::FP4) {
         regs.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            a.k.data + slot * a.k.row_stride + g * (DQK / 2) + part * 16));
-        regs.sc[u] = *reinterpret_cast<const uint16_t*>(a.k.scale + slot * a.k.scale_stride +
-                                                        g * (DQK / 16) + part * 2);
+            a.k.data + (uint64_t)slot * (uint32_t)a.k.row_stride + g * (DQK / 2) + part * 16));
+        regs.sc[u] = *reinterpret_cast<const uint16_t*>(
+            a.k.scale + (uint64_t)slot * (uint32_t)a.k.scale_stride + g * (DQK / 16) + part * 2);
       } else {
-        const char* base = is_k ? a.k.data + slot * a.k.row_stride + g * (DQK * 2)
-                                : a.v.data + slot * a.v.row_stride + g * (DV * 2);
+        const char* base =
+            is_k ? a.k.data + (uint64_t)slot * (uint32_t)a.k.row_stride + g * (DQK * 2)
+                 : a.v.data + (uint64_t)slot * (uint32_t)a.v.row_stride + g * (DV * 2);
         regs.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + part * 16));
       }
     }
@@ -311,7 +325,7 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
     // leave O untouched; probabilities stay below 2^8 (exact bf16 range).
     if (__builtin_amdgcn_ballot_w64(tmax > m_run + 8.0f)) {
       const float m_new = fmaxf(m_run, tmax);
-      const float alpha = m_new == -__builtin_huge_valf() ? 1.0f : exp2f(m_run - m_new);
+      const float alpha = m_new == -__builtin_huge_valf() ? 1.0f : fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt)
@@ -326,7 +340,7 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[mt][i] = exp2f(s[mt][i] - m_use);
+        p[mt][i] = fast_exp2(s[mt][i] - m_use);
         psum += p[mt][i];
       }
     psum = xor16_32_sum(psum);
@@ -419,7 +433,7 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
       const float m = lds.ml[gg][wq][col][0];
-      f[gg] = m == -__builtin_huge_valf() ? 0.0f : exp2f(m - M);
+      f[gg] = m == -__builtin_huge_valf() ? 0.0f : fast_exp2(m - M);
       Ls += f[gg] * lds.ml[gg][wq][col][1];
     }
 #pragma unroll
