@@ -7,21 +7,25 @@
 // scored by its maximum over visible members, the first max_blocks blocks in
 // (max desc, block asc) order are kept and their members form the pool.
 //
-// Scores become order-preserving uint32 keys (-0 folded onto +0).  The kept
-// set is {key > theta} plus the elements with key == theta up to index jstar,
-// where (theta, jstar) is the take-th element of the total order.  Decode
-// rows are few and long, so the per-element work is spread over chunks of
-// 2048 elements on many workgroups and only a small per-row step is serial:
-//   1. hist (chunks x rows): a histogram of the top 12 key bits of every
-//      chunk, merged into the row's histogram with global atomics;
-//   2. threshold (one workgroup per row): the bin of the take-th key; one
-//      light pass over the row counts, per chunk, the keys above that bin and
-//      gathers the bin's few keys into LDS; a second 12-bit level and an
-//      exact comparison rank give (theta, jstar); per-chunk kept counts give
-//      each chunk its output offset;
-//   3. emit (chunks x rows): each chunk writes its kept indices ascending at
-//      its offset (wave-contiguous segments, ballot ranks).
-// The output depends only on the total order, never on thread timing.
+// Scores become order-preserving uint32 keys (-0 folded onto +0; key 0 marks
+// a non-candidate).  The kept set is {key > theta} plus the first t elements
+// (lowest indices) with key == theta, where theta is the key of the take-th
+// element.  Rows are cut into chunks of 2048 elements and every kernel runs
+// one workgroup per (chunk, row), so no step of the selection is serial per
+// row:
+//   1. hist: a histogram of the top 12 key bits of each chunk, merged into
+//      the row's histogram with global atomics;
+//   2. scan: every chunk derives the threshold bin b1 from the row histogram
+//      and records how many of its elements lie above b1; the members of b1
+//      (typically a few hundred to a few thousand) are appended to a per-row
+//      list with their element index, with the list's min and max key;
+//   3. emit: every chunk resolves theta exactly from the member list (two
+//      more histogram levels: key bits 19..8, then 7..0), derives its output
+//      offset from the chunk counts and the members before it, and writes its
+//      kept elements ascending (wave-contiguous segments, ballot ranks).
+// Members that all share one key (ties) need no list; a list that overflows
+// with distinct keys falls back to scanning the row.  The output depends only
+// on the total order, never on thread timing.
 #include "kernels.hpp"
 
 namespace sa {
@@ -55,14 +59,22 @@ __device__ __forceinline__ int wave_sum_i32(int x) {
   auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return (int)(b[0] + b[1]);
 }
-// inclusive prefix sum over the 64 lanes (a few calls per kernel)
+// inclusive prefix sum over the 64 lanes: row_shr steps inside each 16-lane
+// row (lanes shifted in from outside the row read 0), then the row totals
+template <int CTRL>
+__device__ __forceinline__ int dpp_z(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  x += dpp_z<0x111>(x);
+  x += dpp_z<0x112>(x);
+  x += dpp_z<0x114>(x);
+  x += dpp_z<0x118>(x);
+  const int t0 = __builtin_amdgcn_readlane(x, 15);
+  const int t1 = __builtin_amdgcn_readlane(x, 31);
+  const int t2 = __builtin_amdgcn_readlane(x, 47);
+  x += (lane >= 16 ? t0 : 0) + (lane >= 32 ? t1 : 0) + (lane >= 48 ? t2 : 0);
   return x;
 }
 __device__ __forceinline__ uint64_t lanes_below() {
@@ -74,17 +86,27 @@ __device__ __forceinline__ uint64_t lanes_below() {
 constexpr int kL1Bits = 12;            // level-1 digit: key bits 31..20
 constexpr int kL1 = 1 << kL1Bits;      // level-1 bins
 constexpr int kL2 = 4096;              // level-2 bins: key bits 19..8
-constexpr int kCap1 = 8192;            // LDS slots for the level-1 bin's keys
-constexpr int kRankMax = 512;          // largest level-2 bin ranked by comparison
 constexpr int kChunk = 2048;           // elements per chunk workgroup
 constexpr int kChunkT = 256;           // threads per chunk workgroup
-constexpr int kTT = 1024;              // threads of the per-row threshold workgroup
-constexpr int kTW = kTT / 64;
+constexpr int kQ = kChunk / kChunkT;   // elements per thread
+constexpr int kCW = kChunkT / 64;      // waves per chunk workgroup
 constexpr int kMaxChunks = 1024;       // chunks per row (2M elements)
 constexpr int kHistStride = kL1 + 64;  // per-row histogram words (+ valid count)
-constexpr int kThrWords = 8;           // per-row results: theta, jstar, take, extra
+constexpr int kRecWords = 16;          // per-row record (see Rec)
+constexpr int kCapM = 4096;            // member-list capacity per row
 
 enum { SRC_TOKEN_FULL = 0, SRC_TOKEN_CAND = 1, SRC_BLOCK = 2, SRC_POOL = 3 };
+
+// Per-row record words.
+enum {
+  REC_MCOUNT = 0,  // members of the threshold bin seen (may exceed kCapM)
+  REC_MMIN = 1,    // smallest member key
+  REC_MMAX = 2,    // largest member key
+  REC_B1 = 3,      // threshold bin
+  REC_ABOVE = 4,   // elements in bins above it
+  REC_TAKE = 5,    // elements to keep
+  REC_MODE = 6,    // 0 keep nothing, 1 keep every valid element, 2 threshold
+};
 
 // Float value of an order-preserving key (inverse of order_key).
 __device__ __forceinline__ float key_value(uint32_t k) {
@@ -93,10 +115,13 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 
 // Workspace views (see topk_workspace_bytes).
 struct Ws {
-  uint32_t* hist;    // [R][kHistStride], zero on entry, left zero
-  uint32_t* thr;     // [R][kThrWords]
-  int32_t* offs;     // [R][chunk_stride] output offset of every chunk
-  float* beta;       // [R][beta_stride] block maxima (pool mode)
+  uint32_t* hist;  // [R][kHistStride], zero on entry, left zero
+  uint32_t* rec;   // [R][kRecWords]
+  uint32_t* mkey;  // [R][kCapM] member keys
+  int32_t* midx;   // [R][kCapM] member element indices
+  int32_t* cgt;    // [R][chunk_stride] elements above the threshold bin, per chunk
+  int32_t* cm;     // [R][chunk_stride] members of the threshold bin, per chunk
+  float* beta;     // [R][beta_stride] block maxima (pool mode)
   int64_t chunk_stride;
 };
 
@@ -177,11 +202,7 @@ __device__ __forceinline__ Src<KIND> make_src(const SelectArgs& a, const Ws& ws,
   return s;
 }
 
-__device__ __forceinline__ bool kept(uint32_t theta, int jstar, uint32_t key, int j) {
-  return key != 0u && (key > theta || (key == theta && j <= jstar));
-}
-
-// -------------------------------------------------------------- 1. hist
+// -------------------------------------------------------------- 0. blocks
 // beta[r][j] = max of the visible scores of block j (one thread per block).
 __global__ __launch_bounds__(256) void block_max_kernel(SelectArgs a, Ws ws) {
   const int r = blockIdx.y;
@@ -196,12 +217,89 @@ __global__ __launch_bounds__(256) void block_max_kernel(SelectArgs a, Ws ws) {
   ws.beta[(int64_t)r * a.beta_stride + j] = m;
 }
 
-// Level-1 histogram (key bits 31..20) of one chunk, merged into the row's.
+// Element q of thread t in a chunk: wave-contiguous 512-element segments,
+// lane-interleaved inside (coalesced, and in-wave order is (q, lane)).
+__device__ __forceinline__ int chunk_elem(int q) {
+  return (threadIdx.x >> 6) * (kChunk / kCW) + q * 64 + (threadIdx.x & 63);
+}
+
+// The bin holding the rank-th (1-based) element counting from the top bin of
+// an NB-bin LDS histogram (NB = 256 or 4096); returns (bin, elements in
+// higher bins) through u[0], u[1].  Thread t owns bins [NB - BPT(t+1),
+// NB - BPT t); every thread of the workgroup takes part.
+template <int NB>
+__device__ __forceinline__ void locate(const uint32_t* hist, int rank, int* wred, uint32_t* u) {
+  constexpr int BPT = NB / kChunkT;
+  static_assert(BPT == 1 || BPT % 4 == 0, "bins per thread");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int lo = NB - BPT * (tid + 1);
+  uint32_t c[BPT];
+  if constexpr (BPT == 1) {
+    c[0] = hist[lo];
+  } else {
+#pragma unroll
+    for (int v = 0; v < BPT / 4; ++v) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(hist + lo + 4 * v);
+      c[4 * v] = x[0];
+      c[4 * v + 1] = x[1];
+      c[4 * v + 2] = x[2];
+      c[4 * v + 3] = x[3];
+    }
+  }
+  int mine = 0;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) mine += (int)c[q];
+  const int incl = wave_incl_scan(mine);
+  if (lane == 63) wred[tid >> 6] = incl;
+  __syncthreads();
+  int above = incl - mine;
+#pragma unroll
+  for (int w = 0; w < kCW - 1; ++w) above += w < (tid >> 6) ? wred[w] : 0;
+  if (above < rank && rank <= above + mine) {
+    int acc = above;
+    int bin = lo, acc_at = above;
+    bool found = false;
+#pragma unroll
+    for (int q = BPT - 1; q >= 0; --q) {  // from this thread's top bin down
+      const int cq = (int)c[q];
+      if (!found && acc + cq >= rank) {
+        bin = lo + q;
+        acc_at = acc;
+        found = true;
+      }
+      acc += cq;
+    }
+    u[0] = (uint32_t)bin;
+    u[1] = (uint32_t)acc_at;
+  }
+  __syncthreads();
+}
+
+// Sum over the workgroup (every thread gets it).
+__device__ __forceinline__ int block_sum(int v, int* wred) {
+  v = wave_sum_i32(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = 0;
+  for (int w = 0; w < kCW; ++w) t += wred[w];
+  return t;
+}
+
+// -------------------------------------------------------------- 1. hist
+// Level-1 histogram (key bits 31..20) of one chunk, merged into the row's;
+// chunk 0 also resets the row's record for the scan step.
 template <int KIND>
 __global__ __launch_bounds__(kChunkT) void hist_kernel(SelectArgs a, Ws ws) {
   __shared__ uint32_t h[kL1];
   __shared__ uint32_t nvalid;
   const int r = blockIdx.y;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    uint32_t* rec = ws.rec + (int64_t)r * kRecWords;
+    rec[REC_MCOUNT] = 0u;
+    rec[REC_MMIN] = 0xFFFFFFFFu;
+    rec[REC_MMAX] = 0u;
+  }
   const RowInfo ri = row_info(a.rows, r);
   const Src<KIND> s = make_src<KIND>(a, ws, r, ri);
   const int j0 = blockIdx.x * kChunk;
@@ -210,12 +308,12 @@ __global__ __launch_bounds__(kChunkT) void hist_kernel(SelectArgs a, Ws ws) {
   if (threadIdx.x == 0) nvalid = 0u;
   __syncthreads();
   int valid = 0;
-  uint32_t keys[kChunk / kChunkT];
+  uint32_t keys[kQ];
 #pragma unroll
-  for (int i = 0; i < kChunk / kChunkT; ++i) keys[i] = s.key_c(j0 + i * kChunkT + (int)threadIdx.x);
+  for (int q = 0; q < kQ; ++q) keys[q] = s.key_c(j0 + chunk_elem(q));
 #pragma unroll
-  for (int i = 0; i < kChunk / kChunkT; ++i) {
-    const uint32_t key = keys[i];
+  for (int q = 0; q < kQ; ++q) {
+    const uint32_t key = keys[q];
     if (key) {
       atomicAdd(&h[key >> (32 - kL1Bits)], 1u);
       ++valid;
@@ -232,390 +330,302 @@ __global__ __launch_bounds__(kChunkT) void hist_kernel(SelectArgs a, Ws ws) {
   if (Src<KIND>::may_be_invalid() && threadIdx.x == 0) atomicAdd(&gh[kL1], nvalid);
 }
 
-// --------------------------------------------------------- 2. threshold
-struct ThrShared {
-  uint32_t hist[kL2];
-  uint32_t ckey[kCap1];
-  int32_t cidx[kCap1];
-  int32_t ccnt[kMaxChunks];  // per-chunk counts
-  uint32_t wred[kTW];
-  uint32_t u[8];
-};
-
-// Locate, scanning bins from the top, the bin holding the rank-th (1-based)
-// element of a kL2-bin histogram in LDS; writes it and the count above it to
-// sh.u[0], sh.u[1].
-__device__ __forceinline__ void locate(const uint32_t* hist, int rank, ThrShared& sh) {
-  constexpr int BPT = kL2 / kTT;
+// -------------------------------------------------------------- 2. scan
+template <int KIND>
+__global__ __launch_bounds__(kChunkT) void scan_kernel(SelectArgs a, Ws ws, int kk) {
+  __shared__ __align__(16) uint32_t h[kL1];
+  __shared__ int wred[kCW];
+  __shared__ uint32_t u[4];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int hi = kL2 - BPT * tid;
-  int c[BPT];
-  int mine = 0;
+  const int r = blockIdx.y, c = blockIdx.x;
+  const uint32_t* gh = ws.hist + (int64_t)r * kHistStride;
+  // the row histogram: 4 x 16 bytes per thread, loaded before anything else
+  constexpr int HV = kL1 / 4 / kChunkT;
+  u32x4 hv[HV];
 #pragma unroll
-  for (int q = 0; q < BPT; ++q) {
-    c[q] = (int)hist[hi - 1 - q];
-    mine += c[q];
-  }
-  const int incl = wave_incl_scan(mine);
-  if (lane == 63) sh.wred[tid >> 6] = (uint32_t)incl;
-  __syncthreads();
-  int above = incl - mine;
-  for (int w = 0; w < (tid >> 6); ++w) above += (int)sh.wred[w];
-  if (above < rank && rank <= above + mine) {
-    int acc = above;
-#pragma unroll
-    for (int q = 0; q < BPT; ++q) {
-      if (acc + c[q] >= rank) {
-        sh.u[0] = (uint32_t)(hi - 1 - q);
-        sh.u[1] = (uint32_t)acc;
-        break;
-      }
-      acc += c[q];
-    }
-  }
-  __syncthreads();
-}
-
-// Per row: (theta, jstar, take) and the output offset of every chunk.
-// Element j of the row is visited by thread j % kTT (coalesced loads); its
-// chunk is j / kChunk.  Rows longer than kMaxCnt elements keep chunk counts
-// in LDS with atomics instead of registers.
-template <int KIND, int KPT>
-__global__ __launch_bounds__(kTT) void threshold_kernel(SelectArgs a, Ws ws, int kk) {
-  __shared__ ThrShared sh;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const uint64_t below = lanes_below();
-  const int r = blockIdx.x;
+  for (int v = 0; v < HV; ++v) hv[v] = reinterpret_cast<const u32x4*>(gh)[v * kChunkT + tid];
+  const uint32_t gvalid = gh[kL1];
   const RowInfo ri = row_info(a.rows, r);
   const Src<KIND> s = make_src<KIND>(a, ws, r, ri);
-  uint32_t* gh = ws.hist + (int64_t)r * kHistStride;
-  uint32_t* thr = ws.thr + (int64_t)r * kThrWords;
-  int32_t* offs = ws.offs + (int64_t)r * ws.chunk_stride;
   const int n = s.n;
-  const int nch = (n + kChunk - 1) / kChunk;
-
-  for (int i = tid; i < kL1; i += kTT) sh.hist[i] = gh[i];
-  const int n_valid = Src<KIND>::may_be_invalid() ? (int)gh[kL1] : n;
+  const int j0 = c * kChunk;
+  if (j0 >= n && c > 0) return;
+  uint32_t* rec = ws.rec + (int64_t)r * kRecWords;
+#pragma unroll
+  for (int v = 0; v < HV; ++v) reinterpret_cast<u32x4*>(h)[v * kChunkT + tid] = hv[v];
+  const int n_valid = Src<KIND>::may_be_invalid() ? (int)gvalid : n;
   __syncthreads();
-  for (int i = tid; i < kHistStride; i += kTT) gh[i] = 0u;  // leave it zero for the next call
   const int take = min(kk, n_valid);
-
-  // How elements are kept: everything valid (mode 1), nothing (mode 0), or
-  // by threshold (mode 2).
-  int mode = take == 0 ? 0 : (take == n_valid ? 1 : 2);
+  const int mode = take == 0 ? 0 : (take == n_valid ? 1 : 2);
   uint32_t b1 = 0;
-  int need = 0;
+  int above = 0;
   if (mode == 2) {
-    locate(sh.hist, take, sh);
-    b1 = sh.u[0];
-    need = take - (int)sh.u[1];
+    locate<kL1>(h, take, wred, u);
+    b1 = u[0];
+    above = (int)u[1];
   }
-  const int m1 = mode == 2 ? (int)sh.hist[b1] : 0;
-  __syncthreads();
-
-  // One pass: per-chunk counts of certainly-kept (or valid) elements, and the
-  // level-1 bin's keys into LDS with a level-2 histogram.
-  for (int i = tid; i < nch; i += kTT) sh.ccnt[i] = 0;
-  for (int i = tid; i < kL2; i += kTT) sh.hist[i] = 0u;
-  if (tid == 0) sh.u[2] = 0u;
-  __syncthreads();
-  const bool gather = mode == 2 && m1 <= kCap1;
-  // Element j = it*kTT*KPT + i*kTT + tid: all KPT loads of a super-chunk are
-  // issued before any processing; chunk of slot i is it*KPT/2 + i/2.
-  constexpr int CPS = KPT / (kChunk / kTT);  // chunks per super-chunk
-  for (int it = 0; it * kTT * KPT < n; ++it) {
-    uint32_t kc[KPT];
+  if (c == 0 && tid == 0) {
+    rec[REC_B1] = b1;
+    rec[REC_ABOVE] = (uint32_t)above;
+    rec[REC_TAKE] = (uint32_t)take;
+    rec[REC_MODE] = (uint32_t)mode;
+  }
+  if (j0 >= n) return;
+  uint32_t keys[kQ];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) kc[i] = s.key_c(it * kTT * KPT + i * kTT + tid);
-    int cnt[CPS];
+  for (int q = 0; q < kQ; ++q) keys[q] = s.key_c(j0 + chunk_elem(q));
+  int n_gt = 0, n_hit = 0;
+  uint32_t hits = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-    for (int q = 0; q < CPS; ++q) cnt[q] = 0;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const uint32_t key = kc[i];
-      const uint32_t d1 = key >> 20;
-      cnt[i / (kChunk / kTT)] += mode == 1 ? key != 0u : (mode == 2 && key != 0u && d1 > b1);
-    }
-#pragma unroll
-    for (int q = 0; q < CPS; ++q) {
-      const int c = it * CPS + q;
-      const int v = wave_sum_i32(cnt[q]);
-      if (lane == 0 && v && c < nch) atomicAdd(&sh.ccnt[c], v);
-    }
-    if (gather) {
-      // hit bits of this thread's slots, then one wave prefix for the LDS
-      // offsets; the (rare) hits are re-read from the cache to be stored
-      uint64_t hits = 0;
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const uint32_t key = kc[i];
-        hits |= (uint64_t)(key != 0u && (key >> 20) == b1) << i;
-      }
-      const int nh = __popcll(hits);
-      const int incl = wave_incl_scan(nh);
-      const int wtot = __builtin_amdgcn_readlane(incl, 63);
-      uint32_t wbase = 0;
-      if (lane == 0 && wtot) wbase = atomicAdd(&sh.u[2], (uint32_t)wtot);
-      wbase = __builtin_amdgcn_readlane(wbase, 0);
-      uint32_t slot = wbase + (uint32_t)(incl - nh);
-      while (hits) {
-        const int i = __ffsll((unsigned long long)hits) - 1;
-        hits &= hits - 1;
-        const int j = it * kTT * KPT + i * kTT + tid;
-        const uint32_t key = s.key_c(j);
-        sh.ckey[slot] = key;
-        sh.cidx[slot] = j;
-        atomicAdd(&sh.hist[(key >> 8) & (kL2 - 1)], 1u);
-        ++slot;
-      }
+  for (int q = 0; q < kQ; ++q) {
+    const uint32_t key = keys[q];
+    const uint32_t d = key >> (32 - kL1Bits);
+    const bool gt = mode == 1 ? key != 0u : (mode == 2 && d > b1);
+    const bool hit = mode == 2 && key != 0u && d == b1;
+    n_gt += gt;
+    hits |= (uint32_t)hit << q;
+    if (hit) {
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
     }
   }
-  __syncthreads();
+  n_hit = __popc(hits);
+  const int64_t co = (int64_t)r * ws.chunk_stride + c;
+  const int tot_gt = block_sum(n_gt, wred);
+  if (mode != 2) {
+    if (tid == 0) {
+      ws.cgt[co] = tot_gt;
+      ws.cm[co] = 0;
+    }
+    return;
+  }
+  // append the members: one global atomic per wave
+  const int incl = wave_incl_scan(n_hit);
+  const int wtot = __builtin_amdgcn_readlane(incl, 63);
+  uint32_t wbase = 0;
+  if (lane == 0 && wtot) wbase = atomicAdd(&rec[REC_MCOUNT], (uint32_t)wtot);
+  wbase = __builtin_amdgcn_readlane(wbase, 0);
+  uint32_t slot = wbase + (uint32_t)(incl - n_hit);
+  uint32_t* mk = ws.mkey + (int64_t)r * kCapM;
+  int32_t* mj = ws.midx + (int64_t)r * kCapM;
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    if ((hits >> q) & 1u) {
+      if (slot < (uint32_t)kCapM) {
+        mk[slot] = keys[q];
+        mj[slot] = j0 + chunk_elem(q);
+      }
+      ++slot;
+    }
+  }
+  kmin = ~wave_max_u32(~kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0 && wtot) {
+    atomicMin(&rec[REC_MMIN], kmin);
+    atomicMax(&rec[REC_MMAX], kmax);
+  }
+  const int tot_hit = block_sum(n_hit, wred);
+  if (tid == 0) {
+    ws.cgt[co] = tot_gt;
+    ws.cm[co] = tot_hit;
+  }
+}
 
-  uint32_t theta = 0u;
-  int jstar = -1;
-  if (mode == 2 && gather) {
-    locate(sh.hist, need, sh);
-    const uint32_t b2 = sh.u[0];
-    const int need2 = need - (int)sh.u[1];
-    const int m2 = (int)sh.hist[b2];
-    const uint32_t pre = (b1 << 20) | (b2 << 8);
-    __syncthreads();
-    if (m2 <= kRankMax) {
-      // compact the level-2 bin, rank it exactly by (key desc, index asc)
-      uint32_t* k2 = sh.hist;
-      int32_t* j2 = reinterpret_cast<int32_t*>(sh.hist + kRankMax);
-      if (tid == 0) sh.u[2] = 0u;
-      __syncthreads();
-      for (int b0 = 0; b0 < m1; b0 += kTT) {
-        const int i = b0 + tid;
-        const bool hit = i < m1 && (sh.ckey[i] & 0xFFFFFF00u) == pre;
-        const uint64_t mk = __ballot(hit);
-        if (mk) {
-          const int lead = __ffsll((unsigned long long)mk) - 1;
-          uint32_t sl = 0;
-          if (lane == lead) sl = atomicAdd(&sh.u[2], (uint32_t)__popcll(mk));
-          sl = __builtin_amdgcn_readlane(sl, lead);
-          if (hit) {
-            const uint32_t slot = sl + (uint32_t)__popcll(mk & below);
-            k2[slot] = sh.ckey[i];
-            j2[slot] = sh.cidx[i];
+// -------------------------------------------------------------- 3. emit
+struct __align__(16) EmitShared {
+  uint32_t h[kL2];
+  uint32_t mk[kCapM];
+  int32_t mj[kCapM];
+  int wred[kCW];
+  int wcnt[kCW][2];
+  uint32_t u[4];
+};
+
+template <int KIND>
+__global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int pool_mode) {
+  __shared__ EmitShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = lanes_below();
+  const int r = blockIdx.y, c = blockIdx.x;
+  const RowInfo ri = row_info(a.rows, r);
+  const Src<KIND> s = make_src<KIND>(a, ws, r, ri);
+  const int n = s.n;
+  const int j0 = c * kChunk;
+  if (j0 >= n && c > 0) return;
+  const uint32_t* rec = ws.rec + (int64_t)r * kRecWords;
+  const int mode = (int)rec[REC_MODE];
+  const int take = (int)rec[REC_TAKE];
+  const uint32_t b1 = rec[REC_B1];
+  const int above = (int)rec[REC_ABOVE];
+  const int m1 = (int)rec[REC_MCOUNT];
+  const uint32_t mmin = rec[REC_MMIN], mmax = rec[REC_MMAX];
+  const int32_t* cgt = ws.cgt + (int64_t)r * ws.chunk_stride;
+  const int32_t* cm = ws.cm + (int64_t)r * ws.chunk_stride;
+  if (c == 0) {  // the histogram is not read after the scan step: leave it zero
+    uint32_t* gh = ws.hist + (int64_t)r * kHistStride;
+    for (int i = tid; i < kHistStride; i += kChunkT) gh[i] = 0u;
+  }
+
+  // theta, the theta-ties to keep (t_eq) and, for this chunk, the kept
+  // elements before it (offset) and the theta-ties before it (e_before)
+  uint32_t theta = mode == 1 ? 0u : 0xFFFFFFFFu;
+  int t_eq = 0, e_before = 0, e_total = 0, m_gt_before = 0;
+  int gt_before = 0;
+  for (int i = tid; i < c; i += kChunkT) gt_before += cgt[i];
+  gt_before = block_sum(gt_before, sh.wred);
+  if (mode == 2) {
+    const int need = take - above;
+    const uint32_t pre1 = b1 << 20;
+    int cnt_gt = above;
+    if (mmin == mmax) {
+      // every member has the same key: all of them are theta-ties
+      theta = mmin;
+      int eb = 0;
+      for (int i = tid; i < c; i += kChunkT) eb += cm[i];
+      e_before = block_sum(eb, sh.wred);
+      e_total = m1;
+    } else if (m1 <= kCapM) {
+      const uint32_t* gmk = ws.mkey + (int64_t)r * kCapM;
+      const int32_t* gmj = ws.midx + (int64_t)r * kCapM;
+      for (int i = tid; i < kL2; i += kChunkT) sh.h[i] = 0u;
+      for (int i0 = 0; i0 < m1; i0 += 4 * kChunkT) {
+        uint32_t kv[4];
+        int32_t jv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int i = min(i0 + v * kChunkT + tid, m1 - 1);
+          kv[v] = gmk[i];
+          jv[v] = gmj[i];
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int i = i0 + v * kChunkT + tid;
+          if (i < m1) {
+            sh.mk[i] = kv[v];
+            sh.mj[i] = jv[v];
           }
         }
       }
       __syncthreads();
-      if (tid < m2) {
-        const uint32_t ki = k2[tid];
-        const int ji = j2[tid];
-        int rank = 0;
-        for (int l = 0; l < m2; ++l) {
-          const uint32_t kl = k2[l];
-          rank += kl > ki || (kl == ki && j2[l] < ji);
-        }
-        if (rank == need2 - 1) {
-          sh.u[3] = ki;
-          sh.u[4] = (uint32_t)ji;
-        }
+      for (int i = tid; i < m1; i += kChunkT) atomicAdd(&sh.h[(sh.mk[i] >> 8) & (kL2 - 1)], 1u);
+      __syncthreads();
+      locate<kL2>(sh.h, need, sh.wred, sh.u);
+      const uint32_t b2 = sh.u[0];
+      const int above2 = (int)sh.u[1];
+      const uint32_t pre2 = pre1 | (b2 << 8);
+      __syncthreads();
+      for (int i = tid; i < 256; i += kChunkT) sh.h[i] = 0u;
+      __syncthreads();
+      for (int i = tid; i < m1; i += kChunkT)
+        if ((sh.mk[i] & 0xFFFFFF00u) == pre2) atomicAdd(&sh.h[sh.mk[i] & 255u], 1u);
+      __syncthreads();
+      locate<256>(sh.h, need - above2, sh.wred, sh.u);
+      theta = pre2 | sh.u[0];
+      cnt_gt = above + above2 + (int)sh.u[1];
+      int eb = 0, gb = 0, et = 0;
+      for (int i = tid; i < m1; i += kChunkT) {
+        const uint32_t k = sh.mk[i];
+        const bool before = sh.mj[i] < j0;
+        eb += before && k == theta;
+        gb += before && k > theta;
+        et += k == theta;
       }
-      __syncthreads();
-      theta = sh.u[3];
-      jstar = (int)sh.u[4];
-      __syncthreads();
+      e_before = block_sum(eb, sh.wred);
+      m_gt_before = block_sum(gb, sh.wred);
+      e_total = block_sum(et, sh.wred);
     } else {
-      // crowded level-2 bin: the last 8 bits by histogram over the LDS keys,
-      // then the need3-th tie by index (ties are few relative to the row)
-      for (int i = tid; i < 256; i += kTT) sh.hist[i] = 0u;
+      // the list overflowed with distinct keys: resolve over the whole row
+      for (int i = tid; i < kL2; i += kChunkT) sh.h[i] = 0u;
       __syncthreads();
-      for (int i = tid; i < m1; i += kTT)
-        if ((sh.ckey[i] & 0xFFFFFF00u) == pre) atomicAdd(&sh.hist[sh.ckey[i] & 255u], 1u);
-      __syncthreads();
-      if (tid == 0) {
-        int above = 0, d = 255;
-        for (; d > 0; --d) {
-          const int c = (int)sh.hist[d];
-          if (above + c >= need2) break;
-          above += c;
-        }
-        sh.u[0] = (uint32_t)d;
-        sh.u[1] = (uint32_t)above;
+      for (int j = tid; j < n; j += kChunkT) {
+        const uint32_t k = s.key(j);
+        if (k != 0u && (k >> 20) == b1) atomicAdd(&sh.h[(k >> 8) & (kL2 - 1)], 1u);
       }
       __syncthreads();
-      theta = pre | sh.u[0];
-      const int need3 = need2 - (int)sh.u[1];
-      // the need3-th smallest index among keys == theta: count, per tie, the
-      // ties with a smaller index
-      for (int i = tid; i < m1; i += kTT) {
-        if (sh.ckey[i] != theta) continue;
-        const int ji = sh.cidx[i];
-        int rank = 0;
-        for (int l = 0; l < m1; ++l) rank += sh.ckey[l] == theta && sh.cidx[l] < ji;
-        if (rank == need3 - 1) sh.u[4] = (uint32_t)ji;
+      locate<kL2>(sh.h, need, sh.wred, sh.u);
+      const uint32_t b2 = sh.u[0];
+      const int above2 = (int)sh.u[1];
+      const uint32_t pre2 = pre1 | (b2 << 8);
+      __syncthreads();
+      for (int i = tid; i < 256; i += kChunkT) sh.h[i] = 0u;
+      __syncthreads();
+      for (int j = tid; j < n; j += kChunkT) {
+        const uint32_t k = s.key(j);
+        if (k != 0u && (k & 0xFFFFFF00u) == pre2) atomicAdd(&sh.h[k & 255u], 1u);
       }
       __syncthreads();
-      jstar = (int)sh.u[4];
-      __syncthreads();
+      locate<256>(sh.h, need - above2, sh.wred, sh.u);
+      theta = pre2 | sh.u[0];
+      cnt_gt = above + above2 + (int)sh.u[1];
+      int eb = 0, gb = 0, et = 0;
+      for (int j = tid; j < n; j += kChunkT) {
+        const uint32_t k = s.key(j);
+        if (k == 0u || (k >> 20) != b1) continue;
+        eb += j < j0 && k == theta;
+        gb += j < j0 && k > theta;
+        et += k == theta;
+      }
+      e_before = block_sum(eb, sh.wred);
+      m_gt_before = block_sum(gb, sh.wred);
+      e_total = block_sum(et, sh.wred);
     }
-    // chunk counts of the kept keys inside the level-1 bin
-    for (int i = tid; i < m1; i += kTT) {
-      const int j = sh.cidx[i];
-      if (kept(theta, jstar, sh.ckey[i], j)) atomicAdd(&sh.ccnt[j / kChunk], 1);
-    }
-    __syncthreads();
-  } else if (mode == 2) {
-    // level-1 bin too crowded for LDS: resolve the remaining 20 key bits by
-    // radix passes over the row, then the tie by index, counting kept
-    // elements per chunk in the final pass
-    uint32_t prefix = b1 << 20, pmask = 0xFFF00000u;
-    int remaining = need;
-    const int shifts[3] = {12, 4, 0};
-    const int widths[3] = {8, 8, 4};
-    for (int p = 0; p < 3; ++p) {
-      const int shift = shifts[p];
-      const uint32_t dmask = (1u << widths[p]) - 1u;
-      for (int i = tid; i <= (int)dmask; i += kTT) sh.hist[i] = 0u;
-      __syncthreads();
-      for (int j = tid; j < n; j += kTT) {
-        const uint32_t key = s.key(j);
-        if (key != 0u && (key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int above = 0, d = (int)dmask;
-        for (; d > 0; --d) {
-          const int c = (int)sh.hist[d];
-          if (above + c >= remaining) break;
-          above += c;
-        }
-        sh.u[0] = (uint32_t)d;
-        sh.u[1] = (uint32_t)above;
-      }
-      __syncthreads();
-      remaining -= (int)sh.u[1];
-      prefix |= sh.u[0] << shift;
-      pmask |= dmask << shift;
-      __syncthreads();
-    }
-    theta = prefix;
-    // ties of theta in index order: per-chunk tie counts, then the chunk
-    // holding the remaining-th tie is scanned in order by one wave
-    for (int i = tid; i < nch; i += kTT) sh.hist[i] = 0u;
-    __syncthreads();
-    for (int j = tid; j < n; j += kTT)
-      if (s.key(j) == theta) atomicAdd(&sh.hist[j / kChunk], 1u);
-    __syncthreads();
-    if (tid < 64) {
-      int acc = 0, c = 0;
-      for (; c < nch; ++c) {
-        const int t = (int)sh.hist[c];
-        if (acc + t >= remaining) break;
-        acc += t;
-      }
-      // wave 0 walks chunk c in index order
-      int found = -1;
-      for (int j0 = c * kChunk; j0 < min(n, (c + 1) * kChunk) && found < 0; j0 += 64) {
-        const int j = j0 + lane;
-        const bool tie = j < n && s.key(j) == theta;
-        const uint64_t m = __ballot(tie);
-        const int cnt = __popcll(m);
-        if (acc + cnt >= remaining) {
-          const int want = remaining - acc;  // 1-based within this group
-          if (tie && (int)__popcll(m & below) == want - 1) sh.u[4] = (uint32_t)j;
-          found = 1;
-        }
-        acc += cnt;
-      }
-    }
-    __syncthreads();
-    jstar = (int)sh.u[4];
-    __syncthreads();
-    for (int j = tid; j < n; j += kTT) {
-      const uint32_t key = s.key(j);
-      if ((key >> 20) == b1 && kept(theta, jstar, key, j)) atomicAdd(&sh.ccnt[j / kChunk], 1);
-    }
-    __syncthreads();
+    t_eq = take - cnt_gt;
   }
+  const int offset = gt_before + m_gt_before + min(e_before, t_eq);
 
-  // exclusive prefix of the chunk counts -> output offsets
-  if (tid < 64) {
-    int run = 0;
-    for (int c0 = 0; c0 < nch; c0 += 64) {
-      const int c = c0 + lane;
-      const int v = c < nch ? sh.ccnt[c] : 0;
-      const int incl = wave_incl_scan(v);
-      if (c < nch) offs[c] = run + incl - v;
-      run += __builtin_amdgcn_readlane(incl, 63);
-    }
-  }
-  if (tid == 0) {
-    thr[0] = mode == 1 ? 0u : (mode == 0 ? 0xFFFFFFFFu : theta);
-    thr[1] = (uint32_t)(mode == 1 ? -1 : jstar);
-    thr[2] = (uint32_t)take;
-  }
-}
-
-// ------------------------------------------------------------- 3. emit
-// Each chunk writes its kept elements ascending at its offset.  Wave w owns
-// the contiguous quarter [w*512, (w+1)*512) of the chunk; lane l holds
-// elements q*64 + l, so in-wave order is (q, lane).
-template <int KIND>
-__global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int pool_mode) {
-  __shared__ int wtot[kChunkT / 64];
-  const int r = blockIdx.y, c = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t below = lanes_below();
-  const RowInfo ri = row_info(a.rows, r);
-  const Src<KIND> s = make_src<KIND>(a, ws, r, ri);
-  const uint32_t* thr = ws.thr + (int64_t)r * kThrWords;
-  const uint32_t theta = thr[0];
-  const int jstar = (int)thr[1];
-  const int take = (int)thr[2];
+  // padding and count (only the last block can be partial)
   const int bs = a.block;
   int32_t* out = pool_mode ? a.pool + (int64_t)r * a.pool_stride : a.idx + (int64_t)r * a.idx_stride;
   if (c == 0) {
-    // padding and count (only the last kept block can be partial)
     if (pool_mode) {
-      const int nb = s.n;
-      int pool_n = take * bs;
-      if (take > 0) {
-        const uint32_t klast = s.key(nb - 1);
-        if (kept(theta, jstar, klast, nb - 1)) pool_n -= nb * bs - ri.n_avail;
+      bool last_kept = false;
+      if (mode != 0 && n > 0) {
+        const uint32_t kl = s.key(n - 1);
+        last_kept = mode == 1 ? kl != 0u : (kl > theta || (kl == theta && e_total - 1 < t_eq));
       }
-      for (int i = pool_n + threadIdx.x; i < a.max_blocks * bs; i += kChunkT) out[i] = -1;
-      if (threadIdx.x == 0) a.pool_count[r] = pool_n;
+      const int pool_n = take * bs - (last_kept ? n * bs - ri.n_avail : 0);
+      for (int i = pool_n + tid; i < a.max_blocks * bs; i += kChunkT) out[i] = -1;
+      if (tid == 0) a.pool_count[r] = pool_n;
     } else {
-      for (int i = take + threadIdx.x; i < a.k; i += kChunkT) out[i] = -1;
-      if (threadIdx.x == 0) a.count[r] = take;
+      for (int i = take + tid; i < a.k; i += kChunkT) out[i] = -1;
+      if (tid == 0) a.count[r] = take;
     }
   }
-  const int j0 = c * kChunk;
-  if (take == 0 || j0 >= s.n) return;
-  constexpr int Q = kChunk / kChunkT;
-  uint32_t keys[Q];
+  if (mode == 0 || j0 >= n) return;
+
+  // emission: kept = key > theta, or a theta-tie whose rank among the row's
+  // ties (index order) is below t_eq
+  uint32_t keys[kQ];
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int j = j0 + wave * (kChunk / 4) + q * 64 + lane;
-    keys[q] = s.key_c(j);
-  }
-  uint32_t flags = 0u;
-  int tot = 0;
+  for (int q = 0; q < kQ; ++q) keys[q] = s.key_c(j0 + chunk_elem(q));
+  int w_gt = 0, w_eq = 0;
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int j = j0 + wave * (kChunk / 4) + q * 64 + lane;
-    const bool me = kept(theta, jstar, keys[q], j);
-    flags |= (uint32_t)me << q;
-    tot += __popcll(__ballot(me));
+  for (int q = 0; q < kQ; ++q) {
+    w_gt += __popcll(__ballot(keys[q] != 0u && keys[q] > theta));
+    w_eq += __popcll(__ballot(mode == 2 && keys[q] != 0u && keys[q] == theta));
   }
-  if (lane == 0) wtot[wave] = tot;
+  if (lane == 0) {
+    sh.wcnt[wave][0] = w_gt;
+    sh.wcnt[wave][1] = w_eq;
+  }
   __syncthreads();
-  int base = ws.offs[(int64_t)r * ws.chunk_stride + c];
-  for (int w = 0; w < wave; ++w) base += wtot[w];
+  int o = offset, eseen = e_before;
+  for (int w = 0; w < wave; ++w) {
+    const int eq = sh.wcnt[w][1];
+    o += sh.wcnt[w][0] + max(0, min(eq, t_eq - eseen));
+    eseen += eq;
+  }
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const bool me = (flags >> q) & 1u;
-    const uint64_t m = __ballot(me);
-    if (me) {
-      const int j = j0 + wave * (kChunk / 4) + q * 64 + lane;
-      const int rank = base + (int)__popcll(m & below);
+  for (int q = 0; q < kQ; ++q) {
+    const uint32_t k = keys[q];
+    const bool gt = k != 0u && k > theta;
+    const bool eq = mode == 2 && k != 0u && k == theta;
+    const uint64_t me = __ballot(eq);
+    const bool keep = gt || (eq && eseen + (int)__popcll(me & below) < t_eq);
+    const uint64_t mk = __ballot(keep);
+    if (keep) {
+      const int j = j0 + chunk_elem(q);
+      const int rank = o + (int)__popcll(mk & below);
       if (pool_mode) {
         const int lo = j * bs, mm = min(bs, ri.n_avail - lo);
         for (int u = 0; u < mm; ++u) out[rank * bs + u] = lo + u;
@@ -623,7 +633,8 @@ __global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int 
         out[rank] = s.position(j);
       }
     }
-    base += (int)__popcll(m);
+    o += (int)__popcll(mk);
+    eseen += (int)__popcll(me);
   }
 }
 
@@ -632,11 +643,9 @@ void run_select(const SelectArgs& a, const Ws& ws, int64_t max_n, int kk, int po
                 hipStream_t st) {
   const int R = a.rows.n_rows;
   dim3 gc((unsigned)((max_n + kChunk - 1) / kChunk), R);
+  if (gc.x == 0) gc.x = 1;  // chunk 0 writes counts and padding
   hipLaunchKernelGGL(hist_kernel<KIND>, gc, dim3(kChunkT), 0, st, a, ws);
-  if (max_n <= kTT * 32)
-    hipLaunchKernelGGL((threshold_kernel<KIND, 32>), dim3(R), dim3(kTT), 0, st, a, ws, kk);
-  else
-    hipLaunchKernelGGL((threshold_kernel<KIND, 64>), dim3(R), dim3(kTT), 0, st, a, ws, kk);
+  hipLaunchKernelGGL(scan_kernel<KIND>, gc, dim3(kChunkT), 0, st, a, ws, kk);
   hipLaunchKernelGGL(emit_kernel<KIND>, gc, dim3(kChunkT), 0, st, a, ws, pool_mode);
 }
 
@@ -650,30 +659,40 @@ int64_t chunk_stride(const SelectArgs& a) {
 
 size_t topk_workspace_bytes(const SelectArgs& a) {
   const int64_t R = a.rows.n_rows;
-  size_t b = (size_t)R * (kHistStride + kThrWords) * sizeof(uint32_t);
-  b += (size_t)R * chunk_stride(a) * sizeof(int32_t);
+  size_t b = (size_t)R * (kHistStride + kRecWords + 2 * kCapM) * sizeof(uint32_t);
+  b += (size_t)R * 2 * chunk_stride(a) * sizeof(int32_t);
   if (a.pool) b += (size_t)R * a.beta_stride * sizeof(float);
   return b;
 }
 
 // Workspace: level-1 histograms [R][kHistStride] (zero on entry, left zero),
-// per-row thresholds, per-chunk offsets, then (pool mode) block maxima.
+// per-row records, member lists, per-chunk counts, then (pool mode) block
+// maxima.
 hipError_t launch_topk_select(const SelectArgs& a, hipStream_t st) {
   if (a.rows.n_rows == 0) return hipSuccess;
   const int64_t R = a.rows.n_rows;
   Ws ws;
   ws.hist = reinterpret_cast<uint32_t*>(a.beta);
-  ws.thr = ws.hist + R * kHistStride;
+  ws.rec = ws.hist + R * kHistStride;
+  ws.mkey = ws.rec + R * kRecWords;
+  ws.midx = reinterpret_cast<int32_t*>(ws.mkey + R * kCapM);
   ws.chunk_stride = chunk_stride(a);
-  ws.offs = reinterpret_cast<int32_t*>(ws.thr + R * kThrWords);
-  ws.beta = reinterpret_cast<float*>(ws.offs + R * ws.chunk_stride);
-  if ((a.pool ? a.beta_stride : a.max_elems) > (int64_t)kChunk * kMaxChunks) return hipErrorInvalidValue;
+  ws.cgt = ws.midx + R * kCapM;
+  ws.cm = ws.cgt + R * ws.chunk_stride;
+  ws.beta = reinterpret_cast<float*>(ws.cm + R * ws.chunk_stride);
+  if ((a.pool ? max((int64_t)a.max_elems, a.beta_stride) : a.max_elems) >
+      (int64_t)kChunk * kMaxChunks)
+    return hipErrorInvalidValue;
   if (a.pool) {
     dim3 g2((unsigned)((a.beta_stride + 255) / 256), a.rows.n_rows);
     hipLaunchKernelGGL(block_max_kernel, g2, dim3(256), 0, st, a, ws);
     run_select<SRC_BLOCK>(a, ws, a.beta_stride, a.max_blocks, 1, st);
   }
   if (a.k > 0) {
+    // The pool holds the whole token top-k when there is no window and at
+    // least k blocks are kept: a block left out has max_blocks blocks before
+    // it in (max desc, block asc) order, and each of their maxima ranks
+    // before every token of the left-out block.
     if (a.pool && a.rows.window == 0 && a.max_blocks >= a.k)
       run_select<SRC_POOL>(a, ws, (int64_t)a.max_blocks * a.block, a.k, 0, st);
     else if (a.cand)
