@@ -201,6 +201,53 @@ def test_select_exact_on_given_scores(dev):
     assert np.array_equal(gi.cpu().numpy(), oi)
 
 
+def test_select_crowded_threshold_bin(dev):
+    """Rows whose threshold falls in a crowded top-12-bit key bin: thousands
+    of distinct keys (more than the per-row member list holds), thousands of
+    exact ties at the threshold, and both at once.  Token and pool selection
+    stay bit-exact against the oracle."""
+    from index_reuse_amd import Rows, topk_select
+
+    import oracle
+
+    S = 20000
+    g = torch.Generator().manual_seed(11)
+    ulp = 2.0 ** -23
+    rows = []
+    # distinct values in [1, 1.125): one level-1 bin holds all of them
+    perm = torch.randperm(S, generator=g).double()
+    rows.append(1.0 + perm * 32 * ulp)
+    # 6000 ties at 1.5 straddling the threshold, larger and smaller values around
+    r = torch.rand(S, generator=g).double()
+    idx = torch.randperm(S, generator=g)
+    r[idx[:6000]] = 1.5
+    r[idx[6000:8000]] = 3.0
+    rows.append(r)
+    # 3000 distinct values in one bin, each repeated about 7 times
+    rows.append(1.0 + (torch.randperm(S, generator=g) % 3000).double() * 64 * ulp)
+    # mostly one bin, with signed zeros and a few negatives
+    r = 1.0 + torch.randperm(S, generator=g).double() * 16 * ulp
+    r[idx[:500]] = -0.0
+    r[idx[500:700]] = 0.0
+    r[idx[700:900]] = -2.0
+    rows.append(r)
+    scores = torch.stack(rows).float()
+    R = scores.shape[0]
+    so = torch.zeros(R, dtype=torch.int32)
+    po = torch.full((R,), S - 1, dtype=torch.int32)
+    sl = torch.tensor([S], dtype=torch.int32)
+    for window, k, mb in ((0, 5000, 1000), (0, 4000, 2048), (50, 12000, 600)):
+        rr = Rows(so.to(dev), po.to(dev), sl.to(dev), 1, window)
+        gi, gc, gp, gpc = topk_select(rr, scores.to(dev), k, block=8, max_blocks=mb)
+        oi, oc, op, opc = oracle.topk_select(so, po, sl, 1, window, scores.double().numpy(), k,
+                                             block=8, max_blocks=mb)
+        torch.cuda.synchronize()
+        assert np.array_equal(gc.cpu().numpy(), oc)
+        assert np.array_equal(gi.cpu().numpy(), oi), (window, k)
+        assert np.array_equal(gpc.cpu().numpy(), opc)
+        assert np.array_equal(gp.cpu().numpy(), op), (window, k, mb)
+
+
 def test_deterministic_and_reuse(dev):
     """Two runs are bitwise identical; one fused call over all query sets
     equals one call per set (index reuse changes nothing numerically)."""
