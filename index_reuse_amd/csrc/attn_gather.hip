@@ -53,7 +53,6 @@ __device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) {
 // below 2^-126 flush to zero, which softmax weights can afford.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-constexpr int32_t kPadSlot = int32_t(0x80000000u);  // marks a padding entry
 
 // Dequantise 32 FP4 channels (16 code bytes, 2 E4M3 scales) into 16 packed
 // bf16 pairs.  e2m1 * e4m3 has at most 6 significant bits, so the bf16 value
@@ -97,11 +96,11 @@ struct AttnLds {
   };
   union {
     Tiles t;
-    float comb[(NG > 1 ? NG - 1 : 1) * W * 64 * CSTRIDE];
+    float comb[NG * W * 64 * CSTRIDE];
   } u;
   float ml[NG][W][16][2];
-  int32_t first;        // first entry of the range with a slot
-  int32_t slot[SLOTS];  // cache slot of every entry (-1: none)
+  int32_t wfirst[W * NG];  // per wave: first entry of the range with a slot
+  int32_t slot[SLOTS];     // cache slot of every entry (-1: none)
 };
 
 // Per-thread share of one step (NG tiles) of gathered rows, held in
@@ -184,9 +183,8 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
   // Padding to whole steps, and the D steps past the end that the prefetch
   // ring reads, are -1.  Loads are clamped rather than guarded so that a
   // thread's loads all issue before the first wait.
-  if (tid == 0) lds.first = 0x7FFFFFFF;
-  __syncthreads();
   {
+    int wfirst = 0x7FFFFFFF;
     const int n_tab = (nsteps + D) * NG * kTile;
     for (int i0 = 0; i0 < n_tab; i0 += PT * NTH) {
       int pos[PT];
@@ -206,25 +204,22 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
           slot = pos[j] >= 0 ? sl : -1;
         }
         if (i < n_tab) lds.slot[i] = slot;
-        // one LDS atomic per wave: the wave's lowest entry with a slot
+        // the wave's lowest entry with a slot
         const uint64_t has = __builtin_amdgcn_ballot_w64(slot >= 0);
-        if (has && lane == __builtin_ctzll(has)) atomicMin(&lds.first, i);
+        if (has) wfirst = min(wfirst, i0 + j * NTH + (tid & ~63) + (int)__builtin_ctzll(has));
       }
     }
+    if (lane == 0) lds.wfirst[wave] = wfirst;
   }
   __syncthreads();
-  // A range with no real entry computes nothing.
-  const int first = lds.first;
+  // Padding entries (slot -1) read the rows of the range's first real entry:
+  // finite data that the mask gives weight exactly 0.  A range with no real
+  // entry computes nothing.
+  int first = 0x7FFFFFFF;
+#pragma unroll
+  for (int w = 0; w < W * NG; ++w) first = min(first, lds.wfirst[w]);
   const int nsteps_run = first < ne ? nsteps : 0;
-  {
-    // Padding entries read the range's first real entry: finite data that
-    // the mask gives weight exactly 0.  Bit 31 marks them.
-    const int dummy = first < ne ? lds.slot[first] : 0;
-    const int n_tab = (nsteps + D) * NG * kTile;
-    for (int i = tid; i < n_tab; i += NTH)
-      if (lds.slot[i] < 0) lds.slot[i] = dummy | kPadSlot;
-  }
-  __syncthreads();
+  const uint32_t dummy = first < ne ? (uint32_t)lds.slot[first] : 0u;
 
   // Chunk c of a step: tile c / C_ALL of the step, then K or V row part.
   // Issue the global loads of step s into registers.  Branch-free, so the
@@ -241,7 +236,8 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
       const int cc = is_k ? cw : cw - T::C_K;
       const int cpr = is_k ? T::CPR_K : T::CPR_V;
       const int e = cc / cpr, part = cc % cpr;
-      const uint32_t slot = (uint32_t)lds.slot[(s * NG + gs) * kTile + e] & 0x7FFFFFFFu;
+      const int sv = lds.slot[(s * NG + gs) * kTile + e];
+      const uint32_t slot = sv >= 0 ? (uint32_t)sv : dummy;
       if constexpr (T::FP4) {
         regs.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
             a.k.data + (uint64_t)slot * (uint32_t)a.k.row_stride + g * (DQK / 2) + part * 16));
@@ -407,46 +403,84 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
     }
   }
 
-  // Merge the entry groups: every wave publishes (m, l, O^T) in LDS (same
-  // lane layout for every group), then group 0 rescales to the common max
-  // and sums.
+  // Merge the entry groups: every wave publishes (m, l, O^T) in LDS, lane
+  // (row, gq) storing its 32 channels as [i][j] (channel 32gq + 8i + j);
+  // then wave (grp, wq) finalises channel blocks grp, grp + NG, ... (32
+  // channels each) of its 16 query rows over all groups: lane (row, i) sums 8
+  // contiguous channels and stores them.
   if constexpr (NG > 1) {
-    static_assert(NJB == 1, "the group merge holds one 128-channel block");
+    static_assert(NJB == 1 && 4 % NG == 0, "the group merge spreads 4 channel blocks over the groups");
     __syncthreads();  // every tile buffer is free from here on
     if (gq == 0) {
       lds.ml[grp][wq][col][0] = m_run;
       lds.ml[grp][wq][col][1] = l_run;
     }
-    if (grp > 0) {
-      f32x4* dst = reinterpret_cast<f32x4*>(
-          &lds.u.comb[(((grp - 1) * W + wq) * 64 + lane) * L::CSTRIDE]);
+    {
+      f32x4* dst = reinterpret_cast<f32x4*>(&lds.u.comb[((grp * W + wq) * 64 + lane) * L::CSTRIDE]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) dst[j] = O[j];
+      for (int i = 0; i < 4; ++i) {
+        dst[2 * i] = f32x4{O[0][i], O[1][i], O[2][i], O[3][i]};
+        dst[2 * i + 1] = f32x4{O[4][i], O[5][i], O[6][i], O[7][i]};
+      }
     }
     __syncthreads();
-    if (grp != 0) return;
+    if (!active) return;
+    const int row = lane & 15, part = lane >> 4;
+    const int qr = qrow0 + row;
+    if (qr >= Mq) return;
     float M = -__builtin_huge_valf();
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, lds.ml[gg][wq][col][0]);
-    float f[NG];
-    float Ls = 0.0f;
+    for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, lds.ml[gg][wq][row][0]);
+    float Ls = 0.0f, f[NG];
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
-      const float m = lds.ml[gg][wq][col][0];
+      const float m = lds.ml[gg][wq][row][0];
       f[gg] = m == -__builtin_huge_valf() ? 0.0f : fast_exp2(m - M);
-      Ls += f[gg] * lds.ml[gg][wq][col][1];
+      Ls += f[gg] * lds.ml[gg][wq][row][1];
     }
+    const int R = a.rows.n_rows;
+    const int set = qr / G, h = g * G + qr % G;
+    const int64_t orow = ((int64_t)set * R + r) * a.hq + h;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) O[j] *= f[0];
+    for (int cb = grp; cb < 4; cb += NG) {
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int gg = 1; gg < NG; ++gg) {
+    for (int gg = 0; gg < NG; ++gg) {
       const f32x4* src = reinterpret_cast<const f32x4*>(
-          &lds.u.comb[(((gg - 1) * W + wq) * 64 + lane) * L::CSTRIDE]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) O[j] += f[gg] * src[j];
+          &lds.u.comb[((gg * W + wq) * 64 + row + 16 * cb) * L::CSTRIDE + 8 * part]);
+      acc0 += f[gg] * src[0];
+      acc1 += f[gg] * src[1];
     }
-    m_run = M;
-    l_run = Ls;
+    const int c0 = 32 * cb + 8 * part;
+    if (a.n_split == 1) {
+      const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+      if (a.o_dtype == 1) {
+        u32x4 pk;
+        pk[0] = pack_bf16x2(acc0[0] * inv, acc0[1] * inv);
+        pk[1] = pack_bf16x2(acc0[2] * inv, acc0[3] * inv);
+        pk[2] = pack_bf16x2(acc1[0] * inv, acc1[1] * inv);
+        pk[3] = pack_bf16x2(acc1[2] * inv, acc1[3] * inv);
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.o) + orow * DV + c0) = pk;
+      } else {
+        float* op = reinterpret_cast<float*>(a.o) + orow * DV + c0;
+        reinterpret_cast<f32x4*>(op)[0] = acc0 * inv;
+        reinterpret_cast<f32x4*>(op)[1] = acc1 * inv;
+      }
+      if (a.lse && cb == 0 && part == 0)
+        a.lse[orow] = Ls > 0.0f ? (M + __log2f(Ls)) * 0.6931471805599453f : -__builtin_huge_valf();
+    } else {
+      const int64_t nrows = (int64_t)a.n_qsets * R * a.hq;
+      float* op = a.part + ((int64_t)sp * nrows + orow) * DV + c0;
+      reinterpret_cast<f32x4*>(op)[0] = acc0;
+      reinterpret_cast<f32x4*>(op)[1] = acc1;
+      if (cb == 0 && part == 0) {
+        float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 2;
+        ml[0] = M;
+        ml[1] = Ls;
+      }
+    }
+    }
+    return;
   }
 
   if (!active) return;

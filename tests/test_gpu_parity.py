@@ -129,6 +129,36 @@ def test_attention_given_oracle_indices(name, dev):
                         what="%s call %d" % (name, c))
 
 
+ATTN_SHAPES = {
+    # 10 query sets x 8 heads per KV head: 80 rows, two row groups per KV head
+    "sep128_q10": dict(n_qsets=10),
+    # 16 query heads per KV head, 3 sets
+    "sep128_g16": dict(hq=64, hkv=4, n_qsets=3),
+    # one 128-wide row serving as K and V
+    "shared128": dict(kv_mode="shared", hq=32, hkv=2, n_qsets=2),
+    # separate K and V rows of 256 channels
+    "sep256": dict(dqk=256, dv=256, hq=16, hkv=2, n_qsets=2),
+}
+
+
+@pytest.mark.parametrize("shape", list(ATTN_SHAPES))
+def test_attention_shapes(shape, dev):
+    """Gather attention for other head / width / query-set layouts (the kernel
+    picks a different work shape for each) against the oracle, given oracle
+    indices."""
+    wl = synth.HYSPARSE2.replace(n_seqs=3, seq_lens_override=(3000, 777, 1500),
+                                 **ATTN_SHAPES[shape])
+    prob = synth.make_problem(wl, device="cpu")
+    _flush("case %s" % shape)
+    p, step = _step(prob, dev)
+    sc = H.oracle_scores(prob, 0)
+    idx, cnt = H.oracle_select(prob, sc, wl.k)
+    step.run_attention(idx=[torch.from_numpy(idx).to(dev)], count=[torch.from_numpy(cnt).to(dev)])
+    torch.cuda.synchronize()
+    o_ref, l_ref = H.oracle_attention(prob, 0, idx, cnt)
+    H.check_outputs(step.o[0], o_ref, step.lse[0], l_ref, torch.bfloat16, what=shape)
+
+
 def test_dsa_rows_fp8_latent(dev):
     """DSA-shaped prefill rows (FP8 indexer 64x128, top-2048, latent 576 with
     V = first 512, 128 heads) on a 4096-token sequence; rows straddle the
