@@ -69,12 +69,20 @@ def algorithmic_bytes(step, name: str) -> float:
     geo = row_geometry(step)
     R = len(geo)
     ie = _elem(wl.idx_dtype)
+    pool_n = int(step.pool_count.sum()) if step.pool_count is not None else 0
     if name == "index_score":
         n = sum(g[0] for g in geo)
         return n * wl.idx_dim * ie + R * wl.idx_heads * (wl.idx_dim * ie + 4) + n * 4
+    if name == "index_score_reindex":  # pool members: key rows, positions, scores
+        return pool_n * (wl.idx_dim * ie + 4 + 4) + R * wl.idx_heads * (wl.idx_dim * ie + 4)
     if name == "topk_select":
+        if wl.block:  # scores of every visible entry, the pool, then top-k inside the pool
+            n = sum(g[0] for g in geo)
+            return n * 4 + pool_n * 4 + R * (wl.max_blocks * wl.block + wl.k + 2) * 4
         c = sum(g[1] for g in geo)
         return c * 4 + R * (wl.k + 1) * 4
+    if name == "topk_select_reindex":  # pool scores and positions -> top-k
+        return pool_n * 8 + R * (wl.k + 1) * 4
     if name.startswith("attn_gather_fwd"):
         call = 0 if name == "attn_gather_fwd" else int(name.rsplit("_", 1)[1])
         sets = p.q[call].shape[0]

@@ -242,7 +242,9 @@ typedef struct {
  *            v_from_k != 0, in which case V is the first d_v
  *            channels of the K row (MLA latent / shared-row caches,
  *            "Lecture 10", section 5.1: one latent entry serves all heads)
- *   idx      [R][idx_stride] int32 (NULL: window only); count [R]
+ *   idx      [R][idx_stride] int32 (NULL: window only); count [R].
+ *            window + idx_stride must not exceed 131072 entries
+ *            (SA_ERR_UNSUPPORTED otherwise)
  *   o        [n_qsets][R][n_heads_q][d_v], dtype o_dtype (F32 or BF16)
  *   lse      optional [n_qsets][R][n_heads_q] f32
  * Softmax statistics and accumulation are fp32; BF16 / FP4 operands go

@@ -266,6 +266,8 @@ sa_status validate_attn(const sa_attn_desc* d, sa::AttnArgs* out) {
     CHECK(d->count, SA_ERR_NULL, "%s: count is required with idx", op);
     CHECK(d->idx_stride >= 1, SA_ERR_SHAPE, "%s: idx_stride must be >= 1", op);
   }
+  CHECK((int64_t)d->rows.window + (d->idx ? d->idx_stride : 0) <= 131072, SA_ERR_UNSUPPORTED,
+        "%s: window + idx_stride above 131072 entries per row", op);
   if (out) {
     out->rows = to_dev(d->rows);
     out->k = to_dev(d->k);

@@ -539,35 +539,45 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
 }
 
 // Merge split partials: o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i.
+// One wave per output row: lane i < n_split holds split i's (m, l) and its
+// weight; every lane then sums 4 consecutive channels per 256-channel block
+// over the splits with 16-byte loads.
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t nrows = (int64_t)a.n_qsets * a.rows.n_rows * a.hq;
   if (row >= nrows) return;
-  const int DV = a.dv;
-  const float* ml = a.part + (int64_t)a.n_split * nrows * DV;
-  float M = -__builtin_huge_valf();
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, ml[((int64_t)s * nrows + row) * 2]);
-  float Lsum = 0.0f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const float m = ml[((int64_t)s * nrows + row) * 2], l = ml[((int64_t)s * nrows + row) * 2 + 1];
-    if (l > 0.0f) Lsum += exp2f(m - M) * l;
+  const int DV = a.dv, ns = a.n_split;
+  const float* ml = a.part + (int64_t)ns * nrows * DV;
+  float m = -__builtin_huge_valf(), l = 0.0f;
+  if (lane < ns) {
+    m = ml[((int64_t)lane * nrows + row) * 2];
+    l = ml[((int64_t)lane * nrows + row) * 2 + 1];
   }
-  const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
-  for (int c = lane; c < DV; c += 64) {
-    float acc = 0.0f;
-    for (int s = 0; s < a.n_split; ++s) {
-      const float m = ml[((int64_t)s * nrows + row) * 2], l = ml[((int64_t)s * nrows + row) * 2 + 1];
-      if (l > 0.0f) acc += exp2f(m - M) * a.part[((int64_t)s * nrows + row) * DV + c];
+  const float M = wave_max(m);
+  const float f = (l > 0.0f && M != -__builtin_huge_valf()) ? exp2f(m - M) : 0.0f;
+  const float L = wave_sum(f * l);
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  for (int c0 = 4 * lane; c0 < DV; c0 += 256) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int sp = 0; sp < ns; ++sp) {
+      const float fs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), sp));
+      const f32x4 v = *reinterpret_cast<const f32x4*>(a.part + ((int64_t)sp * nrows + row) * DV + c0);
+      acc += fs * v;
     }
     acc *= inv;
-    if (a.o_dtype == 1)
-      reinterpret_cast<uint16_t*>(a.o)[row * DV + c] = (uint16_t)f32_to_bf16_bits(acc);
-    else
-      reinterpret_cast<float*>(a.o)[row * DV + c] = acc;
+    if (a.o_dtype == 1) {
+      uint2 pk;
+      pk.x = pack_bf16x2(acc[0], acc[1]);
+      pk.y = pack_bf16x2(acc[2], acc[3]);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.o) + row * DV + c0) = pk;
+    } else {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + row * DV + c0) = acc;
+    }
   }
   if (a.lse && lane == 0)
-    a.lse[row] = Lsum > 0.0f ? (M + __log2f(Lsum)) * 0.6931471805599453f : -__builtin_huge_valf();
+    a.lse[row] = L > 0.0f ? (M + __log2f(L)) * 0.6931471805599453f : -__builtin_huge_valf();
 }
 
 // F32 path: one wave per (row, KV head, query set, query head); entries in

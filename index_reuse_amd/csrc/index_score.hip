@@ -74,10 +74,13 @@ __device__ __forceinline__ f32x4 mfma_slice(const LaneSlice<DIM, true>& a,
   return acc;
 }
 
-// grid = (ceil(n_slots / (64*kWaves*gpw)), R); every wave scores gpw groups of
-// 64 consecutive slots of row blockIdx.y, 16 entries per MFMA tile.
-template <int NMT, int DIM, bool FP8>
-__global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int gpw) {
+// grid = (ceil(n_slots / (64*kWaves*GPW)), R); wave w scores GPW groups of 64
+// consecutive slots of row blockIdx.y, 16 entries per MFMA tile.  All of a
+// wave's key rows are loaded before the first MFMA: slot -> entry -> cache
+// row addresses first, then every row load (unconditional, with the entry
+// clamped to a visible one), so a wave keeps 4*GPW tiles of loads in flight.
+template <int NMT, int DIM, bool FP8, int GPW>
+__global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a) {
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -85,10 +88,36 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
   const RowInfo ri = row_info(a.rows, r);
   const bool cand_mode = a.cand != nullptr;
   const int n_slots = cand_mode ? a.cand_count[r] : ri.n_avail;
-  const int wg_base = blockIdx.x * (64 * kWaves * gpw);
+  const int wg_base = blockIdx.x * (64 * kWaves * GPW);
   if (wg_base >= n_slots) return;
+  float* out = a.scores + (int64_t)r * a.score_stride;
+  if (ri.n_avail == 0) {  // nothing visible: every listed candidate scores -inf
+    for (int i = threadIdx.x; i < 64 * kWaves * GPW && wg_base + i < n_slots; i += 64 * kWaves)
+      out[wg_base + i] = -__builtin_huge_valf();
+    return;
+  }
+  const int32_t* cand = cand_mode ? a.cand + (int64_t)r * a.cand_stride : nullptr;
+  const int wbase = wg_base + wave * 64 * GPW;
 
+  // entries of this lane's rows (tile t of group gi: slot wbase + 64 gi + 16 t + col)
+  int pos[GPW][4];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int slot = wbase + 64 * gi + 16 * t + col;
+      pos[gi][t] = cand_mode ? cand[min(slot, n_slots - 1)] : slot;
+    }
   constexpr int EB = ElemTraits<FP8>::bytes;
+  LaneSlice<DIM, FP8> ks[GPW][4];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int pc = min(max(pos[gi][t], 0), ri.n_avail - 1);
+      ks[gi][t].load(cache_row(a.k, ri.b, pc), g);
+    }
+
   // Query slices (A operand: head = mt*16 + col) and head weights in the
   // accumulator layout (head = mt*16 + 4*g + i).
   LaneSlice<DIM, FP8> qs[NMT];
@@ -107,30 +136,20 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
     }
   }
 
-  float* out = a.scores + (int64_t)r * a.score_stride;
-  const int32_t* cand = cand_mode ? a.cand + (int64_t)r * a.cand_stride : nullptr;
-
-  for (int gi = 0; gi < gpw; ++gi) {
-    const int base = wg_base + (gi * kWaves + wave) * 64;
-    if (base >= n_slots) break;
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int base = wbase + 64 * gi;
     float res[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int slot = base + t * 16 + col;
-      int pos = slot;
-      bool valid = slot < n_slots;
-      if (cand_mode && valid) pos = cand[slot];
-      valid = valid && pos >= 0 && pos < ri.n_avail;
-      LaneSlice<DIM, FP8> ks;
-      if (valid)
-        ks.load(cache_row(a.k, ri.b, pos), g);
-      else
-        ks.zero();
+      const int slot = base + 16 * t + col;
+      const int p = pos[gi][t];
+      const bool valid = slot < n_slots && p >= 0 && p < ri.n_avail;
       float part = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma_slice<DIM>(qs[mt], ks, acc);
+        acc = mfma_slice<DIM>(qs[mt], ks[gi][t], acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) part = fmaf(wv[mt][i], fmaxf(acc[i], 0.0f), part);
       }
@@ -138,7 +157,7 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
       res[t] = valid ? part : -__builtin_huge_valf();
     }
     // lane l stores the result of slot base + l (tile l/16, column l%16)
-    float mine = g == 0 ? res[0] : g == 1 ? res[1] : g == 2 ? res[2] : res[3];
+    const float mine = g == 0 ? res[0] : g == 1 ? res[1] : g == 2 ? res[2] : res[3];
     if (base + lane < n_slots) out[base + lane] = mine;
   }
 }
@@ -174,14 +193,12 @@ __global__ __launch_bounds__(256) void index_score_f32(IndexArgs a) {
 
 template <int NMT, int DIM, bool FP8>
 hipError_t launch_mfma(const IndexArgs& a, hipStream_t s) {
-  const int per_group = 64 * kWaves;
-  const int groups = (a.n_slots + per_group - 1) / per_group;
-  // Enough workgroups to cover 256 CUs several times over; longer rows give
-  // each wave several 64-entry groups to amortise the query load.
-  int gpw = 1;
-  while (gpw < 8 && (int64_t)((groups + 2 * gpw - 1) / (2 * gpw)) * a.rows.n_rows >= 2048) gpw *= 2;
-  dim3 grid((groups + gpw - 1) / gpw, a.rows.n_rows);
-  hipLaunchKernelGGL((index_score_mfma<NMT, DIM, FP8>), grid, dim3(64 * kWaves), 0, s, a, gpw);
+  // Rows of keys per lane held at once: 4 tiles x GPW groups; wide keys
+  // (dim 128) keep one group per wave so the loads fit the register file.
+  constexpr int GPW = DIM == 64 ? 2 : 1;
+  const int per_wg = 64 * kWaves * GPW;
+  dim3 grid((a.n_slots + per_wg - 1) / per_wg, a.rows.n_rows);
+  hipLaunchKernelGGL((index_score_mfma<NMT, DIM, FP8, GPW>), grid, dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
 

@@ -141,6 +141,12 @@ def test_attn_validation_and_workspace(lib):
     bad = B.sa_attn_desc.from_buffer_copy(d)
     bad.k.dtype = B.SA_FP4_E2M1
     assert _status(lib.sparse_attn_gather_fwd, bad) == -4  # FP4 needs v_from_k
+    bad = B.sa_attn_desc.from_buffer_copy(d)
+    bad.rows.window = 131072 - 1024 + 1  # window + idx_stride beyond the per-row limit
+    assert _status(lib.sparse_attn_gather_fwd, bad) == -4
+    bad = B.sa_attn_desc.from_buffer_copy(d)
+    bad.k.row_stride = bad.v.row_stride = 1 << 31  # strides must stay below 2^31
+    assert _status(lib.sparse_attn_gather_fwd, bad) == -2
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
