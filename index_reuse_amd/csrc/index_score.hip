@@ -30,7 +30,10 @@ struct ElemTraits<true> {  // OCP e4m3
 };
 
 // One lane's slice of a key or query row for the MFMA: lane group g = lane/16
-// holds channels [g*dim/4, (g+1)*dim/4); k-step ks uses its ks-th group of 8.
+// holds the 16-byte pieces [64 i + 16 g, 64 i + 16 g + 16) of the row, so one
+// load instruction reads 64 contiguous bytes of each of its 16 rows; k-step
+// ks uses the lane's ks-th 8 elements.  Keys and queries share the mapping,
+// so every k-step contracts the same channel set on both operands.
 template <int DIM, bool FP8>
 struct LaneSlice {
   static constexpr int KS = DIM / 32;
@@ -39,9 +42,9 @@ struct LaneSlice {
   u32x4 v[VEC];
 
   __device__ __forceinline__ void load(const char* row, int g) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(row + g * BYTES);
+    const u32x4* p = reinterpret_cast<const u32x4*>(row);
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) v[i] = __builtin_nontemporal_load(p + i);
+    for (int i = 0; i < VEC; ++i) v[i] = __builtin_nontemporal_load(p + 4 * i + g);
   }
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -74,13 +77,52 @@ __device__ __forceinline__ f32x4 mfma_slice(const LaneSlice<DIM, true>& a,
   return acc;
 }
 
-// grid = (ceil(n_slots / (64*kWaves*GPW)), R); wave w scores GPW groups of 64
-// consecutive slots of row blockIdx.y, 16 entries per MFMA tile.  All of a
-// wave's key rows are loaded before the first MFMA: slot -> entry -> cache
-// row addresses first, then every row load (unconditional, with the entry
-// clamped to a visible one), so a wave keeps 4*GPW tiles of loads in flight.
-template <int NMT, int DIM, bool FP8, int GPW>
-__global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a) {
+// acc[t][mt] += Q[mt] . K[t] for the four key tiles of a group, k-step
+// outermost so the 4*NMT accumulator chains interleave.
+template <int NMT, int DIM>
+__device__ __forceinline__ void mfma_tiles(const LaneSlice<DIM, false> (&q)[NMT],
+                                           const LaneSlice<DIM, false> (&k)[4], f32x4 (&acc)[4][NMT]) {
+#pragma unroll
+  for (int ks = 0; ks < LaneSlice<DIM, false>::KS; ++ks)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+        acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, q[mt].v[ks]), __builtin_bit_cast(bf16x8, k[t].v[ks]),
+            acc[t][mt], 0, 0, 0);
+}
+template <int NMT, int DIM>
+__device__ __forceinline__ void mfma_tiles(const LaneSlice<DIM, true> (&q)[NMT],
+                                           const LaneSlice<DIM, true> (&k)[4], f32x4 (&acc)[4][NMT]) {
+#pragma unroll
+  for (int ks = 0; ks < LaneSlice<DIM, true>::KS; ++ks)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        const uint32_t* pa = reinterpret_cast<const uint32_t*>(&q[mt].v[0]) + 2 * ks;
+        const uint32_t* pb = reinterpret_cast<const uint32_t*>(&k[t].v[0]) + 2 * ks;
+        const long la = (long)(((uint64_t)pa[1] << 32) | pa[0]);
+        const long lb = (long)(((uint64_t)pb[1] << 32) | pb[0]);
+        acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(la, lb, acc[t][mt], 0, 0, 0);
+      }
+}
+
+// grid = (ceil(n_slots / (64*kWaves*gpw)), R); wave w scores gpw groups of 64
+// consecutive slots of row blockIdx.y (gpw even), 16 entries per MFMA tile.
+// The query slices and head weights are loaded once per wave; key rows
+// stream through a two-deep register pipeline (the next group's rows load
+// while the current group is scored).  Loads are unconditional, with the
+// entry clamped to a visible one.
+template <int DIM, bool FP8>
+struct Group {
+  LaneSlice<DIM, FP8> ks[4];
+  int pos[4];
+};
+
+template <int NMT, int DIM, bool FP8>
+__global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int gpw) {
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -88,38 +130,37 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a) {
   const RowInfo ri = row_info(a.rows, r);
   const bool cand_mode = a.cand != nullptr;
   const int n_slots = cand_mode ? a.cand_count[r] : ri.n_avail;
-  const int wg_base = blockIdx.x * (64 * kWaves * GPW);
+  const int wg_base = blockIdx.x * (64 * kWaves * gpw);
   if (wg_base >= n_slots) return;
   float* out = a.scores + (int64_t)r * a.score_stride;
   if (ri.n_avail == 0) {  // nothing visible: every listed candidate scores -inf
-    for (int i = threadIdx.x; i < 64 * kWaves * GPW && wg_base + i < n_slots; i += 64 * kWaves)
+    for (int i = threadIdx.x; i < 64 * kWaves * gpw && wg_base + i < n_slots; i += 64 * kWaves)
       out[wg_base + i] = -__builtin_huge_valf();
     return;
   }
   const int32_t* cand = cand_mode ? a.cand + (int64_t)r * a.cand_stride : nullptr;
-  const int wbase = wg_base + wave * 64 * GPW;
+  const int wbase = wg_base + wave * 64 * gpw;
+  const int ngrp = min(gpw, (n_slots - wbase + 63) / 64);  // groups of this wave
+  if (ngrp <= 0) return;
 
-  // entries of this lane's rows (tile t of group gi: slot wbase + 64 gi + 16 t + col)
-  int pos[GPW][4];
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi)
+  auto load_group = [&](int gi, Group<DIM, FP8>& G) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int slot = wbase + 64 * gi + 16 * t + col;
-      pos[gi][t] = cand_mode ? cand[min(slot, n_slots - 1)] : slot;
+      G.pos[t] = cand_mode ? cand[min(slot, n_slots - 1)] : slot;
     }
-  constexpr int EB = ElemTraits<FP8>::bytes;
-  LaneSlice<DIM, FP8> ks[GPW][4];
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int pc = min(max(pos[gi][t], 0), ri.n_avail - 1);
-      ks[gi][t].load(cache_row(a.k, ri.b, pc), g);
+      const int pc = min(max(G.pos[t], 0), ri.n_avail - 1);
+      G.ks[t].load(cache_row(a.k, ri.b, pc), g);
     }
+  };
+  Group<DIM, FP8> buf[2];
+  load_group(0, buf[0]);
 
   // Query slices (A operand: head = mt*16 + col) and head weights in the
   // accumulator layout (head = mt*16 + 4*g + i).
+  constexpr int EB = ElemTraits<FP8>::bytes;
   LaneSlice<DIM, FP8> qs[NMT];
   float wv[NMT][4];
 #pragma unroll
@@ -136,30 +177,48 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a) {
     }
   }
 
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
+  // The four tiles' MFMA chains and epilogues are independent: interleave
+  // them (k-step outermost) so the chains overlap.
+  auto score_group = [&](int gi, const Group<DIM, FP8>& G) {
     const int base = wbase + 64 * gi;
+    f32x4 acc[4][NMT];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mfma_tiles<NMT, DIM>(qs, G.ks, acc);
     float res[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      float part[4] = {0.f, 0.f, 0.f, 0.f};  // one chain per accumulator row
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[i] = fmaf(wv[mt][i], fmaxf(acc[t][mt][i], 0.0f), part[i]);
+      res[t] = (part[0] + part[1]) + (part[2] + part[3]);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
       const int slot = base + 16 * t + col;
-      const int p = pos[gi][t];
+      const int p = G.pos[t];
       const bool valid = slot < n_slots && p >= 0 && p < ri.n_avail;
-      float part = 0.0f;
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma_slice<DIM>(qs[mt], ks[gi][t], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part = fmaf(wv[mt][i], fmaxf(acc[i], 0.0f), part);
-      }
-      part = xor16_32_sum(part);
-      res[t] = valid ? part : -__builtin_huge_valf();
+      const float sum = xor16_32_sum(res[t]);  // all lanes take part
+      res[t] = valid ? sum : -__builtin_huge_valf();
     }
     // lane l stores the result of slot base + l (tile l/16, column l%16)
     const float mine = g == 0 ? res[0] : g == 1 ? res[1] : g == 2 ? res[2] : res[3];
     if (base + lane < n_slots) out[base + lane] = mine;
+  };
+
+  // two groups per iteration so the buffer index stays static
+  int gi = 0;
+  for (; gi + 2 <= ngrp; gi += 2) {
+    load_group(gi + 1, buf[1]);
+    score_group(gi, buf[0]);
+    if (gi + 2 < ngrp) load_group(gi + 2, buf[0]);
+    score_group(gi + 1, buf[1]);
   }
+  if (gi < ngrp) score_group(gi, buf[0]);
 }
 
 // F32 path: one thread per (row, slot); the row's query and weights in LDS.
@@ -193,12 +252,14 @@ __global__ __launch_bounds__(256) void index_score_f32(IndexArgs a) {
 
 template <int NMT, int DIM, bool FP8>
 hipError_t launch_mfma(const IndexArgs& a, hipStream_t s) {
-  // Rows of keys per lane held at once: 4 tiles x GPW groups; wide keys
-  // (dim 128) keep one group per wave so the loads fit the register file.
-  constexpr int GPW = DIM == 64 ? 2 : 1;
-  const int per_wg = 64 * kWaves * GPW;
-  dim3 grid((a.n_slots + per_wg - 1) / per_wg, a.rows.n_rows);
-  hipLaunchKernelGGL((index_score_mfma<NMT, DIM, FP8, GPW>), grid, dim3(64 * kWaves), 0, s, a);
+  // Enough workgroups to cover the 256 CUs several times; long rows give each
+  // wave more 64-entry groups, so the query load is amortised over them.
+  const int per_group = 64 * kWaves;
+  const int groups = (a.n_slots + per_group - 1) / per_group;
+  int gpw = 2;
+  while (gpw < 16 && (int64_t)((groups + 2 * gpw - 1) / (2 * gpw)) * a.rows.n_rows >= 1024) gpw *= 2;
+  dim3 grid((groups + gpw - 1) / gpw, a.rows.n_rows);
+  hipLaunchKernelGGL((index_score_mfma<NMT, DIM, FP8>), grid, dim3(64 * kWaves), 0, s, a, gpw);
   return hipGetLastError();
 }
 
