@@ -164,8 +164,10 @@ def calibration_copy(mib: int):
 
 def cpu_baseline(step, n_rows: int, min_seconds: float):
     """The fp64 oracle on the first ``n_rows`` decode rows of the same inputs
-    (whole step: score, select, attention for every query set), repeated
-    until at least ``min_seconds`` of host time have elapsed."""
+    (whole step: score, select, and attention for every query set; with a
+    block pool the Full layer's score + top-k + pool, the Reindex layer's
+    rescoring + top-k, and both attention calls), repeated until at least
+    ``min_seconds`` of host time have elapsed."""
     import numpy as np
 
     import oracle
@@ -179,35 +181,59 @@ def cpu_baseline(step, n_rows: int, min_seconds: float):
     sl = p.seq_len[seqs].cpu().numpy().astype(np.int32)
     cap = wl.n_entries_cap
 
-    def logical(c):
+    def logical(c, which="pool"):
+        t = c.pool if which == "pool" else c.scale
         bt = c.block_table[seqs] if c.block_table is not None else None
-        pool = c.pool if bt is not None else c.pool[seqs]
-        return oracle.unpage(pool, bt, c.page_size or cap, len(seqs), cap)
+        t = t if bt is not None else t[seqs]
+        return oracle.unpage(t, bt, c.page_size or cap, len(seqs), cap)
 
+    fp4 = wl.kv_mode == "fp4"
     kl = logical(p.kidx)
     K = logical(p.k)
+    KS = logical(p.k, "scale") if fp4 else None
     V = logical(p.v) if p.v is not None else None
-    q_idx = p.idx_q[0][rows].cpu()
-    w = p.idx_w[0][rows].cpu()
-    q = p.q[0][:, rows].cpu()
+    q_idx = [x[rows].cpu() for x in p.idx_q]
+    w = [x[rows].cpu() for x in p.idx_w]
+    q = [x[:, rows].cpu() for x in p.q]
     scale = float(np.float32(wl.dqk ** -0.5))
+    geo = (so, po, sl, wl.stride)
+
+    def attend(qq, idx, cnt):
+        if fp4:
+            oracle.attention(*geo, wl.window, qq, K, None, idx, cnt, scale=scale, hkv=wl.hkv,
+                             k_scale=KS, v_from_k=True, dv=wl.dv, fp4=True)
+        else:
+            oracle.attention(*geo, wl.window, qq, K, V, idx, cnt, scale=scale,
+                             v_from_k=V is None, dv=wl.dv)
+
+    def one_step():
+        sc = oracle.index_score(*geo, q_idx[0], w[0], kl)
+        if not wl.block:
+            idx, cnt = oracle.topk_select(*geo, wl.window, sc, wl.k)
+            attend(q[0], idx, cnt)
+            return
+        idx, cnt, pool, pc = oracle.topk_select(*geo, wl.window, sc, wl.k, block=wl.block,
+                                                max_blocks=wl.max_blocks)
+        rs = oracle.index_score(*geo, q_idx[1], w[1], kl, cand=pool, cand_count=pc)
+        ridx, rcnt = oracle.topk_select(*geo, wl.window, rs, wl.k, cand=pool, cand_count=pc)
+        attend(q[0], idx, cnt)
+        attend(q[1], ridx, rcnt)
+
     reps = 0
     t0 = time.perf_counter()
     while True:
-        sc = oracle.index_score(so, po, sl, wl.stride, q_idx, w, kl)
-        idx, cnt = oracle.topk_select(so, po, sl, wl.stride, wl.window, sc, wl.k)
-        oracle.attention(so, po, sl, wl.stride, wl.window, q, K, V, idx, cnt,
-                         scale=scale, v_from_k=V is None, dv=wl.dv)
+        one_step()
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
-    queries = reps * n_rows * q.shape[0]
+    queries = reps * n_rows * sum(x.shape[0] for x in q)
     return {"value": round(queries / dt, 3), "unit": "queries/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": "%d pass(es) over %d of %d decode rows of one replica (whole step: score "
                       "%d entries/row, select, attention for %d query sets), %.1f s" % (
-                          reps, n_rows, p.n_rows, int(sl.max()) // wl.stride, q.shape[0], dt)}
+                          reps, n_rows, p.n_rows, int(sl.max()) // wl.stride,
+                          sum(x.shape[0] for x in q), dt)}
 
 
 def main():
