@@ -221,6 +221,137 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
   if (gi < ngrp) score_group(gi, buf[0]);
 }
 
+// ----------------------------------------------------------------- prefill
+// Many query rows of one sequence (prefill) make the score a GEMM: M = (query
+// row, head), N = cache entries, K = dim.  A workgroup holds kPRowsW rows per
+// wave (their FP8 query rows as the A operand of v_mfma_scale 16x16x128,
+// heads on M, the whole 128-wide contraction in one instruction) and streams
+// 64-entry chunks of the sequence's keys through LDS, shared by every row of
+// the workgroup.  Blocks run heaviest (latest rows) first; a block whose rows
+// span several sequences makes one pass per sequence.
+constexpr int kPWaves = 8;
+constexpr int kPRowsW = 2;                  // rows per wave
+constexpr int kPRows = kPWaves * kPRowsW;   // rows per workgroup
+constexpr int kPChunk = 64;                 // entries per LDS chunk
+constexpr int kPRowB = 128 + 16;            // LDS bytes per entry (padded)
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+template <int NMT>
+__global__ __launch_bounds__(64 * kPWaves) void index_score_prefill(IndexArgs a, int n_blocks) {
+  __shared__ __align__(16) char kb[2][kPChunk * kPRowB];
+  __shared__ int sb[kPRows], sn[kPRows];
+  __shared__ int wred[kPWaves][2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int r0 = (n_blocks - 1 - (int)blockIdx.x) * kPRows;
+  if (tid < kPRows) {
+    const int r = r0 + tid;
+    int b = -1, n = 0;
+    if (r < a.rows.n_rows) {
+      const RowInfo ri = row_info(a.rows, r);
+      b = ri.b;
+      n = ri.n_avail;
+    }
+    sb[tid] = b;
+    sn[tid] = b >= 0 ? n : 0;
+  }
+  __syncthreads();
+
+  // this wave's rows: A operands (head mt*16 + col, bytes [32g, 32g+32)) and
+  // head weights in the accumulator layout (head mt*16 + 4g + i)
+  i32x8 qa[kPRowsW][NMT];
+  float wv[kPRowsW][NMT][4];
+  int rb[kPRowsW], rn[kPRowsW];
+#pragma unroll
+  for (int j = 0; j < kPRowsW; ++j) {
+    const int lr = wave * kPRowsW + j, r = r0 + lr;
+    rb[j] = sb[lr];
+    rn[j] = sn[lr];
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int h = mt * 16 + col;
+      if (rb[j] >= 0 && h < a.n_heads) {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const char*>(a.q) + ((int64_t)r * a.n_heads + h) * 128 + 32 * g);
+        const u32x4 x0 = qp[0], x1 = qp[1];
+        qa[j][mt] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                          (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      } else {
+        qa[j][mt] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hw = mt * 16 + 4 * g + i;
+        wv[j][mt][i] = (rb[j] >= 0 && hw < a.n_heads) ? a.w[(int64_t)r * a.n_heads + hw] : 0.0f;
+      }
+    }
+  }
+
+  // one pass per distinct sequence of the block, in increasing order
+  int bprev = -1;
+  while (true) {
+    int bs = 0x7FFFFFFF, nmax = 0;
+    for (int i = 0; i < kPRows; ++i)
+      if (sb[i] > bprev) bs = min(bs, sb[i]);
+    if (bs == 0x7FFFFFFF) break;
+    for (int i = 0; i < kPRows; ++i)
+      if (sb[i] == bs) nmax = max(nmax, sn[i]);
+    bprev = bs;
+    if (nmax == 0) continue;
+
+    // chunk loads: thread t takes entry t/8 of the chunk, 16 bytes at 16 (t%8)
+    const int le = tid >> 3, lp = tid & 7;
+    auto load_chunk = [&](int c0) -> u32x4 {
+      const int e = min(c0 + le, nmax - 1);
+      return *reinterpret_cast<const u32x4*>(cache_row(a.k, bs, e) + 16 * lp);
+    };
+    static_assert(kPChunk * 8 == 64 * kPWaves, "one 16-byte piece per thread per chunk");
+    u32x4 pre = load_chunk(0);
+    int buf = 0;
+    for (int c0 = 0; c0 < nmax; c0 += kPChunk) {
+      *reinterpret_cast<u32x4*>(&kb[buf][le * kPRowB + 16 * lp]) = pre;
+      __syncthreads();
+      if (c0 + kPChunk < nmax) pre = load_chunk(c0 + kPChunk);
+      float res[kPRowsW][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const char* kr = &kb[buf][(16 * t + col) * kPRowB + 32 * g];
+        const u32x4 y0 = *reinterpret_cast<const u32x4*>(kr);
+        const u32x4 y1 = *reinterpret_cast<const u32x4*>(kr + 16);
+        const i32x8 kbv = {(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3],
+                           (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
+#pragma unroll
+        for (int j = 0; j < kPRowsW; ++j) {
+          float part[4] = {0.f, 0.f, 0.f, 0.f};
+          if (rb[j] == bs && c0 < rn[j]) {
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) {
+              f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+              acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[j][mt], kbv, acc, 0, 0, 0,
+                                                                     0x7F7F7F7F, 0, 0x7F7F7F7F);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) part[i] = fmaf(wv[j][mt][i], fmaxf(acc[i], 0.0f), part[i]);
+            }
+          }
+          res[j][t] = xor16_32_sum((part[0] + part[1]) + (part[2] + part[3]));
+        }
+      }
+      // lane l stores entry c0 + l (tile l/16, column l%16) of each row
+#pragma unroll
+      for (int j = 0; j < kPRowsW; ++j) {
+        const int e = c0 + lane;
+        if (rb[j] == bs && e < rn[j]) {
+          const float mine = g == 0 ? res[j][0] : g == 1 ? res[j][1] : g == 2 ? res[j][2] : res[j][3];
+          a.scores[(int64_t)(r0 + wave * kPRowsW + j) * a.score_stride + e] = mine;
+        }
+      }
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+}
+
 // F32 path: one thread per (row, slot); the row's query and weights in LDS.
 __global__ __launch_bounds__(256) void index_score_f32(IndexArgs a) {
   extern __shared__ float smem[];
@@ -283,6 +414,20 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   const bool fp8 = a.dtype == 2;
+  // Many rows of FP8 128-wide keys (prefill): the GEMM-shaped kernel.
+  if (fp8 && a.dim == 128 && a.cand == nullptr && a.rows.n_rows >= kPRows && a.n_heads <= 64) {
+    const int n_blocks = (a.rows.n_rows + kPRows - 1) / kPRows;
+    const int nmt = (a.n_heads + 15) / 16;
+    if (nmt == 4)
+      hipLaunchKernelGGL(index_score_prefill<4>, dim3(n_blocks), dim3(64 * kPWaves), 0, s, a, n_blocks);
+    else if (nmt == 2)
+      hipLaunchKernelGGL(index_score_prefill<2>, dim3(n_blocks), dim3(64 * kPWaves), 0, s, a, n_blocks);
+    else if (nmt == 3)
+      hipLaunchKernelGGL(index_score_prefill<3>, dim3(n_blocks), dim3(64 * kPWaves), 0, s, a, n_blocks);
+    else
+      hipLaunchKernelGGL(index_score_prefill<1>, dim3(n_blocks), dim3(64 * kPWaves), 0, s, a, n_blocks);
+    return hipGetLastError();
+  }
   if (a.dim == 64) return fp8 ? dispatch_heads<64, true>(a, s) : dispatch_heads<64, false>(a, s);
   return fp8 ? dispatch_heads<128, true>(a, s) : dispatch_heads<128, false>(a, s);
 }

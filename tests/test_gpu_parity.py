@@ -187,6 +187,51 @@ def test_dsa_rows_fp8_latent(dev):
         H.check_outputs(step.o[0], o_ref, step.lse[0], l_ref, torch.bfloat16, what="dsa")
 
 
+def test_prefill_indexer_blocks(dev):
+    """The prefill (row-block GEMM) indexer: blocks of consecutive rows of one
+    sequence, blocks mixing two sequences, and padding rows, with the FP8
+    64x128 indexer; exact on integer inputs, within the fp32 bound on
+    N(0,1) inputs."""
+    import dataclasses
+
+    from index_reuse_amd import Cache, Rows, index_score
+
+    wl = synth.DSA.replace(n_seqs=2, seq_lens_override=(3000, 1500))
+    pos0 = list(range(0, 40)) + list(range(2030, 2070)) + [2999]
+    rows = [(0, t) for t in pos0] + [(1, t) for t in range(1480, 1500)]
+    rows += [(0, 5), (1, 7), (0, 2500), (1, 1499), (-1, -1), (0, 1024)] * 3
+    for integer in (True, False):
+        base = synth.make_problem(wl, device="cpu", integer=integer, rows=[0])
+        R = len(rows)
+        so = torch.tensor([b for b, _ in rows], dtype=torch.int32)
+        po = torch.tensor([t for _, t in rows], dtype=torch.int32)
+        draw = synth.small_ints if integer else synth.normal
+        q = draw((R, wl.idx_heads, wl.idx_dim), seed=4242, dtype=wl.idx_dtype)
+        if integer:
+            w = synth.small_ints((R, wl.idx_heads), seed=4243, lo=0)
+        else:
+            w = synth.uniform01((R, wl.idx_heads), seed=4243)
+        prob = dataclasses.replace(base, seq_of_row=so, pos_of_row=po, idx_q=[q], idx_w=[w])
+        _flush("case prefill indexer integer=%s R=%d" % (integer, R))
+        p = H.move(prob, dev)
+        S = wl.n_entries_cap
+        scores = torch.full((R, S), float("nan"), dtype=torch.float32, device=dev)
+        rr = Rows(p.seq_of_row, p.pos_of_row, p.seq_len, wl.stride, wl.window)
+        kc = Cache(p.kidx.pool, p.kidx.block_table, 1, wl.idx_dim)
+        index_score(rr, p.idx_q[0], p.idx_w[0], kc, scores=scores)
+        torch.cuda.synchronize()
+        sc = H.oracle_scores(prob, 0)
+        g = scores.cpu().double().numpy()
+        valid = ~np.isnan(sc)
+        assert not np.isnan(g[valid]).any()
+        if integer:
+            assert np.array_equal(g[valid], sc[valid])
+        else:
+            tau = H.fp32_score_bound(prob, 0)
+            err = np.abs(g - np.nan_to_num(sc))
+            assert np.all(err[valid] <= np.broadcast_to(tau[:, None], sc.shape)[valid])
+
+
 def test_select_exact_on_given_scores(dev):
     """Selection alone on generated scores with heavy ties and signed zeros
     (token, candidate and pool modes) is bit-exact."""
