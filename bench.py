@@ -236,6 +236,147 @@ def cpu_baseline(step, n_rows: int, min_seconds: float):
                           sum(x.shape[0] for x in q), dt)}
 
 
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}  # MI355X dense
+
+
+def prefill_work(wl, prob):
+    """Algorithmic work of one pass over every row of a prefill workload:
+    indexer flops (causal pairs x heads x dim x 2), attention flops (gathered
+    pairs x heads x (d_qk + d_v) x 2), and selection bytes."""
+    import numpy as np
+
+    pos = prob.pos_of_row.cpu().numpy().astype(np.int64)
+    n = np.minimum(pos + 1, int(prob.seq_len.max())) // wl.stride
+    pairs = int(n.sum())
+    cand = np.maximum(n - wl.window, 0)
+    sel = np.minimum(cand, wl.k)
+    attn_pairs = int((np.minimum(n, wl.window) + sel).sum())
+    return {
+        "index_score": 2.0 * pairs * wl.idx_heads * wl.idx_dim,
+        "attn_gather_fwd": 2.0 * attn_pairs * wl.hq * (wl.dqk + wl.dv),
+        "topk_select": 4.0 * int(cand.sum()) + 4.0 * len(pos) * (wl.k + 1),
+        "pairs": pairs, "attn_pairs": attn_pairs,
+    }
+
+
+def prefill_cpu_baseline(prob, n_rows: int, min_seconds: float):
+    """The fp64 oracle (score, select, attention) on n_rows rows spread evenly
+    over the sequence, repeated until min_seconds have elapsed."""
+    import numpy as np
+
+    import oracle
+
+    wl = prob.wl
+    R = prob.n_rows
+    rows = [int((i + 0.5) * R / n_rows) for i in range(n_rows)]
+    so = prob.seq_of_row[rows].cpu().numpy().astype(np.int32)
+    po = prob.pos_of_row[rows].cpu().numpy().astype(np.int32)
+    sl = prob.seq_len.cpu().numpy().astype(np.int32)
+    cap = wl.n_entries_cap
+
+    def logical(c):
+        return oracle.unpage(c.pool, c.block_table, c.page_size or cap, wl.n_seqs, cap)
+
+    kl = logical(prob.kidx)
+    K = logical(prob.k)
+    q_idx, w = prob.idx_q[0][rows].cpu(), prob.idx_w[0][rows].cpu()
+    q = prob.q[0][:, rows].cpu()
+    scale = float(np.float32(wl.dqk ** -0.5))
+    geo = (so, po, sl, wl.stride)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        sc = oracle.index_score(*geo, q_idx, w, kl)
+        idx, cnt = oracle.topk_select(*geo, wl.window, sc, wl.k)
+        oracle.attention(*geo, wl.window, q, K, None, idx, cnt, scale=scale, v_from_k=True,
+                         dv=wl.dv)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": round(reps * n_rows / dt, 3), "unit": "rows/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d pass(es) over %d rows spread evenly over the %d-row prefill (score, "
+                      "select, attention), %.1f s" % (reps, n_rows, R, dt)}
+
+
+def run_prefill(args, wl):
+    """Prefill: one step = the hot path over every query row, in row blocks."""
+    import torch
+
+    import synth
+    from index_reuse_amd.pipeline import PrefillStep
+
+    dev = torch.device("cuda:0")
+    prob = synth.make_problem(wl, device=dev)
+    step = PrefillStep(prob, row_block=args.row_block)
+    calls = step.prepare()
+    names = [n for n, _ in calls]
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        for _, c in calls:
+            c()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e = evs[i]
+        for j, (_, c) in enumerate(calls):
+            e[j].record()
+            c()
+        e[-1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fam_ms = {}
+    for j, n in enumerate(names):
+        fam_ms[n] = fam_ms.get(n, 0.0) + sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K
+    gpu_ms = sum(evs[i][0].elapsed_time(evs[i][-1]) for i in range(K)) / K
+    work = prefill_work(wl, prob)
+    kernels = {}
+    for n, ms in fam_ms.items():
+        if n == "topk_select":
+            kernels[n] = {"ms": round(ms, 4), "alg_bytes": int(work[n]),
+                          "GB/s": round(work[n] / (ms * 1e-3) / 1e9, 1)}
+        else:
+            kernels[n] = {"ms": round(ms, 4), "alg_tflop": round(work[n] / 1e12, 3),
+                          "TFLOP/s": round(work[n] / (ms * 1e-3) / 1e12, 1)}
+    dom = max(("index_score", "attn_gather_fwd"), key=lambda n: fam_ms[n])
+    dt = "fp8" if wl.idx_dtype == torch.float8_e4m3fn and dom == "index_score" else "bf16"
+    achieved = work[dom] / (fam_ms[dom] * 1e-3) / 1e12
+    R = prob.n_rows
+    out = {
+        "metric": METRIC,
+        "value": round(R * K / elapsed, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / K, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 indexer, bf16 attention",
+        "data": "synthetic",
+        "config": {"workload": "%s_prefill" % wl.name, "rows": R, "context": wl.seq_len,
+                   "topk": wl.k, "indexer": "%dx%d %s" % (wl.idx_heads, wl.idx_dim,
+                                                          str(wl.idx_dtype).replace("torch.", "")),
+                   "q_heads": wl.hq, "latent": wl.dqk, "v_width": wl.dv,
+                   "row_block": args.row_block, "causal_pairs": work["pairs"],
+                   "attention_pairs": work["attn_pairs"]},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_PEAK_TFLOPS[dt], 4), "traffic": None,
+                     "alg_tflop": round(work[dom] / 1e12, 3)},
+        "gpu_ms_per_step": round(gpu_ms, 3),
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = prefill_cpu_baseline(prob, args.cpu_rows or 16, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +389,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum host time of the oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--row-block", type=int, default=8192,
+                    help="prefill: query rows per block (the score buffer holds one block)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run a plain copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -271,7 +414,7 @@ def main():
         calibration_copy(args.copy_mib)
     wl = synth.WORKLOADS[args.workload]
     if wl.prefill:
-        raise SystemExit("prefill workloads are benchmarked by their own script")
+        return run_prefill(args, wl)
     steps = []
     for i in range(args.replicas):
         prob = synth.make_problem(wl, device=dev, seed_base=1000 * (wl.cfg_id + 1) + 100 * i)

@@ -291,7 +291,7 @@ class Prepared:
     so that each launch costs one ctypes call.  Every tensor the descriptor
     points to must stay alive as long as this object."""
 
-    def __init__(self, fn_name: str, desc, op: int, device, keep=()):
+    def __init__(self, fn_name: str, desc, op: int, device, keep=(), workspace=None):
         L = load()
         self.fn = getattr(L, fn_name)
         self.desc = desc
@@ -299,8 +299,12 @@ class Prepared:
         need = int(L.sa_workspace_size(op, self.ref))
         if need == ctypes.c_size_t(-1).value:
             _check(-2)
-        # zero-filled: the selection requires it on first use
-        self.ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=device) if need else None
+        if need and workspace is not None and workspace.numel() >= need:
+            # shared with calls of the same entry point that never overlap in time
+            self.ws = workspace
+        else:
+            # zero-filled: the selection requires it on first use
+            self.ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=device) if need else None
         self.ws_ptr = _ptr(self.ws)
         self.need = need
         self.keep = keep
@@ -316,11 +320,12 @@ def prepare_index_score(rows: Rows, q, w, k: Cache, scores, cand=None, cand_coun
 
 
 def prepare_topk_select(rows: Rows, scores, k, idx, count, cand=None, cand_count=None, block=0,
-                        max_blocks=0, pool=None, pool_count=None):
+                        max_blocks=0, pool=None, pool_count=None, workspace=None):
     d = topk_desc(rows, scores, k, idx, count, cand, cand_count, block, max_blocks, pool,
                   pool_count)
     return Prepared("sparse_topk_select", d, SA_OP_TOPK_SELECT, scores.device,
-                    keep=(rows, scores, idx, count, cand, cand_count, pool, pool_count))
+                    keep=(rows, scores, idx, count, cand, cand_count, pool, pool_count),
+                    workspace=workspace)
 
 
 def prepare_attn_gather_fwd(rows: Rows, q, k: Cache, v: Optional[Cache], idx, count, o, lse=None,

@@ -139,3 +139,64 @@ class Step:
     def outputs(self) -> StepOutputs:
         return StepOutputs(self.scores, self.idx, self.count, self.pool, self.pool_count, self.o,
                            self.lse)
+
+
+class PrefillStep:
+    """One pass of the hot path over every query row of a prefill workload,
+    in blocks of ``row_block`` rows so that the block's score matrix
+    ([row_block, n] f32) is the only materialised scores: per block, the
+    indexer scores the causal history of each row, the selection keeps the
+    top-k, and attention gathers it.  Indices, outputs and LSE cover all
+    rows; the score buffer is reused from block to block."""
+
+    def __init__(self, prob, row_block: int = 8192):
+        wl = prob.wl
+        assert wl.prefill and not wl.block, "prefill workloads without a block pool"
+        self.prob = prob
+        self.wl = wl
+        dev = prob.seq_of_row.device
+        R = prob.n_rows
+        self.R = R
+        self.row_block = row_block
+        self.kidx = _cache(prob.kidx, 1, wl.idx_dim)
+        self.k = _cache(prob.k, wl.hkv, wl.dqk)
+        self.v = _cache(prob.v, wl.hkv, wl.dv) if prob.v is not None else None
+        self.S = wl.n_entries_cap
+        self.scores = torch.empty(min(row_block, R), self.S, dtype=torch.float32, device=dev)
+        self.idx = torch.empty(R, wl.k, dtype=torch.int32, device=dev)
+        self.count = torch.empty(R, dtype=torch.int32, device=dev)
+        q = prob.q[0]
+        self.o = torch.empty(q.shape[0], R, wl.hq, wl.dv, dtype=q.dtype, device=dev)
+        self.lse = torch.empty(q.shape[0], R, wl.hq, dtype=torch.float32, device=dev)
+        self.scale = wl.dqk ** -0.5
+        self._prepared = None
+
+    def blocks(self):
+        return [(lo, min(self.R, lo + self.row_block)) for lo in range(0, self.R, self.row_block)]
+
+    def prepare(self):
+        """Launch-only call list of one pass: (name, callable) for every block
+        and entry point, names repeated per block."""
+        if self._prepared is not None:
+            return self._prepared
+        p, wl = self.prob, self.wl
+        calls = []
+        ws = None  # one selection workspace for every block (the calls never overlap)
+        for lo, hi in self.blocks():
+            rows = Rows(p.seq_of_row[lo:hi], p.pos_of_row[lo:hi], p.seq_len, wl.stride, wl.window)
+            sc = self.scores[: hi - lo]
+            calls.append(("index_score", prepare_index_score(rows, p.idx_q[0][lo:hi],
+                                                             p.idx_w[0][lo:hi], self.kidx, sc)))
+            sel = prepare_topk_select(rows, sc, wl.k, self.idx[lo:hi], self.count[lo:hi],
+                                      workspace=ws)
+            ws = sel.ws if ws is None else ws
+            calls.append(("topk_select", sel))
+            calls.append(("attn_gather_fwd", prepare_attn_gather_fwd(
+                rows, p.q[0][:, lo:hi], self.k, self.v, self.idx[lo:hi], self.count[lo:hi],
+                self.o[:, lo:hi], self.lse[:, lo:hi], self.scale, wl.dv)))
+        self._prepared = calls
+        return calls
+
+    def run(self):
+        for _, c in self.prepare():
+            c()
