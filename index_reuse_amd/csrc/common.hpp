@@ -121,6 +121,14 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t nib) {
   return (nib & 8u) ? -mag : mag;
 }
 
+// max(x, 0) for a finite float in one v_max_i32: a negative float (and -0)
+// is a negative int32, so the integer max with 0 gives +0, and a positive
+// float keeps its bits.  (fmaxf also canonicalises its operand: two
+// instructions.)
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // ---------------------------------------------------------------------------
 // Orderable score keys: a larger float maps to a larger uint32; -0 maps to
 // the key of +0 so the two tie.

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part[i] = fmaf(wv[mt][i], fmaxf(acc[t][mt][i], 0.0f), part[i]);
+        for (int i = 0; i < 4; ++i) part[i] = fmaf(wv[mt][i], relu(acc[t][mt][i]), part[i]);
       res[t] = (part[0] + part[1]) + (part[2] + part[3]);
     }
 #pragma unroll
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
 // the workgroup.  Blocks run heaviest (latest rows) first; a block whose rows
 // span several sequences makes one pass per sequence.
 constexpr int kPWaves = 8;
-constexpr int kPRowsW = 2;                  // rows per wave
+constexpr int kPRowsW = 1;                  // rows per wave
 constexpr int kPRows = kPWaves * kPRowsW;   // rows per workgroup
 constexpr int kPChunk = 64;                 // entries per LDS chunk
 constexpr int kPRowB = 128 + 16;            // LDS bytes per entry (padded)
@@ -300,43 +300,69 @@ __global__ __launch_bounds__(64 * kPWaves) void index_score_prefill(IndexArgs a,
     bprev = bs;
     if (nmax == 0) continue;
 
-    // chunk loads: thread t takes entry t/8 of the chunk, 16 bytes at 16 (t%8)
-    const int le = tid >> 3, lp = tid & 7;
-    auto load_chunk = [&](int c0) -> u32x4 {
-      const int e = min(c0 + le, nmax - 1);
-      return *reinterpret_cast<const u32x4*>(cache_row(a.k, bs, e) + 16 * lp);
+    // chunk loads: piece p = tid + i*blockDim is entry p/8 of the chunk,
+    // 16 bytes at 16 (p%8)
+    constexpr int PPT = kPChunk * 8 / (64 * kPWaves);
+    static_assert(PPT * 64 * kPWaves == kPChunk * 8, "whole 16-byte pieces per thread");
+    u32x4 pre[PPT];
+    auto load_chunk = [&](int c0) {
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) {
+        const int pc = tid + i * 64 * kPWaves;
+        const int e = min(c0 + (pc >> 3), nmax - 1);
+        pre[i] = *reinterpret_cast<const u32x4*>(cache_row(a.k, bs, e) + 16 * (pc & 7));
+      }
     };
-    static_assert(kPChunk * 8 == 64 * kPWaves, "one 16-byte piece per thread per chunk");
-    u32x4 pre = load_chunk(0);
+    load_chunk(0);
     int buf = 0;
     for (int c0 = 0; c0 < nmax; c0 += kPChunk) {
-      *reinterpret_cast<u32x4*>(&kb[buf][le * kPRowB + 16 * lp]) = pre;
-      __syncthreads();
-      if (c0 + kPChunk < nmax) pre = load_chunk(c0 + kPChunk);
-      float res[kPRowsW][4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int i = 0; i < PPT; ++i) {
+        const int pc = tid + i * 64 * kPWaves;
+        *reinterpret_cast<u32x4*>(&kb[buf][(pc >> 3) * kPRowB + 16 * (pc & 7)]) = pre[i];
+      }
+      __syncthreads();
+      if (c0 + kPChunk < nmax) load_chunk(c0 + kPChunk);
+      // Tile t's MFMAs are issued before tile t-1's epilogue, so the matrix
+      // pipe works while the VALU applies ReLU and the head weights.
+      float res[kPRowsW][4];
+      bool act[kPRowsW];
+#pragma unroll
+      for (int j = 0; j < kPRowsW; ++j) act[j] = rb[j] == bs && c0 < rn[j];
+      f32x4 acc[2][kPRowsW][NMT];
+      auto issue = [&](int t, f32x4 (&A)[kPRowsW][NMT]) {
         const char* kr = &kb[buf][(16 * t + col) * kPRowB + 32 * g];
         const u32x4 y0 = *reinterpret_cast<const u32x4*>(kr);
         const u32x4 y1 = *reinterpret_cast<const u32x4*>(kr + 16);
         const i32x8 kbv = {(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3],
                            (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
 #pragma unroll
+        for (int j = 0; j < kPRowsW; ++j)
+#pragma unroll
+          for (int mt = 0; mt < NMT; ++mt)
+            A[j][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                qa[j][mt], kbv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+      };
+      auto epilogue = [&](int t, const f32x4 (&A)[kPRowsW][NMT]) {
+#pragma unroll
         for (int j = 0; j < kPRowsW; ++j) {
           float part[4] = {0.f, 0.f, 0.f, 0.f};
-          if (rb[j] == bs && c0 < rn[j]) {
 #pragma unroll
-            for (int mt = 0; mt < NMT; ++mt) {
-              f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-              acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[j][mt], kbv, acc, 0, 0, 0,
-                                                                     0x7F7F7F7F, 0, 0x7F7F7F7F);
+          for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) part[i] = fmaf(wv[j][mt][i], fmaxf(acc[i], 0.0f), part[i]);
-            }
-          }
-          res[j][t] = xor16_32_sum((part[0] + part[1]) + (part[2] + part[3]));
+            for (int i = 0; i < 4; ++i) part[i] = fmaf(wv[j][mt][i], relu(A[j][mt][i]), part[i]);
+          const float sum = xor16_32_sum((part[0] + part[1]) + (part[2] + part[3]));
+          res[j][t] = act[j] ? sum : 0.0f;
         }
-      }
+      };
+      issue(0, acc[0]);
+      issue(1, acc[1]);
+      epilogue(0, acc[0]);
+      issue(2, acc[0]);
+      epilogue(1, acc[1]);
+      issue(3, acc[1]);
+      epilogue(2, acc[0]);
+      epilogue(3, acc[1]);
       // lane l stores entry c0 + l (tile l/16, column l%16) of each row
 #pragma unroll
       for (int j = 0; j < kPRowsW; ++j) {
@@ -375,7 +401,7 @@ __global__ __launch_bounds__(256) void index_score_f32(IndexArgs a) {
     for (int h = 0; h < a.n_heads; ++h) {
       float d = 0.0f;
       for (int c = 0; c < a.dim; ++c) d = fmaf(smem[h * a.dim + c], kr[c], d);
-      s = fmaf(smem[HD + h], fmaxf(d, 0.0f), s);
+      s = fmaf(smem[HD + h], relu(d), s);
     }
   }
   a.scores[(int64_t)r * a.score_stride + slot] = s;
