@@ -219,8 +219,9 @@ __global__ __launch_bounds__(256) void block_max_kernel(SelectArgs a, Ws ws) {
 
 // Element q of thread t in a chunk: wave-contiguous 512-element segments,
 // lane-interleaved inside (coalesced, and in-wave order is (q, lane)).
+template <int CHUNK>
 __device__ __forceinline__ int chunk_elem(int q) {
-  return (threadIdx.x >> 6) * (kChunk / kCW) + q * 64 + (threadIdx.x & 63);
+  return (threadIdx.x >> 6) * (CHUNK / kCW) + q * 64 + (threadIdx.x & 63);
 }
 
 // The bin holding the rank-th (1-based) element counting from the top bin of
@@ -289,7 +290,7 @@ __device__ __forceinline__ int block_sum(int v, int* wred) {
 // -------------------------------------------------------------- 1. hist
 // Level-1 histogram (key bits 31..20) of one chunk, merged into the row's;
 // chunk 0 also resets the row's record for the scan step.
-template <int KIND>
+template <int KIND, int CHUNK>
 __global__ __launch_bounds__(kChunkT) void hist_kernel(SelectArgs a, Ws ws) {
   __shared__ uint32_t h[kL1];
   __shared__ uint32_t nvalid;
@@ -302,17 +303,17 @@ __global__ __launch_bounds__(kChunkT) void hist_kernel(SelectArgs a, Ws ws) {
   }
   const RowInfo ri = row_info(a.rows, r);
   const Src<KIND> s = make_src<KIND>(a, ws, r, ri);
-  const int j0 = blockIdx.x * kChunk;
+  const int j0 = blockIdx.x * CHUNK;
   if (j0 >= s.n) return;
   for (int i = threadIdx.x; i < kL1; i += kChunkT) h[i] = 0u;
   if (threadIdx.x == 0) nvalid = 0u;
   __syncthreads();
   int valid = 0;
-  uint32_t keys[kQ];
+  uint32_t keys[CHUNK / kChunkT];
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) keys[q] = s.key_c(j0 + chunk_elem(q));
+  for (int q = 0; q < CHUNK / kChunkT; ++q) keys[q] = s.key_c(j0 + chunk_elem<CHUNK>(q));
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) {
+  for (int q = 0; q < CHUNK / kChunkT; ++q) {
     const uint32_t key = keys[q];
     if (key) {
       atomicAdd(&h[key >> (32 - kL1Bits)], 1u);
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(kChunkT) void hist_kernel(SelectArgs a, Ws ws) {
 }
 
 // -------------------------------------------------------------- 2. scan
-template <int KIND>
+template <int KIND, int CHUNK>
 __global__ __launch_bounds__(kChunkT) void scan_kernel(SelectArgs a, Ws ws, int kk) {
   __shared__ __align__(16) uint32_t h[kL1];
   __shared__ int wred[kCW];
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(kChunkT) void scan_kernel(SelectArgs a, Ws ws, int 
   const RowInfo ri = row_info(a.rows, r);
   const Src<KIND> s = make_src<KIND>(a, ws, r, ri);
   const int n = s.n;
-  const int j0 = c * kChunk;
+  const int j0 = c * CHUNK;
   if (j0 >= n && c > 0) return;
   uint32_t* rec = ws.rec + (int64_t)r * kRecWords;
 #pragma unroll
@@ -371,13 +372,13 @@ __global__ __launch_bounds__(kChunkT) void scan_kernel(SelectArgs a, Ws ws, int 
     rec[REC_MODE] = (uint32_t)mode;
   }
   if (j0 >= n) return;
-  uint32_t keys[kQ];
+  uint32_t keys[CHUNK / kChunkT];
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) keys[q] = s.key_c(j0 + chunk_elem(q));
+  for (int q = 0; q < CHUNK / kChunkT; ++q) keys[q] = s.key_c(j0 + chunk_elem<CHUNK>(q));
   int n_gt = 0, n_hit = 0;
   uint32_t hits = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) {
+  for (int q = 0; q < CHUNK / kChunkT; ++q) {
     const uint32_t key = keys[q];
     const uint32_t d = key >> (32 - kL1Bits);
     const bool gt = mode == 1 ? key != 0u : (mode == 2 && d > b1);
@@ -409,11 +410,11 @@ __global__ __launch_bounds__(kChunkT) void scan_kernel(SelectArgs a, Ws ws, int 
   uint32_t* mk = ws.mkey + (int64_t)r * kCapM;
   int32_t* mj = ws.midx + (int64_t)r * kCapM;
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) {
+  for (int q = 0; q < CHUNK / kChunkT; ++q) {
     if ((hits >> q) & 1u) {
       if (slot < (uint32_t)kCapM) {
         mk[slot] = keys[q];
-        mj[slot] = j0 + chunk_elem(q);
+        mj[slot] = j0 + chunk_elem<CHUNK>(q);
       }
       ++slot;
     }
@@ -441,7 +442,7 @@ struct __align__(16) EmitShared {
   uint32_t u[4];
 };
 
-template <int KIND>
+template <int KIND, int CHUNK>
 __global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int pool_mode) {
   __shared__ EmitShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -450,7 +451,7 @@ __global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int 
   const RowInfo ri = row_info(a.rows, r);
   const Src<KIND> s = make_src<KIND>(a, ws, r, ri);
   const int n = s.n;
-  const int j0 = c * kChunk;
+  const int j0 = c * CHUNK;
   if (j0 >= n && c > 0) return;
   const uint32_t* rec = ws.rec + (int64_t)r * kRecWords;
   const int mode = (int)rec[REC_MODE];
@@ -595,12 +596,12 @@ __global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int 
 
   // emission: kept = key > theta, or a theta-tie whose rank among the row's
   // ties (index order) is below t_eq
-  uint32_t keys[kQ];
+  uint32_t keys[CHUNK / kChunkT];
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) keys[q] = s.key_c(j0 + chunk_elem(q));
+  for (int q = 0; q < CHUNK / kChunkT; ++q) keys[q] = s.key_c(j0 + chunk_elem<CHUNK>(q));
   int w_gt = 0, w_eq = 0;
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) {
+  for (int q = 0; q < CHUNK / kChunkT; ++q) {
     w_gt += __popcll(__ballot(keys[q] != 0u && keys[q] > theta));
     w_eq += __popcll(__ballot(mode == 2 && keys[q] != 0u && keys[q] == theta));
   }
@@ -616,7 +617,7 @@ __global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int 
     eseen += eq;
   }
 #pragma unroll
-  for (int q = 0; q < kQ; ++q) {
+  for (int q = 0; q < CHUNK / kChunkT; ++q) {
     const uint32_t k = keys[q];
     const bool gt = k != 0u && k > theta;
     const bool eq = mode == 2 && k != 0u && k == theta;
@@ -624,7 +625,7 @@ __global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int 
     const bool keep = gt || (eq && eseen + (int)__popcll(me & below) < t_eq);
     const uint64_t mk = __ballot(keep);
     if (keep) {
-      const int j = j0 + chunk_elem(q);
+      const int j = j0 + chunk_elem<CHUNK>(q);
       const int rank = o + (int)__popcll(mk & below);
       if (pool_mode) {
         const int lo = j * bs, mm = min(bs, ri.n_avail - lo);
@@ -638,15 +639,28 @@ __global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int 
   }
 }
 
+// Chunks of 2048 elements; when rows x chunks already gives many workgroups
+// (prefill row blocks), chunks of 8192, so the per-chunk fixed work (row
+// histogram, member list) is spread over 4x more elements.
+template <int KIND, int CHUNK>
+void run_select_chunk(const SelectArgs& a, const Ws& ws, int64_t max_n, int kk, int pool_mode,
+                      hipStream_t st) {
+  const int R = a.rows.n_rows;
+  int64_t nchunks = (max_n + CHUNK - 1) / CHUNK;
+  dim3 gc((unsigned)(nchunks > 0 ? nchunks : 1), R);
+  hipLaunchKernelGGL((hist_kernel<KIND, CHUNK>), gc, dim3(kChunkT), 0, st, a, ws);
+  hipLaunchKernelGGL((scan_kernel<KIND, CHUNK>), gc, dim3(kChunkT), 0, st, a, ws, kk);
+  hipLaunchKernelGGL((emit_kernel<KIND, CHUNK>), gc, dim3(kChunkT), 0, st, a, ws, pool_mode);
+}
+
 template <int KIND>
 void run_select(const SelectArgs& a, const Ws& ws, int64_t max_n, int kk, int pool_mode,
                 hipStream_t st) {
-  const int R = a.rows.n_rows;
-  dim3 gc((unsigned)((max_n + kChunk - 1) / kChunk), R);
-  if (gc.x == 0) gc.x = 1;  // chunk 0 writes counts and padding
-  hipLaunchKernelGGL(hist_kernel<KIND>, gc, dim3(kChunkT), 0, st, a, ws);
-  hipLaunchKernelGGL(scan_kernel<KIND>, gc, dim3(kChunkT), 0, st, a, ws, kk);
-  hipLaunchKernelGGL(emit_kernel<KIND>, gc, dim3(kChunkT), 0, st, a, ws, pool_mode);
+  const int64_t wgs = (int64_t)a.rows.n_rows * ((max_n + kChunk - 1) / kChunk);
+  if (wgs >= 16384)
+    run_select_chunk<KIND, 4 * kChunk>(a, ws, max_n, kk, pool_mode, st);
+  else
+    run_select_chunk<KIND, kChunk>(a, ws, max_n, kk, pool_mode, st);
 }
 
 int64_t chunk_stride(const SelectArgs& a) {

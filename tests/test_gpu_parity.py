@@ -323,6 +323,30 @@ def test_select_crowded_threshold_bin(dev):
         assert np.array_equal(gp.cpu().numpy(), op), (window, k, mb)
 
 
+def test_select_many_rows(dev):
+    """Selection over many long rows (the prefill regime, where each
+    workgroup takes a larger chunk): 2048 rows of up to 16384 candidates with
+    integer ties and signed zeros, bit-exact against the oracle."""
+    from index_reuse_amd import Rows, topk_select
+
+    import oracle
+
+    R, S = 2048, 16384
+    scores = synth.small_ints((R, S), seed=99, lo=-20, hi=20)
+    scores[scores == 0] = -0.0
+    scores[7] = 2.0  # a row of ties
+    so = torch.zeros(R, dtype=torch.int32)
+    po = torch.tensor([S - 1 - 5 * r for r in range(R)], dtype=torch.int32)
+    sl = torch.tensor([S], dtype=torch.int32)
+    for window, k in ((0, 1000), (64, 3000)):
+        rows = Rows(so.to(dev), po.to(dev), sl.to(dev), 1, window)
+        gi, gc = topk_select(rows, scores.to(dev), k)
+        oi, oc = oracle.topk_select(so, po, sl, 1, window, scores.double().numpy(), k)
+        torch.cuda.synchronize()
+        assert np.array_equal(gc.cpu().numpy(), oc)
+        assert np.array_equal(gi.cpu().numpy(), oi), (window, k)
+
+
 def test_deterministic_and_reuse(dev):
     """Two runs are bitwise identical; one fused call over all query sets
     equals one call per set (index reuse changes nothing numerically)."""
