@@ -351,6 +351,12 @@ __global__ __launch_bounds__(kChunkT) void scan_kernel(SelectArgs a, Ws ws, int 
   const int n = s.n;
   const int j0 = c * CHUNK;
   if (j0 >= n && c > 0) return;
+  // this chunk's keys: issued now, used after the threshold bin is known
+  uint32_t keys[CHUNK / kChunkT];
+  if (j0 < n) {
+#pragma unroll
+    for (int q = 0; q < CHUNK / kChunkT; ++q) keys[q] = s.key_c(j0 + chunk_elem<CHUNK>(q));
+  }
   uint32_t* rec = ws.rec + (int64_t)r * kRecWords;
 #pragma unroll
   for (int v = 0; v < HV; ++v) reinterpret_cast<u32x4*>(h)[v * kChunkT + tid] = hv[v];
@@ -372,9 +378,6 @@ __global__ __launch_bounds__(kChunkT) void scan_kernel(SelectArgs a, Ws ws, int 
     rec[REC_MODE] = (uint32_t)mode;
   }
   if (j0 >= n) return;
-  uint32_t keys[CHUNK / kChunkT];
-#pragma unroll
-  for (int q = 0; q < CHUNK / kChunkT; ++q) keys[q] = s.key_c(j0 + chunk_elem<CHUNK>(q));
   int n_gt = 0, n_hit = 0;
   uint32_t hits = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
@@ -453,6 +456,12 @@ __global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int 
   const int n = s.n;
   const int j0 = c * CHUNK;
   if (j0 >= n && c > 0) return;
+  // this chunk's keys: issued first, used at emission
+  uint32_t keys[CHUNK / kChunkT];
+  if (j0 < n) {
+#pragma unroll
+    for (int q = 0; q < CHUNK / kChunkT; ++q) keys[q] = s.key_c(j0 + chunk_elem<CHUNK>(q));
+  }
   const uint32_t* rec = ws.rec + (int64_t)r * kRecWords;
   const int mode = (int)rec[REC_MODE];
   const int take = (int)rec[REC_TAKE];
@@ -596,9 +605,6 @@ __global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int 
 
   // emission: kept = key > theta, or a theta-tie whose rank among the row's
   // ties (index order) is below t_eq
-  uint32_t keys[CHUNK / kChunkT];
-#pragma unroll
-  for (int q = 0; q < CHUNK / kChunkT; ++q) keys[q] = s.key_c(j0 + chunk_elem<CHUNK>(q));
   int w_gt = 0, w_eq = 0;
 #pragma unroll
   for (int q = 0; q < CHUNK / kChunkT; ++q) {
