@@ -98,7 +98,7 @@ struct AttnLds {
     Tiles t;
     float comb[NG * W * 64 * CSTRIDE];
   } u;
-  float ml[NG][W][16][2];
+  float ml[NG][W][16][3];  // m, rounded and unrounded probability sums
   int32_t wfirst[W * NG];  // per wave: first entry of the range with a slot
   int32_t slot[SLOTS];     // cache slot of every entry (-1: none)
 };
@@ -280,10 +280,18 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
     }
   };
 
+  // Softmax state per query row (lane col).  The reference m_run is fixed
+  // by the first tile with a finite logit and never moves inside the loop,
+  // so O is only ever touched by MFMAs there and stays in accumulation
+  // registers.  Probabilities 2^(x - m_run) may exceed 1: they are bf16, so
+  // up to 2^kHeadroom they keep full relative precision and O, l stay far
+  // from fp32 overflow.  m_top tracks the largest tile max; if it ever
+  // exceeds m_run by more than kHeadroom, the range is run a second time with
+  // m_run fixed to m_top (every probability then <= 1).
+  constexpr float kHeadroom = 64.0f;
   f32x4 O[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_huge_valf(), l_run = 0.0f;
+  float m_run = -__builtin_huge_valf(), m_top = -__builtin_huge_valf();
+  float l_run = 0.0f, l_lse = 0.0f;  // rounded / unrounded probability sums
 
   // One tile (LDS buffer `buf`, entry tile t) for this wave's query rows.
   auto compute = [&](int buf, int t) {
@@ -316,31 +324,14 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
         tmax = fmaxf(tmax, x);
       }
     tmax = xor16_32_max(tmax);
-    // Lazy rescale: the reference max m_run only moves when some row's tile
-    // max exceeds it by more than 2^8 (in the exp2 domain), so most tiles
-    // leave O untouched; probabilities stay below 2^8 (exact bf16 range).
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run + 8.0f)) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = m_new == -__builtin_huge_valf() ? 1.0f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) O[tt][i] *= alpha;
-      m_run = m_new;
-    }
+    if (m_run == -__builtin_huge_valf()) m_run = tmax;  // O is still all zero
+    m_top = fmaxf(m_top, tmax);
     const float m_use = m_run == -__builtin_huge_valf() ? 0.0f : m_run;
-    float psum = 0.0f;
     float p[2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[mt][i] = fast_exp2(s[mt][i] - m_use);
-        psum += p[mt][i];
-      }
-    psum = xor16_32_sum(psum);
-    l_run += psum;
+      for (int i = 0; i < 4; ++i) p[mt][i] = fast_exp2(s[mt][i] - m_use);
 
     // P^T as the B operand: k-slot 8*gq + i <-> entry (i<4 ? 4gq+i : 16+4gq+i-4)
     u32x4 pa;
@@ -348,6 +339,17 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
     pa[1] = pack_bf16x2(p[0][2], p[0][3]);
     pa[2] = pack_bf16x2(p[1][0], p[1][1]);
     pa[3] = pack_bf16x2(p[1][2], p[1][3]);
+    // The output's normaliser sums the same rounded probabilities that weight
+    // V, so the output is an exact convex combination of the gathered rows;
+    // the log-sum-exp sums the unrounded ones.
+    float psum = 0.0f, xsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      psum += __uint_as_float(pa[i] << 16) + __uint_as_float(pa[i] & 0xFFFF0000u);
+      xsum += (p[i >> 1][2 * (i & 1)] + p[i >> 1][2 * (i & 1) + 1]);
+    }
+    l_run += xor16_32_sum(psum);
+    l_lse += xor16_32_sum(xsum);
     const bf16x8 pab = __builtin_bit_cast(bf16x8, pa);
     const uint16_t* vbase = KV == KV_SEPARATE ? lds.u.t.v[buf] : kb;
     constexpr int VR = KV == KV_SEPARATE ? L::VROW : L::KROW;
@@ -380,27 +382,37 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
   // of each unrolled step is static); the last partial group is guarded.
   static_assert(D == 1 || D % 2 == 0, "prefetch depth must be 1 or even");
   T ring[D];
+  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-  for (int u = 0; u < D; ++u) load_step(u, ring[u]);
-  int s0 = 0;
-  for (; s0 + D <= nsteps_run; s0 += D) {
+    for (int t = 0; t < NT; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < D; ++u) load_step(u, ring[u]);
+    int s0 = 0;
+    for (; s0 + D <= nsteps_run; s0 += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        const int sb = D % 2 == 0 ? (u & 1) : ((s0 + u) & 1);
+        store_step(ring[u], sb);
+        __syncthreads();
+        load_step(s0 + u + D, ring[u]);
+        if (active) compute(sb * NG + grp, (s0 + u) * NG + grp);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      const int sb = D % 2 == 0 ? (u & 1) : ((s0 + u) & 1);
-      store_step(ring[u], sb);
-      __syncthreads();
-      load_step(s0 + u + D, ring[u]);
-      if (active) compute(sb * NG + grp, (s0 + u) * NG + grp);
+      if (s0 + u < nsteps_run) {
+        const int sb = (s0 + u) & 1;
+        store_step(ring[u], sb);
+        __syncthreads();
+        if (active) compute(sb * NG + grp, (s0 + u) * NG + grp);
+      }
     }
-  }
-#pragma unroll
-  for (int u = 0; u < D; ++u) {
-    if (s0 + u < nsteps_run) {
-      const int sb = (s0 + u) & 1;
-      store_step(ring[u], sb);
-      __syncthreads();
-      if (active) compute(sb * NG + grp, (s0 + u) * NG + grp);
-    }
+    // Every wave of the workgroup takes the same decision (the loop holds
+    // barriers); after a second pass m_top == m_run.
+    if (!__syncthreads_or(m_top > m_run + kHeadroom)) break;
+    m_run = m_top;
+    l_run = 0.0f;
+    l_lse = 0.0f;
   }
 
   // Merge the entry groups: every wave publishes (m, l, O^T) in LDS, lane
@@ -414,6 +426,7 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
     if (gq == 0) {
       lds.ml[grp][wq][col][0] = m_run;
       lds.ml[grp][wq][col][1] = l_run;
+      lds.ml[grp][wq][col][2] = l_lse;
     }
     {
       f32x4* dst = reinterpret_cast<f32x4*>(&lds.u.comb[((grp * W + wq) * 64 + lane) * L::CSTRIDE]);
@@ -431,12 +444,13 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
     float M = -__builtin_huge_valf();
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, lds.ml[gg][wq][row][0]);
-    float Ls = 0.0f, f[NG];
+    float Ls = 0.0f, Lx = 0.0f, f[NG];
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
       const float m = lds.ml[gg][wq][row][0];
       f[gg] = m == -__builtin_huge_valf() ? 0.0f : fast_exp2(m - M);
       Ls += f[gg] * lds.ml[gg][wq][row][1];
+      Lx += f[gg] * lds.ml[gg][wq][row][2];
     }
     const int R = a.rows.n_rows;
     const int set = qr / G, h = g * G + qr % G;
@@ -467,16 +481,17 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
         reinterpret_cast<f32x4*>(op)[1] = acc1 * inv;
       }
       if (a.lse && cb == 0 && part == 0)
-        a.lse[orow] = Ls > 0.0f ? (M + __log2f(Ls)) * 0.6931471805599453f : -__builtin_huge_valf();
+        a.lse[orow] = Lx > 0.0f ? (M + __log2f(Lx)) * 0.6931471805599453f : -__builtin_huge_valf();
     } else {
       const int64_t nrows = (int64_t)a.n_qsets * R * a.hq;
       float* op = a.part + ((int64_t)sp * nrows + orow) * DV + c0;
       reinterpret_cast<f32x4*>(op)[0] = acc0;
       reinterpret_cast<f32x4*>(op)[1] = acc1;
       if (cb == 0 && part == 0) {
-        float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 2;
+        float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 3;
         ml[0] = M;
         ml[1] = Ls;
+        ml[2] = Lx;
       }
     }
     }
@@ -515,7 +530,7 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
         }
       }
     if (a.lse && gq == 0)
-      a.lse[orow] = l_run > 0.0f ? (m_run + __log2f(l_run)) * 0.6931471805599453f
+      a.lse[orow] = l_lse > 0.0f ? (m_run + __log2f(l_lse)) * 0.6931471805599453f
                                  : -__builtin_huge_valf();
   } else {
     const int64_t nrows = (int64_t)a.n_qsets * R * a.hq;
@@ -531,17 +546,19 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
         reinterpret_cast<f32x4*>(op)[1] = v1;
       }
     if (gq == 0) {
-      float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 2;
+      float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 3;
       ml[0] = m_run;
       ml[1] = l_run;
+      ml[2] = l_lse;
     }
   }
 }
 
-// Merge split partials: o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i.
-// One wave per output row: lane i < n_split holds split i's (m, l) and its
-// weight; every lane then sums 4 consecutive channels per 256-channel block
-// over the splits with 16-byte loads.
+// Merge split partials: o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i,
+// lse from the unrounded sums lx_i the same way.  One wave per output row:
+// lane i < n_split holds split i's (m, l, lx) and its weight; every lane then
+// sums 4 consecutive channels per 256-channel block over the splits with
+// 16-byte loads.
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -549,14 +566,15 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   if (row >= nrows) return;
   const int DV = a.dv, ns = a.n_split;
   const float* ml = a.part + (int64_t)ns * nrows * DV;
-  float m = -__builtin_huge_valf(), l = 0.0f;
+  float m = -__builtin_huge_valf(), l = 0.0f, lx = 0.0f;
   if (lane < ns) {
-    m = ml[((int64_t)lane * nrows + row) * 2];
-    l = ml[((int64_t)lane * nrows + row) * 2 + 1];
+    m = ml[((int64_t)lane * nrows + row) * 3];
+    l = ml[((int64_t)lane * nrows + row) * 3 + 1];
+    lx = ml[((int64_t)lane * nrows + row) * 3 + 2];
   }
   const float M = wave_max(m);
   const float f = (l > 0.0f && M != -__builtin_huge_valf()) ? exp2f(m - M) : 0.0f;
-  const float L = wave_sum(f * l);
+  const float L = wave_sum(f * l), Lx = wave_sum(f * lx);
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   for (int c0 = 4 * lane; c0 < DV; c0 += 256) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -577,7 +595,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
     }
   }
   if (a.lse && lane == 0)
-    a.lse[row] = L > 0.0f ? (M + __log2f(L)) * 0.6931471805599453f : -__builtin_huge_valf();
+    a.lse[row] = Lx > 0.0f ? (M + __log2f(Lx)) * 0.6931471805599453f : -__builtin_huge_valf();
 }
 
 // F32 path: one wave per (row, KV head, query set, query head); entries in
@@ -726,7 +744,7 @@ void attn_plan(AttnArgs& a) {
 size_t attn_workspace_bytes(const AttnArgs& a) {
   if (a.n_split <= 1) return 0;
   const int64_t nrows = (int64_t)a.n_qsets * a.rows.n_rows * a.hq;
-  return (size_t)a.n_split * nrows * (a.dv + 2) * sizeof(float);
+  return (size_t)a.n_split * nrows * (a.dv + 3) * sizeof(float);
 }
 
 hipError_t launch_attn_gather(const AttnArgs& a, hipStream_t s) {

@@ -159,6 +159,33 @@ def test_attention_shapes(shape, dev):
     H.check_outputs(step.o[0], o_ref, step.lse[0], l_ref, torch.bfloat16, what=shape)
 
 
+@pytest.mark.parametrize("shape,gain", [("sep128", 8.0), ("sep128", 40.0), ("dsa576", 40.0)])
+def test_attention_peaked_logits(shape, gain, dev):
+    """Queries scaled by `gain` spread the logits of a row over a wide range,
+    so the row's largest logit often lies in a tile far after the first one
+    (beyond 2^64 in the exp2 domain at gain 40, which makes the kernel re-run
+    the range with the true maximum as reference)."""
+    if shape == "sep128":
+        wl = synth.HYSPARSE2.replace(n_seqs=3, seq_lens_override=(3000, 777, 1500))
+        prob = synth.make_problem(wl, device="cpu")
+    else:
+        wl = synth.DSA.replace(seq_len=4096)
+        prob = synth.make_problem(wl, device="cpu", rows=DSA_ROWS)
+    prob.q[0] = (prob.q[0].float() * gain).to(prob.q[0].dtype)
+    _flush("case %s gain %g" % (shape, gain))
+    p, step = _step(prob, dev)
+    # fp32 outputs: a peaked row's output is close to one V row, whose
+    # magnitude can reach 4, where bf16 output rounding alone is 1.6e-2
+    step.o[0] = torch.empty(step.o[0].shape, dtype=torch.float32, device=dev)
+    sc = H.oracle_scores(prob, 0)
+    idx, cnt = H.oracle_select(prob, sc, wl.k)
+    step.run_attention(idx=[torch.from_numpy(idx).to(dev)], count=[torch.from_numpy(cnt).to(dev)])
+    torch.cuda.synchronize()
+    o_ref, l_ref = H.oracle_attention(prob, 0, idx, cnt)
+    H.check_outputs(step.o[0], o_ref, step.lse[0], l_ref, torch.bfloat16,
+                    what="%s gain %g" % (shape, gain))
+
+
 def test_dsa_rows_fp8_latent(dev):
     """DSA-shaped prefill rows (FP8 indexer 64x128, top-2048, latent 576 with
     V = first 512, 128 heads) on a 4096-token sequence; rows straddle the
