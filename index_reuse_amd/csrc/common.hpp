@@ -170,6 +170,19 @@ __device__ __forceinline__ float xor16_32_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Transposed reduction of four per-lane values: afterwards lane group g
+// (lanes 16g .. 16g+15) holds r_g summed over lanes {l, l^16, l^32, l^48}.
+// The 32-lane swap pairs (r0, r2) and (r1, r3); the 16-lane swap then pairs
+// the two half sums: three swaps and three adds for four reductions.
+__device__ __forceinline__ float sum4_transposed(float r0, float r1, float r2, float r3) {
+  const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(r0), __float_as_uint(r2), false, false);
+  const auto x13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(r1), __float_as_uint(r3), false, false);
+  const float h0 = __uint_as_float(x02[0]) + __uint_as_float(x02[1]);  // lanes < 32: r0, else r2
+  const float h1 = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);  // lanes < 32: r1, else r3
+  const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(h0), __float_as_uint(h1), false, false);
+  return __uint_as_float(y[0]) + __uint_as_float(y[1]);
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 }  // namespace sa

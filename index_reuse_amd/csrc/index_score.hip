@@ -197,17 +197,14 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
         for (int i = 0; i < 4; ++i) part[i] = fmaf(wv[mt][i], relu(acc[t][mt][i]), part[i]);
       res[t] = (part[0] + part[1]) + (part[2] + part[3]);
     }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int slot = base + 16 * t + col;
-      const int p = G.pos[t];
-      const bool valid = slot < n_slots && p >= 0 && p < ri.n_avail;
-      const float sum = xor16_32_sum(res[t]);  // all lanes take part
-      res[t] = valid ? sum : -__builtin_huge_valf();
-    }
     // lane l stores the result of slot base + l (tile l/16, column l%16)
-    const float mine = g == 0 ? res[0] : g == 1 ? res[1] : g == 2 ? res[2] : res[3];
-    if (base + lane < n_slots) out[base + lane] = mine;
+    const float sum = sum4_transposed(res[0], res[1], res[2], res[3]);  // all lanes take part
+    // validity of tile t's column as bit t (a lane-dependent pick from G.pos
+    // would put the whole group in scratch memory)
+    unsigned vb = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) vb |= (unsigned)(G.pos[t] >= 0 && G.pos[t] < ri.n_avail) << t;
+    if (base + lane < n_slots) out[base + lane] = (vb >> g) & 1u ? sum : -__builtin_huge_valf();
   };
 
   // two groups per iteration so the buffer index stays static
@@ -233,6 +230,7 @@ constexpr int kPWaves = 8;
 constexpr int kPRowsW = 1;                  // rows per wave
 constexpr int kPRows = kPWaves * kPRowsW;   // rows per workgroup
 constexpr int kPChunk = 64;                 // entries per LDS chunk
+constexpr int kPTiles = kPChunk / 16;       // 16-entry MFMA tiles per chunk
 constexpr int kPRowB = 128 + 16;            // LDS bytes per entry (padded)
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
@@ -323,12 +321,9 @@ __global__ __launch_bounds__(64 * kPWaves) void index_score_prefill(IndexArgs a,
       }
       __syncthreads();
       if (c0 + kPChunk < nmax) load_chunk(c0 + kPChunk);
-      // Tile t's MFMAs are issued before tile t-1's epilogue, so the matrix
+      // Tile t+1's MFMAs are issued before tile t's epilogue, so the matrix
       // pipe works while the VALU applies ReLU and the head weights.
-      float res[kPRowsW][4];
-      bool act[kPRowsW];
-#pragma unroll
-      for (int j = 0; j < kPRowsW; ++j) act[j] = rb[j] == bs && c0 < rn[j];
+      float res[kPRowsW][4];  // lane partial of each of the last 4 tiles
       f32x4 acc[2][kPRowsW][NMT];
       auto issue = [&](int t, f32x4 (&A)[kPRowsW][NMT]) {
         const char* kr = &kb[buf][(16 * t + col) * kPRowB + 32 * g];
@@ -351,26 +346,29 @@ __global__ __launch_bounds__(64 * kPWaves) void index_score_prefill(IndexArgs a,
           for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) part[i] = fmaf(wv[j][mt][i], relu(A[j][mt][i]), part[i]);
-          const float sum = xor16_32_sum((part[0] + part[1]) + (part[2] + part[3]));
-          res[j][t] = act[j] ? sum : 0.0f;
+          res[j][t & 3] = (part[0] + part[1]) + (part[2] + part[3]);
+        }
+        // After every 4 tiles, one transposed reduction over the four lane
+        // groups leaves lane l with entry l of those 64 (tile l/16, column
+        // l%16).
+        if ((t & 3) == 3) {
+#pragma unroll
+          for (int j = 0; j < kPRowsW; ++j) {
+            const float mine = sum4_transposed(res[j][0], res[j][1], res[j][2], res[j][3]);
+            const int e = c0 + 16 * (t - 3) + lane;
+            if (rb[j] == bs && e < rn[j])
+              a.scores[(int64_t)(r0 + wave * kPRowsW + j) * a.score_stride + e] = mine;
+          }
         }
       };
+      static_assert(kPTiles % 4 == 0, "whole 64-entry store groups per chunk");
       issue(0, acc[0]);
-      issue(1, acc[1]);
-      epilogue(0, acc[0]);
-      issue(2, acc[0]);
-      epilogue(1, acc[1]);
-      issue(3, acc[1]);
-      epilogue(2, acc[0]);
-      epilogue(3, acc[1]);
-      // lane l stores entry c0 + l (tile l/16, column l%16) of each row
 #pragma unroll
-      for (int j = 0; j < kPRowsW; ++j) {
-        const int e = c0 + lane;
-        if (rb[j] == bs && e < rn[j]) {
-          const float mine = g == 0 ? res[j][0] : g == 1 ? res[j][1] : g == 2 ? res[j][2] : res[j][3];
-          a.scores[(int64_t)(r0 + wave * kPRowsW + j) * a.score_stride + e] = mine;
-        }
+      for (int t = 0; t < kPTiles; t += 2) {
+        issue(t + 1, acc[1]);
+        epilogue(t, acc[0]);
+        if (t + 2 < kPTiles) issue(t + 2, acc[0]);
+        epilogue(t + 1, acc[1]);
       }
       __syncthreads();
       buf ^= 1;
