@@ -341,12 +341,14 @@ __global__ __launch_bounds__(64 * kPWaves) void index_score_prefill(IndexArgs a,
       auto epilogue = [&](int t, const f32x4 (&A)[kPRowsW][NMT]) {
 #pragma unroll
         for (int j = 0; j < kPRowsW; ++j) {
-          float part[4] = {0.f, 0.f, 0.f, 0.f};
+          // one fma chain: the tiles in flight and the waves sharing the
+          // SIMD cover its latency, and no adds are needed to join chains
+          float part = 0.f;
 #pragma unroll
           for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) part[i] = fmaf(wv[j][mt][i], relu(A[j][mt][i]), part[i]);
-          res[j][t & 3] = (part[0] + part[1]) + (part[2] + part[3]);
+            for (int i = 0; i < 4; ++i) part = fmaf(wv[j][mt][i], relu(A[j][mt][i]), part);
+          res[j][t & 3] = part;
         }
         // After every 4 tiles, one transposed reduction over the four lane
         // groups leaves lane l with entry l of those 64 (tile l/16, column
@@ -370,7 +372,9 @@ __global__ __launch_bounds__(64 * kPWaves) void index_score_prefill(IndexArgs a,
         if (t + 2 < kPTiles) issue(t + 2, acc[0]);
         epilogue(t + 1, acc[1]);
       }
-      __syncthreads();
+      // No barrier here: the next chunk is stored into the other buffer,
+      // whose last readers (the previous chunk) all passed this chunk's
+      // barrier.
       buf ^= 1;
     }
   }
