@@ -645,6 +645,279 @@ __global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int 
   }
 }
 
+// ------------------------------------------------------- one row per workgroup
+// For rows of at most kRowT * EPT elements the whole selection runs in one
+// workgroup of 1024 threads: the row's keys stay in registers (EPT per
+// thread), so the three steps above become one kernel with no global round
+// trips between them.
+//   - threshold: the histogram range adapts to the keys it still has to
+//     split: 4096 bins over [lo, hi] (first the row's min and max valid key,
+//     then the threshold bin), so even tightly clustered scores spread over
+//     many bins (few LDS atomic collisions) and every pass narrows the range
+//     4096-fold: at most three passes reach a single key theta;
+//   - emission: wave w owns elements [w * 64 EPT, (w + 1) * 64 EPT), element
+//     q of a lane at w * 64 EPT + 64 q + lane (coalesced loads, in-wave order
+//     (q, lane)), so ranks come from ballots and one prefix over the waves.
+constexpr int kRowT = 1024;           // threads per row workgroup
+constexpr int kRowW = kRowT / 64;     // waves per row workgroup
+constexpr int kRowBins = 4096;        // histogram bins per pass
+constexpr int kRowBpt = kRowBins / kRowT;
+
+constexpr int kRowFew = 64;           // threshold-bin members resolved by one wave
+
+struct __align__(16) RowShared {
+  uint32_t h[kRowBins];
+  int wi[kRowW][2];
+  uint32_t wu[kRowW][2];
+  int wscan[kRowW];
+  uint32_t u[4];
+  uint32_t mkeys[kRowFew];
+  uint32_t mcount;
+};
+
+// The bin holding the rank-th (1-based) element counting from the top bin;
+// returns (bin, elements in higher bins, elements in the bin).  Thread t owns
+// the kRowBpt bins just below those of thread t - 1, starting from the top,
+// and zeroes them once every thread has read its own (ready for the next
+// pass).
+__device__ __forceinline__ void row_locate(RowShared& sh, int rank, uint32_t& bin, int& above_bin,
+                                           int& in_bin) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lo = kRowBins - kRowBpt * (tid + 1);
+  const u32x4 c = *reinterpret_cast<const u32x4*>(&sh.h[lo]);
+  static_assert(kRowBpt == 4, "four bins per thread");
+  const int mine = (int)(c[0] + c[1] + c[2] + c[3]);
+  const int incl = wave_incl_scan(mine);
+  if (lane == 63) sh.wscan[wave] = incl;
+  __syncthreads();
+  *reinterpret_cast<u32x4*>(&sh.h[lo]) = u32x4{0u, 0u, 0u, 0u};
+  int above = incl - mine;
+#pragma unroll
+  for (int w = 0; w < kRowW - 1; ++w) above += w < wave ? sh.wscan[w] : 0;
+  if (above < rank && rank <= above + mine) {
+    int acc = above, b = lo, at = above, cb = 0;
+    bool found = false;
+#pragma unroll
+    for (int q = kRowBpt - 1; q >= 0; --q) {  // from this thread's top bin down
+      const int cq = (int)c[q];
+      if (!found && acc + cq >= rank) {
+        b = lo + q;
+        at = acc;
+        cb = cq;
+        found = true;
+      }
+      acc += cq;
+    }
+    sh.u[0] = (uint32_t)b;
+    sh.u[1] = (uint32_t)at;
+    sh.u[2] = (uint32_t)cb;
+  }
+  __syncthreads();
+  bin = sh.u[0];
+  above_bin = (int)sh.u[1];
+  in_bin = (int)sh.u[2];
+}
+
+template <int KIND, int EPT>
+__global__ __launch_bounds__(kRowT) void row_select_kernel(SelectArgs a, Ws ws, int kk) {
+  constexpr bool pool_mode = KIND == SRC_BLOCK;  // blocks expand into the pool
+  __shared__ RowShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = lanes_below();
+  const int r = blockIdx.x;
+  const RowInfo ri = row_info(a.rows, r);
+  const Src<KIND> s = make_src<KIND>(a, ws, r, ri);
+  const int n = s.n;
+  const int jw = wave * (64 * EPT) + lane;  // element of q = 0
+  uint32_t keys[EPT];
+  if (n > 0) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) keys[q] = s.key_c(jw + 64 * q);
+  } else {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) keys[q] = 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < kRowBpt; ++i) sh.h[tid + i * kRowT] = 0u;
+  if (tid == 0) sh.mcount = 0u;
+
+  // Valid count, max valid key, and a lower bound on theta: with J =
+  // ceil(take / kRowT) <= 2, each thread's J-th largest key (0 if it has
+  // fewer) is below J * kRowT >= take keys of the row, so the smallest of
+  // them cannot exceed the take-th largest.  Keys under it are never kept
+  // and stay out of the histograms.
+  const int J = (min(kk, kRowT * EPT) + kRowT - 1) / kRowT;  // uniform; the bound is used for J <= 2
+  int nv = 0;
+  uint32_t kmax = 0u, k2 = 0u;  // this thread's largest and second largest valid key
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const uint32_t k = keys[q];
+    nv += k != 0u;
+    k2 = max(k2, min(kmax, k));
+    kmax = max(kmax, k);
+  }
+  uint32_t kmin = 0xFFFFFFFFu;  // smallest valid key
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) kmin = keys[q] ? min(kmin, keys[q]) : kmin;
+  uint32_t lb = J == 1 ? kmax : (J == 2 ? k2 : 0u);
+  nv = wave_sum_i32(nv);
+  kmin = ~wave_max_u32(~kmin);
+  kmax = wave_max_u32(kmax);
+  lb = ~wave_max_u32(~lb);
+  if (lane == 0) {
+    sh.wi[wave][1] = nv;
+    sh.wu[wave][0] = kmin;
+    sh.wu[wave][1] = kmax;
+    sh.wscan[wave] = (int)lb;
+  }
+  __syncthreads();
+  int n_valid = 0;
+#pragma unroll
+  for (int w = 0; w < kRowW; ++w) {
+    n_valid += sh.wi[w][1];
+    kmin = min(kmin, sh.wu[w][0]);
+    kmax = max(kmax, sh.wu[w][1]);
+    lb = min(lb, (uint32_t)sh.wscan[w]);
+  }
+  const int take = min(kk, n_valid);
+  const int mode = take == 0 ? 0 : (take == n_valid ? 1 : 2);
+
+  // theta: narrow [lo, hi] (keys in it rank need-th from its top) to one key
+  uint32_t theta = 0u;
+  int t_eq = 0;
+  if (mode == 2) {
+    uint32_t lo = max(kmin, lb), hi = kmax;  // theta is in [lo, hi], rank take from the top
+    int need = take;
+    // 4096-fold narrowing: 32-bit keys need at most three passes (the cap
+    // only bounds the loop).  Once the range holds at most kRowFew keys,
+    // one wave ranks them directly.
+    int m = n_valid;
+    for (int pass = 0; pass < 4 && lo != hi; ++pass) {
+      if (m <= kRowFew) {
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) {
+          const uint32_t k = keys[q];
+          if (k >= lo && k <= hi) sh.mkeys[atomicAdd(&sh.mcount, 1u)] = k;
+        }
+        __syncthreads();
+        if (wave == 0) {
+          // lane l < m: keys above and at least its own among the m
+          const uint32_t mine = lane < m ? sh.mkeys[lane] : 0u;
+          int gt = 0, ge = 0;
+          for (int i = 0; i < m; ++i) {
+            const uint32_t ki = sh.mkeys[i];
+            gt += ki > mine;
+            ge += ki >= mine;
+          }
+          if (lane < m && gt < need && need <= ge) {  // every such lane holds the same key
+            sh.u[0] = mine;
+            sh.u[1] = (uint32_t)(need - gt);
+          }
+        }
+        __syncthreads();
+        lo = hi = sh.u[0];
+        need = (int)sh.u[1];
+        break;
+      }
+      const uint32_t span1 = hi - lo;
+      int sft = 0;
+      while ((span1 >> sft) >= (uint32_t)kRowBins) ++sft;
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) {
+        const uint32_t k = keys[q];
+        if (k >= lo && k <= hi) atomicAdd(&sh.h[(k - lo) >> sft], 1u);
+      }
+      __syncthreads();
+      uint32_t b;
+      int ab;
+      row_locate(sh, need, b, ab, m);
+      lo += b << sft;
+      hi = (uint32_t)min((uint64_t)hi, (uint64_t)lo + ((1ull << sft) - 1));
+      need -= ab;
+    }
+    theta = lo;
+    t_eq = need;  // theta-ties to keep, in index order
+  }
+
+  // kept: key > theta (mode 1: every valid key), or one of the first t_eq
+  // theta-ties in index order.  Per-thread counts, then per wave.
+  int c_gt = 0, c_eq = 0;
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    c_gt += keys[q] > theta;
+    c_eq += mode == 2 && keys[q] == theta;
+  }
+  c_gt = wave_sum_i32(c_gt);
+  c_eq = wave_sum_i32(c_eq);
+  __syncthreads();  // sh.wi is reused
+  if (lane == 0) {
+    sh.wi[wave][0] = c_gt;
+    sh.wi[wave][1] = c_eq;
+  }
+  __syncthreads();
+  int o = 0, eseen = 0, e_total = 0;
+#pragma unroll
+  for (int w = 0; w < kRowW; ++w) {
+    const int eq = sh.wi[w][1];
+    if (w < wave) {
+      o += sh.wi[w][0] + max(0, min(eq, t_eq - eseen));
+      eseen += eq;
+    }
+    e_total += eq;
+  }
+
+  // padding and count (only the last block can be partial)
+  const int bs = a.block;
+  int32_t* out = pool_mode ? a.pool + (int64_t)r * a.pool_stride : a.idx + (int64_t)r * a.idx_stride;
+  if constexpr (pool_mode) {
+    bool last_kept = false;
+    if (mode != 0) {
+      const uint32_t kl = s.key(n - 1);  // the highest-index block: a tie is kept iff all are
+      last_kept = mode == 1 ? kl != 0u : (kl > theta || (kl == theta && e_total <= t_eq));
+    }
+    const int pool_n = take * bs - (last_kept ? n * bs - ri.n_avail : 0);
+    for (int i = pool_n + tid; i < a.max_blocks * bs; i += kRowT) out[i] = -1;
+    if (tid == 0) a.pool_count[r] = pool_n;
+  } else {
+    for (int i = take + tid; i < a.k; i += kRowT) out[i] = -1;
+    if (tid == 0) a.count[r] = take;
+  }
+  if (mode == 0) return;
+
+  auto put = [&](int j, int rank) {
+    if constexpr (pool_mode) {
+      const int lo = j * bs, mm = min(bs, ri.n_avail - lo);
+      for (int u = 0; u < mm; ++u) out[rank * bs + u] = lo + u;
+    } else {
+      out[rank] = s.position(j);
+    }
+  };
+  // Every theta-tie is kept (the usual case): one ballot per element.
+  // Otherwise the ties also need their rank among the row's ties.
+  const uint32_t kmin_kept = (mode == 2 && e_total <= t_eq) ? theta : theta + 1u;
+  if (mode == 1 || e_total <= t_eq) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const bool keep = keys[q] >= kmin_kept;
+      const uint64_t mk = __ballot(keep);
+      if (keep) put(jw + 64 * q, o + (int)__popcll(mk & below));
+      o += (int)__popcll(mk);
+    }
+    return;
+  }
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const uint32_t k = keys[q];
+    const bool eq = k == theta;
+    const uint64_t me = __ballot(eq);
+    const bool keep = k > theta || (eq && eseen + (int)__popcll(me & below) < t_eq);
+    const uint64_t mk = __ballot(keep);
+    if (keep) put(jw + 64 * q, o + (int)__popcll(mk & below));
+    o += (int)__popcll(mk);
+    eseen += (int)__popcll(me);
+  }
+}
+
 // Chunks of 2048 elements; when rows x chunks already gives many workgroups
 // (prefill row blocks), chunks of 8192, so the per-chunk fixed work (row
 // histogram, member list) is spread over 4x more elements.
@@ -662,7 +935,20 @@ void run_select_chunk(const SelectArgs& a, const Ws& ws, int64_t max_n, int kk, 
 template <int KIND>
 void run_select(const SelectArgs& a, const Ws& ws, int64_t max_n, int kk, int pool_mode,
                 hipStream_t st) {
-  const int64_t wgs = (int64_t)a.rows.n_rows * ((max_n + kChunk - 1) / kChunk);
+  const int R = a.rows.n_rows;
+  if (max_n <= 16 * kRowT) {
+    hipLaunchKernelGGL((row_select_kernel<KIND, 16>), dim3(R), dim3(kRowT), 0, st, a, ws, kk);
+    return;
+  }
+  if (max_n <= 32 * kRowT) {
+    hipLaunchKernelGGL((row_select_kernel<KIND, 32>), dim3(R), dim3(kRowT), 0, st, a, ws, kk);
+    return;
+  }
+  if (max_n <= 64 * kRowT) {
+    hipLaunchKernelGGL((row_select_kernel<KIND, 64>), dim3(R), dim3(kRowT), 0, st, a, ws, kk);
+    return;
+  }
+  const int64_t wgs = (int64_t)R * ((max_n + kChunk - 1) / kChunk);
   if (wgs >= 16384)
     run_select_chunk<KIND, 4 * kChunk>(a, ws, max_n, kk, pool_mode, st);
   else

@@ -374,6 +374,34 @@ def test_select_many_rows(dev):
         assert np.array_equal(gi.cpu().numpy(), oi), (window, k)
 
 
+def test_select_long_rows_chunked(dev):
+    """Rows longer than one workgroup holds in registers (65536 keys) take
+    the chunk-parallel path: token selection over 100000-entry rows with a
+    wide tie at the threshold, next to the block pool of the same rows,
+    bit-exact."""
+    from index_reuse_amd import Rows, topk_select
+
+    import oracle
+
+    R, S = 3, 100000
+    scores = synth.small_ints((R, S), seed=123, lo=-50, hi=50)
+    scores[scores == 0] = -0.0
+    scores[1, 5000:60000] = 7.0  # a wide tie straddling the threshold
+    so = torch.zeros(R, dtype=torch.int32)
+    po = torch.tensor([S - 1, S - 2, S - 1000], dtype=torch.int32)
+    sl = torch.tensor([S], dtype=torch.int32)
+    for window, k, mb in ((0, 3000, 2000), (40, 20000, 1000)):
+        rows = Rows(so.to(dev), po.to(dev), sl.to(dev), 1, window)
+        gi, gc, gp, gpc = topk_select(rows, scores.to(dev), k, block=8, max_blocks=mb)
+        oi, oc, op, opc = oracle.topk_select(so, po, sl, 1, window, scores.double().numpy(), k,
+                                             block=8, max_blocks=mb)
+        torch.cuda.synchronize()
+        assert np.array_equal(gc.cpu().numpy(), oc)
+        assert np.array_equal(gi.cpu().numpy(), oi), (window, k)
+        assert np.array_equal(gpc.cpu().numpy(), opc)
+        assert np.array_equal(gp.cpu().numpy(), op), (window, k, mb)
+
+
 def test_deterministic_and_reuse(dev):
     """Two runs are bitwise identical; one fused call over all query sets
     equals one call per set (index reuse changes nothing numerically)."""
