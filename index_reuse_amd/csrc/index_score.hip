@@ -143,16 +143,35 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
   const int ngrp = min(gpw, (n_slots - wbase + 63) / 64);  // groups of this wave
   if (ngrp <= 0) return;
 
+  // Without a candidate list, a group's 64 slots are consecutive; when a
+  // paged cache's pages hold whole groups, the group lies in one page, read
+  // from the block table with one scalar load (no vector load then waits on
+  // a table load).  Slots past the row stay inside that page.
+  const bool page_per_group =
+      !cand_mode && a.k.block_table != nullptr && a.k.page_shift >= 6;
+  const int wbase_u = __builtin_amdgcn_readfirstlane(wbase);
   auto load_group = [&](int gi, Group<DIM, FP8>& G) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int slot = wbase + 64 * gi + 16 * t + col;
       G.pos[t] = cand_mode ? cand[min(slot, n_slots - 1)] : slot;
     }
+    if (page_per_group) {
+      const int s0 = wbase_u + 64 * gi;
+      const int64_t page =
+          a.k.block_table[(int64_t)ri.b * a.k.max_pages + (s0 >> a.k.page_shift)];
+      const char* pbase = a.k.data + page * a.k.page_size * a.k.row_stride;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int pc = min(max(G.pos[t], 0), ri.n_avail - 1);
-      G.ks[t].load(cache_row(a.k, ri.b, pc), g);
+      for (int t = 0; t < 4; ++t) {
+        const int off = (s0 + 16 * t + col) & (a.k.page_size - 1);
+        G.ks[t].load(pbase + (int64_t)off * a.k.row_stride, g);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int pc = min(max(G.pos[t], 0), ri.n_avail - 1);
+        G.ks[t].load(cache_row(a.k, ri.b, pc), g);
+      }
     }
   };
   Group<DIM, FP8> buf[2];
