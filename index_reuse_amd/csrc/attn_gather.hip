@@ -118,6 +118,83 @@ struct TileRegs {
   uint32_t sc[FP4 ? U : 1];  // FP4: the two E4M3 scales of each 32-channel chunk
 };
 
+// ------------------------------------------------------ entry range table
+// A workgroup serves entries [e0, e0 + per_split) of its row, in this order:
+// the selected ones (idx[0 .. count)), then the window.  Selected entries
+// come first so that their index loads depend only on the row, not on the
+// sequence length; they are issued before anything else.
+constexpr int kPT = 4;  // table entries per thread per pass
+
+template <int NTH>
+__device__ __forceinline__ void issue_index_loads(const AttnArgs& a, int r, int e0, int (&sel_pre)[kPT]) {
+  const int32_t* idx = a.idx ? a.idx + (int64_t)r * a.idx_stride : nullptr;
+#pragma unroll
+  for (int j = 0; j < kPT; ++j)
+    sel_pre[j] = idx ? idx[min(e0 + j * NTH + (int)threadIdx.x, a.idx_stride - 1)] : -1;
+}
+
+struct RangeTable {
+  int ne;          // entries in the range
+  int nsteps;      // steps of NG tiles covering them
+  int nsteps_run;  // nsteps, or 0 when no entry of the range has a slot
+  uint32_t dummy;  // slot read by padding entries
+};
+
+// Cache slot of every entry of the range, once, through the block table,
+// into slot[] (LDS).  Padding to whole steps, and the D steps past the end
+// that a prefetch ring reads, are -1.  Loads are clamped rather than guarded
+// so that a thread's loads all issue before the first wait.  Padding entries
+// later read the rows of the range's first real entry: finite data that the
+// mask gives weight exactly 0.  Ends with a barrier.
+template <int NTH, int NG, int D>
+__device__ __forceinline__ RangeTable build_range_table(const AttnArgs& a, int r, int e0, int per_split,
+                                                        const RowInfo& ri, const int (&sel_pre)[kPT],
+                                                        int32_t* slot_tab, int32_t* wfirst_tab) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t* idx = a.idx ? a.idx + (int64_t)r * a.idx_stride : nullptr;
+  const int n_w = ri.n_avail - ri.win_lo;
+  const int cnt = (idx && ri.b >= 0) ? a.count[r] : 0;
+  const int n_e = ri.b < 0 ? 0 : n_w + cnt;
+  const int e1 = min(n_e, e0 + per_split);
+  RangeTable rt;
+  rt.ne = max(0, e1 - e0);
+  const int ntiles = (rt.ne + kTile - 1) / kTile;
+  rt.nsteps = (ntiles + NG - 1) / NG;
+  int wfirst = 0x7FFFFFFF;
+  const int n_tab = (rt.nsteps + D) * NG * kTile;
+  for (int i0 = 0; i0 < n_tab; i0 += kPT * NTH) {
+    int pos[kPT];
+#pragma unroll
+    for (int j = 0; j < kPT; ++j) {
+      const int i = i0 + j * NTH + tid;
+      const int e = e0 + i;
+      const int sel = i0 == 0 ? sel_pre[j] : (idx ? idx[min(e, a.idx_stride - 1)] : -1);
+      pos[j] = i < rt.ne ? (e < cnt ? sel : ri.win_lo + (e - cnt)) : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kPT; ++j) {
+      const int i = i0 + j * NTH + tid;
+      int slot = -1;
+      if (ri.b >= 0) {
+        const int sl = (int)cache_slot(a.k, ri.b, max(pos[j], 0));
+        slot = pos[j] >= 0 ? sl : -1;
+      }
+      if (i < n_tab) slot_tab[i] = slot;
+      // the wave's lowest entry with a slot
+      const uint64_t has = __builtin_amdgcn_ballot_w64(slot >= 0);
+      if (has) wfirst = min(wfirst, i0 + j * NTH + (tid & ~63) + (int)__builtin_ctzll(has));
+    }
+  }
+  if (lane == 0) wfirst_tab[wave] = wfirst;
+  __syncthreads();
+  int first = 0x7FFFFFFF;
+#pragma unroll
+  for (int w = 0; w < NTH / 64; ++w) first = min(first, wfirst_tab[w]);
+  rt.nsteps_run = first < rt.ne ? rt.nsteps : 0;
+  rt.dummy = first < rt.ne ? (uint32_t)slot_tab[first] : 0u;
+  return rt;
+}
+
 template <int DQK, int DV, int KV, int W, int NG, int D>
 __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_split) {
   constexpr int NTH = 64 * W * NG;
@@ -159,67 +236,13 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
     }
   }
 
-  // Entries of the row in this order: the selected ones (idx[0 .. count)),
-  // then the window.  Selected entries come first so that their index loads
-  // depend only on the row, not on the sequence length.
-  const int32_t* idx = a.idx ? a.idx + (int64_t)r * a.idx_stride : nullptr;
-  const int e0 = sp * per_split;
-  constexpr int PT = 4;  // table entries per thread per pass
-  int sel_pre[PT];
-#pragma unroll
-  for (int j = 0; j < PT; ++j)
-    sel_pre[j] = idx ? idx[min(e0 + j * NTH + tid, a.idx_stride - 1)] : -1;
-
+  int sel_pre[kPT];
+  issue_index_loads<NTH>(a, r, sp * per_split, sel_pre);
   const RowInfo ri = row_info(a.rows, r);
-  const int n_w = ri.n_avail - ri.win_lo;
-  const int cnt = (idx && ri.b >= 0) ? a.count[r] : 0;
-  const int n_e = ri.b < 0 ? 0 : n_w + cnt;
-  const int e1 = min(n_e, e0 + per_split);
-  const int ne = max(0, e1 - e0);
-  const int ntiles = (ne + kTile - 1) / kTile;
-  const int nsteps = (ntiles + NG - 1) / NG;
-
-  // Cache slot of every entry of this range, once, through the block table.
-  // Padding to whole steps, and the D steps past the end that the prefetch
-  // ring reads, are -1.  Loads are clamped rather than guarded so that a
-  // thread's loads all issue before the first wait.
-  {
-    int wfirst = 0x7FFFFFFF;
-    const int n_tab = (nsteps + D) * NG * kTile;
-    for (int i0 = 0; i0 < n_tab; i0 += PT * NTH) {
-      int pos[PT];
-#pragma unroll
-      for (int j = 0; j < PT; ++j) {
-        const int i = i0 + j * NTH + tid;
-        const int e = e0 + i;
-        const int sel = i0 == 0 ? sel_pre[j] : (idx ? idx[min(e, a.idx_stride - 1)] : -1);
-        pos[j] = i < ne ? (e < cnt ? sel : ri.win_lo + (e - cnt)) : -1;
-      }
-#pragma unroll
-      for (int j = 0; j < PT; ++j) {
-        const int i = i0 + j * NTH + tid;
-        int slot = -1;
-        if (ri.b >= 0) {
-          const int sl = (int)cache_slot(a.k, ri.b, max(pos[j], 0));
-          slot = pos[j] >= 0 ? sl : -1;
-        }
-        if (i < n_tab) lds.slot[i] = slot;
-        // the wave's lowest entry with a slot
-        const uint64_t has = __builtin_amdgcn_ballot_w64(slot >= 0);
-        if (has) wfirst = min(wfirst, i0 + j * NTH + (tid & ~63) + (int)__builtin_ctzll(has));
-      }
-    }
-    if (lane == 0) lds.wfirst[wave] = wfirst;
-  }
-  __syncthreads();
-  // Padding entries (slot -1) read the rows of the range's first real entry:
-  // finite data that the mask gives weight exactly 0.  A range with no real
-  // entry computes nothing.
-  int first = 0x7FFFFFFF;
-#pragma unroll
-  for (int w = 0; w < W * NG; ++w) first = min(first, lds.wfirst[w]);
-  const int nsteps_run = first < ne ? nsteps : 0;
-  const uint32_t dummy = first < ne ? (uint32_t)lds.slot[first] : 0u;
+  const RangeTable rt = build_range_table<NTH, NG, D>(a, r, sp * per_split, per_split, ri, sel_pre,
+                                                      lds.slot, lds.wfirst);
+  const int ne = rt.ne, nsteps = rt.nsteps, nsteps_run = rt.nsteps_run;
+  const uint32_t dummy = rt.dummy;
 
   // Chunk c of a step: tile c / C_ALL of the step, then K or V row part.
   // Issue the global loads of step s into registers.  Branch-free, so the
@@ -554,6 +577,309 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
   }
 }
 
+// ---------------------------------------------------------- latent prefill
+// The latent shape of prefill: one 576-wide row per entry serves as K, its
+// first 512 channels as V, with 64 query rows per workgroup (4 waves, one
+// per SIMD; RT = 4 row tiles of 16).  Wave w = (hh, dh), hh = w & 1,
+// dh = w >> 1:
+//   - S: partial logits of row tiles {2 hh, 2 hh + 1} over k-steps
+//     [9 dh, 9 dh + 9) of the 18; every K fragment read from LDS feeds both
+//     row tiles;
+//   - the two dim halves hand each other the partials of one row tile
+//     through LDS; wave w then finishes row tile 2 hh + dh: mask, softmax,
+//     and its probabilities (bf16) into LDS;
+//   - O: channels [128 w, 128 w + 128) of all four row tiles, so each V
+//     channel block is read from LDS by one wave.
+// Per 32-entry tile a wave reads 18 KB of K, 8 KB of V and 4 KB of P from
+// LDS, against 68 KB of K and V when a wave owns one row tile outright.
+// (Two row tiles per workgroup with one K buffer, two workgroups per CU, ran
+// 15% slower: each K fragment then feeds one MFMA, with four barriers per
+// tile.)
+constexpr int kMlaDqk = 576, kMlaDv = 512, kMlaRT = 4, kMlaD = 2;
+
+struct MlaLds {
+  static constexpr int RT = kMlaRT, D = kMlaD;
+  static constexpr int KROW = kMlaDqk + 8;  // bf16 per LDS row (padded)
+  static constexpr int SLOTS = kMaxEntries + (D + 1) * kTile;
+  uint16_t k[2][kTile * KROW];
+  float sx[4][8][64];      // S partials handed to the other dim half
+  u32x4 p[RT][64];         // P^T operand of each row tile
+  float ml[RT][16][3];     // per row tile: m, rounded and unrounded sums
+  int32_t wfirst[4];
+  int32_t slot[SLOTS];
+};
+
+// The Z query-row groups of one (split, row, KV head) gather the same rows,
+// so they run on one XCD at about the same time and the later reads hit that
+// XCD's L2: a 1-D grid, workgroups 8 apart in launch order (one XCD) take the
+// Z groups of one unit, units rotate over the 8 XCDs.
+__device__ __forceinline__ void mla_unit(int n_units, int Z, int& unit, int& z) {
+  const int L = blockIdx.x;
+  const int rest = L >> 3;
+  z = rest % Z;
+  unit = (rest / Z) * 8 + (L & 7);
+  if (unit >= n_units) unit = -1;
+}
+
+__global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, int n_units, int Z) {
+  constexpr int NTH = 256, DQK = kMlaDqk, DV = kMlaDv, RT = kMlaRT, D = kMlaD;
+  constexpr int KH = DQK / 64;      // k-steps per dim half
+  constexpr int HT = 2;             // row tiles in this wave's S
+  using L = MlaLds;
+  using T = TileRegs<DQK, DV, KV_SHARED, NTH, 1>;
+  static_assert(sizeof(L) <= 160 * 1024, "LDS budget");
+  __shared__ __align__(16) L lds;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, gq = lane >> 4;
+  const int hh = wave & 1, dh = wave >> 1;
+  const int own = 2 * hh + dh;  // row tile this wave finishes
+  int unit, zg;
+  mla_unit(n_units, Z, unit, zg);
+  if (unit < 0) return;
+  const int sp = unit % a.n_split;
+  const int ry = unit / a.n_split;
+  const int r = ry / a.hkv, g = ry % a.hkv;
+  const int G = a.hq / a.hkv;
+  const int Mq = a.n_qsets * G;
+  const int qrow0 = zg * 16 * RT;
+
+  // this wave's S row tiles, k-steps [KH dh, KH dh + KH), as B operands
+  u32x4 qv[HT][KH];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int qr = qrow0 + 16 * (HT * hh + ht) + col;
+    if (qr < Mq) {
+      const int set = qr / G, h = g * G + qr % G;
+      const u32x4* qp = reinterpret_cast<const u32x4*>(
+          reinterpret_cast<const uint16_t*>(a.q) +
+          (((int64_t)set * a.rows.n_rows + r) * a.hq + h) * DQK + gq * (DQK / 4));
+#pragma unroll
+      for (int i = 0; i < KH; ++i) qv[ht][i] = qp[KH * dh + i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < KH; ++i) qv[ht][i] = u32x4{0, 0, 0, 0};
+    }
+  }
+  int sel_pre[kPT];
+  issue_index_loads<NTH>(a, r, sp * per_split, sel_pre);
+  const RowInfo ri = row_info(a.rows, r);
+  const RangeTable rt = build_range_table<NTH, 1, D>(a, r, sp * per_split, per_split, ri, sel_pre,
+                                                     lds.slot, lds.wfirst);
+  const int nsteps_run = rt.nsteps_run;
+  const uint32_t dummy = rt.dummy;
+
+  // step s = tile s: 16-byte pieces of its 32 rows, through registers
+  static_assert(T::TOT % NTH == 0, "whole pieces per thread");
+  auto load_step = [&](int s, T& regs) {
+#pragma unroll
+    for (int u = 0; u < T::U; ++u) {
+      const int c = tid + NTH * u;
+      const int e = c / T::CPR_K, part = c % T::CPR_K;
+      const int sv = lds.slot[s * kTile + e];
+      const uint32_t slot = sv >= 0 ? (uint32_t)sv : dummy;
+      regs.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          a.k.data + (uint64_t)slot * (uint32_t)a.k.row_stride + g * (DQK * 2) + part * 16));
+    }
+  };
+  auto store_step = [&](const T& regs, int sb) {
+#pragma unroll
+    for (int u = 0; u < T::U; ++u) {
+      const int c = tid + NTH * u;
+      const int e = c / T::CPR_K, part = c % T::CPR_K;
+      *reinterpret_cast<u32x4*>(&lds.k[sb][e * L::KROW + part * 8]) = regs.v[u];
+    }
+  };
+
+  // Softmax state of the finished row tile (lane col), as in attn_mfma: the
+  // reference m_run is fixed by the first tile with a finite logit; a
+  // second pass runs with m_run = m_top if some tile exceeds it by more than
+  // kHeadroom.
+  constexpr float kHeadroom = 64.0f;
+  f32x4 O[RT][8];  // [row tile][channel tile j]: channels 128 w + 8 (4 gq + i) + j
+  float m_run = -__builtin_huge_valf(), m_top = -__builtin_huge_valf();
+  float l_run = 0.0f, l_lse = 0.0f;
+
+  auto compute = [&](int sb, int t) {
+    const uint16_t* kb = lds.k[sb];
+    // partial S^T tiles [ht][mt]: entries (M) x query rows (N)
+    f32x4 s[HT][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x4 acc[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* krow = kb + (mt * 16 + col) * L::KROW + gq * (DQK / 4) + KH * dh * 8;
+#pragma unroll
+      for (int i = 0; i < KH; ++i) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(krow + i * 8);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+          acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, qv[ht][i]), acc[ht], 0, 0, 0);
+      }
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) s[ht][mt] = acc[ht];
+    }
+    // hand over row tile 1 - dh, take the other half of row tile dh
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds.sx[wave][4 * mt + i][lane] = dh ? s[0][mt][i] : s[1][mt][i];
+    __syncthreads();
+    const int partner = hh + 2 * (1 - dh);
+    float x[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        x[mt][i] = (dh ? s[1][mt][i] : s[0][mt][i]) + lds.sx[partner][4 * mt + i][lane];
+    // mask and scale: lane holds entries mt*16 + 4*gq + i for query row col
+    float tmax = -__builtin_huge_valf();
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = lds.slot[t * kTile + mt * 16 + 4 * gq + i] >= 0;
+        x[mt][i] = ok ? x[mt][i] * a.scale_log2 : -__builtin_huge_valf();
+        tmax = fmaxf(tmax, x[mt][i]);
+      }
+    tmax = xor16_32_max(tmax);
+    if (m_run == -__builtin_huge_valf()) m_run = tmax;  // O is still all zero
+    m_top = fmaxf(m_top, tmax);
+    const float m_use = m_run == -__builtin_huge_valf() ? 0.0f : m_run;
+    float pr[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[mt][i] = fast_exp2(x[mt][i] - m_use);
+    // P^T as the B operand: k-slot 8*gq + i <-> entry (i<4 ? 4gq+i : 16+4gq+i-4)
+    u32x4 pa;
+    pa[0] = pack_bf16x2(pr[0][0], pr[0][1]);
+    pa[1] = pack_bf16x2(pr[0][2], pr[0][3]);
+    pa[2] = pack_bf16x2(pr[1][0], pr[1][1]);
+    pa[3] = pack_bf16x2(pr[1][2], pr[1][3]);
+    float psum = 0.0f, xsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      psum += __uint_as_float(pa[i] << 16) + __uint_as_float(pa[i] & 0xFFFF0000u);
+      xsum += pr[i >> 1][2 * (i & 1)] + pr[i >> 1][2 * (i & 1) + 1];
+    }
+    l_run += xor16_32_sum(psum);
+    l_lse += xor16_32_sum(xsum);
+    lds.p[own][lane] = pa;
+    __syncthreads();
+    bf16x8 pb[RT];
+#pragma unroll
+    for (int q = 0; q < RT; ++q) pb[q] = __builtin_bit_cast(bf16x8, lds.p[q][lane]);
+    // V^T as the A operand for channels 128 w + 8 col + j of the 8 entries of
+    // each lane's k-slots (an 8x8 bf16 transpose in registers)
+    u32x4 R[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = i < 4 ? 4 * gq + i : 16 + 4 * gq + (i - 4);
+      R[i] = *reinterpret_cast<const u32x4*>(kb + e * L::KROW + wave * 128 + col * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 b;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        b[qd] = (j & 1) ? hi16x2(R[2 * qd][j >> 1], R[2 * qd + 1][j >> 1])
+                        : lo16x2(R[2 * qd][j >> 1], R[2 * qd + 1][j >> 1]);
+#pragma unroll
+      for (int q = 0; q < RT; ++q)
+        O[q][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), pb[q],
+                                                          O[q][j], 0, 0, 0);
+    }
+  };
+
+  T ring[D];
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int q = 0; q < RT; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) O[q][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < D; ++u) load_step(u, ring[u]);
+    int s0 = 0;
+    for (; s0 + D <= nsteps_run; s0 += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        store_step(ring[u], u);  // D = 2: buffer u
+        __syncthreads();
+        load_step(s0 + u + D, ring[u]);
+        compute(u, s0 + u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      if (s0 + u < nsteps_run) {
+        store_step(ring[u], u);
+        __syncthreads();
+        compute(u, s0 + u);
+      }
+    }
+    if (!__syncthreads_or(m_top > m_run + kHeadroom)) break;
+    m_run = m_top;
+    l_run = 0.0f;
+    l_lse = 0.0f;
+  }
+
+  // publish the finished row tile's state, then write channels 128 w.. of
+  // all RT row tiles
+  if (gq == 0) {
+    lds.ml[own][col][0] = m_run;
+    lds.ml[own][col][1] = l_run;
+    lds.ml[own][col][2] = l_lse;
+  }
+  __syncthreads();
+  const int R_ = a.rows.n_rows;
+#pragma unroll
+  for (int q = 0; q < RT; ++q) {
+    const int qr = qrow0 + 16 * q + col;
+    if (qr >= Mq) continue;
+    const int set = qr / G, h = g * G + qr % G;
+    const int64_t orow = ((int64_t)set * R_ + r) * a.hq + h;
+    const float m_r = lds.ml[q][col][0], l_r = lds.ml[q][col][1], lx = lds.ml[q][col][2];
+    const f32x4* o = O[q];
+    if (a.n_split == 1) {
+      const float inv = l_r > 0.0f ? 1.0f / l_r : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c0 = wave * 128 + 32 * gq + 8 * i;
+        if (a.o_dtype == 1) {
+          u32x4 pk;
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            pk[qd] = pack_bf16x2(o[2 * qd][i] * inv, o[2 * qd + 1][i] * inv);
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.o) + orow * DV + c0) = pk;
+        } else {
+          float* op = reinterpret_cast<float*>(a.o) + orow * DV + c0;
+          reinterpret_cast<f32x4*>(op)[0] = f32x4{o[0][i] * inv, o[1][i] * inv, o[2][i] * inv, o[3][i] * inv};
+          reinterpret_cast<f32x4*>(op)[1] = f32x4{o[4][i] * inv, o[5][i] * inv, o[6][i] * inv, o[7][i] * inv};
+        }
+      }
+      if (a.lse && wave == 0 && gq == 0)
+        a.lse[orow] = lx > 0.0f ? (m_r + __log2f(lx)) * 0.6931471805599453f : -__builtin_huge_valf();
+    } else {
+      const int64_t nrows = (int64_t)a.n_qsets * R_ * a.hq;
+      float* po = a.part + ((int64_t)sp * nrows + orow) * DV;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float* op = po + wave * 128 + 32 * gq + 8 * i;
+        reinterpret_cast<f32x4*>(op)[0] = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
+        reinterpret_cast<f32x4*>(op)[1] = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
+      }
+      if (wave == 0 && gq == 0) {
+        float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 3;
+        ml[0] = m_r;
+        ml[1] = l_r;
+        ml[2] = lx;
+      }
+    }
+  }
+}
+
 // Merge split partials: o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i,
 // lse from the unrounded sums lx_i the same way.  One wave per output row:
 // lane i < n_split holds split i's (m, l, lx) and its weight; every lane then
@@ -709,6 +1035,20 @@ hipError_t launch_mfma_attn(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_mla(const AttnArgs& a, hipStream_t s) {
+  const int G = a.hq / a.hkv;
+  const int groups = (a.n_qsets * G + 16 * kMlaRT - 1) / (16 * kMlaRT);
+  const int per = ((a.max_entries + a.n_split - 1) / a.n_split + kTile - 1) / kTile * kTile;
+  const int n_units = a.n_split * a.rows.n_rows * a.hkv;
+  const int64_t nwg = (int64_t)(n_units + 7) / 8 * 8 * groups;
+  hipLaunchKernelGGL(attn_mla, dim3((unsigned)nwg), dim3(256), 0, s, a, per, n_units, groups);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split == 1) return e;
+  const int64_t nrows = (int64_t)a.n_qsets * a.rows.n_rows * a.hq;
+  hipLaunchKernelGGL(attn_combine, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int DQK, int DV, int KV, int D>
 hipError_t launch_shaped(const AttnArgs& a, hipStream_t s) {
   const AttnShape sh = attn_shape(a);
@@ -759,7 +1099,11 @@ hipError_t launch_attn_gather(const AttnArgs& a, hipStream_t s) {
     if (a.dqk == 128 && a.dv == 128) return launch_shaped<128, 128, KV_SEPARATE, 2>(a, s);
     if (a.dqk == 256 && a.dv == 256) return launch_shaped<256, 256, KV_SEPARATE, 2>(a, s);
   } else if (a.kv_kind == KV_SHARED) {
-    if (a.dqk == 576 && a.dv == 512) return launch_shaped<576, 512, KV_SHARED, 2>(a, s);
+    if (a.dqk == 576 && a.dv == 512) {
+      // latent rows with at least 64 query rows per KV head: split S / O
+      if (a.n_qsets * (a.hq / a.hkv) >= 16 * kMlaRT) return launch_mla(a, s);
+      return launch_shaped<576, 512, KV_SHARED, 2>(a, s);
+    }
     if (a.dqk == 512 && a.dv == 512) return launch_shaped<512, 512, KV_SHARED, 2>(a, s);
     if (a.dqk == 128 && a.dv == 128) return launch_shaped<128, 128, KV_SHARED, 2>(a, s);
   } else if (a.kv_kind == KV_FP4) {
