@@ -393,6 +393,9 @@ def main():
                     help="prefill: query rows per block (the score buffer holds one block)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run a plain copy of this size first (counter calibration)")
+    ap.add_argument("--eager", action="store_true",
+                    help="decode: launch every call from the host in the timed region instead of "
+                         "replaying one captured graph of the K steps")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -429,6 +432,9 @@ def main():
             c(stream)
     torch.cuda.synchronize()
 
+    # Per-call times: K steps launched from the host, a HIP event before and
+    # after every call on the launch stream (a call's interval includes its
+    # launch gap, so these are upper bounds on kernel time).
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(K)]
     torch.cuda.synchronize()
@@ -442,6 +448,24 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
+    mode = "eager"
+    if not args.eager:
+        # Throughput: the same K steps captured once as a HIP graph (no host
+        # launches between calls, as a serving loop would run them); one
+        # untimed replay uploads it, the timed replay runs the K steps.
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream().cuda_stream
+            for i in range(K):
+                for _, c in calls[i % len(calls)]:
+                    c(cs)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        mode = "graph"
     ms_step = elapsed * 1e3 / K
     per_call = {}
     for j, n in enumerate(names):
@@ -477,7 +501,7 @@ def main():
                    "query_sets": sum(q.shape[0] for q in step0.prob.q), "kv_heads": wl.hkv,
                    "q_heads": wl.hq, "head_dim": wl.dqk, "indexer": "%dx%d %s" % (
                        wl.idx_heads, wl.idx_dim, str(wl.idx_dtype).replace("torch.", "")),
-                   "page_size": wl.page_size, "replicas": args.replicas},
+                   "page_size": wl.page_size, "replicas": args.replicas, "launch": mode},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else int(traffic),

@@ -402,6 +402,43 @@ def test_select_long_rows_chunked(dev):
         assert np.array_equal(gp.cpu().numpy(), op), (window, k, mb)
 
 
+@pytest.mark.parametrize("name", ["hysparse2", "csa2"])
+def test_graph_replay_matches_eager(name, dev):
+    """A whole step captured as one HIP graph (as the throughput benchmark
+    replays it) gives bit-identical outputs on every replay, with eager work
+    and synchronisation between replays and the outputs cleared before each."""
+    wl, _ = CASES[name]
+    _flush("case graph %s" % name)
+    p, step = _step(synth.make_problem(wl, device="cpu"), dev)
+    p2, other = _step(synth.make_problem(wl, device="cpu", seed_base=777), dev)
+    calls = step.prepare()
+    others = other.prepare()
+    stream = torch.cuda.current_stream().cuda_stream
+    outs = lambda st: [t for t in (st.scores + st.idx + st.count + st.o + st.lse
+                                   + [st.pool, st.pool_count]) if t is not None]
+    for t in outs(step):  # entries no call writes stay zero on both sides
+        t.zero_()
+    for _, c in calls:
+        c(stream)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs(step)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for _, c in calls:
+            c(cs)
+    for rep in range(3):
+        for t in outs(step):
+            t.zero_()
+        for _, c in others:  # the program's own eager work between replays
+            c(stream)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs(step), ref):
+            assert torch.equal(a, b), (name, rep)
+
+
 def test_deterministic_and_reuse(dev):
     """Two runs are bitwise identical; one fused call over all query sets
     equals one call per set (index reuse changes nothing numerically)."""
