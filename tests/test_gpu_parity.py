@@ -374,6 +374,33 @@ def test_select_many_rows(dev):
         assert np.array_equal(gi.cpu().numpy(), oi), (window, k)
 
 
+def test_select_few_long_rows(dev):
+    """The decode regime: a few rows of 16385 to 32768 candidates with
+    integer ties (one tie block of 400 at the top), a row of all-equal
+    scores, a padding row, and windows; bit-exact against the oracle."""
+    from index_reuse_amd import Rows, topk_select
+
+    import oracle
+
+    R, S = 9, 32768
+    scores = synth.small_ints((R, S), seed=31, lo=-40, hi=40)
+    scores[scores == 0] = -0.0
+    scores[2] = 5.0                      # all ties
+    scores[3, 8000:8400] = 100.0         # a tie block across the first part boundary
+    so = torch.zeros(R, dtype=torch.int32)
+    so[8] = -1                           # a padding row
+    po = torch.tensor([S - 1, S - 2, S - 1, 16384, 20000, S - 1, 17000, 30000, S - 1],
+                      dtype=torch.int32)
+    sl = torch.tensor([S], dtype=torch.int32)
+    for window, k in ((0, 1024), (128, 2048), (7, 100)):
+        rows = Rows(so.to(dev), po.to(dev), sl.to(dev), 1, window)
+        gi, gc = topk_select(rows, scores.to(dev), k)
+        oi, oc = oracle.topk_select(so, po, sl, 1, window, scores.double().numpy(), k)
+        torch.cuda.synchronize()
+        assert np.array_equal(gc.cpu().numpy(), oc), (window, k)
+        assert np.array_equal(gi.cpu().numpy(), oi), (window, k)
+
+
 def test_select_long_rows_chunked(dev):
     """Rows longer than one workgroup holds in registers (65536 keys) take
     the chunk-parallel path: token selection over 100000-entry rows with a
