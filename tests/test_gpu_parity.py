@@ -138,6 +138,12 @@ ATTN_SHAPES = {
     "shared128": dict(kv_mode="shared", hq=32, hkv=2, n_qsets=2),
     # separate K and V rows of 256 channels
     "sep256": dict(dqk=256, dv=256, hq=16, hkv=2, n_qsets=2),
+    # 576-wide latent rows (V = first 512): 16 query rows per KV head (one
+    # row tile per wave), 2 x 64 rows (two 64-row groups), and 80 rows (a
+    # partial second group)
+    "latent_h16": dict(dqk=576, dv=512, kv_mode="shared", hq=16, hkv=1, n_qsets=1),
+    "latent_h64_q2": dict(dqk=576, dv=512, kv_mode="shared", hq=64, hkv=1, n_qsets=2),
+    "latent_h80": dict(dqk=576, dv=512, kv_mode="shared", hq=80, hkv=1, n_qsets=1),
 }
 
 
