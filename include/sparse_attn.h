@@ -89,7 +89,7 @@ enum {
   SA_ERR_NULL = -1,        /* a required pointer is NULL                    */
   SA_ERR_SHAPE = -2,       /* sizes, strides or alignment inconsistent       */
   SA_ERR_DTYPE = -3,       /* unsupported dtype or dtype combination        */
-  SA_ERR_UNSUPPORTED = -4, /* valid request this build has no kernel for    */
+  SA_ERR_UNSUPPORTED = -4, /* valid request the library has no kernel for  */
   SA_ERR_WORKSPACE = -5,   /* ws too small or misaligned                    */
   SA_ERR_HIP = -6          /* a HIP runtime call or launch failed           */
 };
