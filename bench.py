@@ -432,9 +432,9 @@ def main():
             c(stream)
     torch.cuda.synchronize()
 
-    # Per-call times: K steps launched from the host, a HIP event before and
-    # after every call on the launch stream (a call's interval includes its
-    # launch gap, so these are upper bounds on kernel time).
+    # K steps launched from the host, a HIP event before and after every call
+    # on the launch stream (gpu_ms_per_step; with --eager also the per-call
+    # times and the throughput).
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(K)]
     torch.cuda.synchronize()
@@ -449,7 +449,29 @@ def main():
     t1 = time.perf_counter()
     elapsed = t1 - t0
     mode = "eager"
+    per_call = {}
+    for j, n in enumerate(names):
+        per_call[n] = sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K
     if not args.eager:
+        # Per-call times: each call captured K times in a row (cycling over
+        # the replicas, on inputs the steps above left in place) and replayed
+        # between two HIP events on the launch stream, so no host launch gap
+        # sits between its kernels.
+        for j, n in enumerate(names):
+            gc = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gc):
+                cs = torch.cuda.current_stream().cuda_stream
+                for i in range(K):
+                    calls[i % len(calls)][j][1](cs)
+            gc.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            gc.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per_call[n] = e0.elapsed_time(e1) / K
         # Throughput: the same K steps captured once as a HIP graph (no host
         # launches between calls, as a serving loop would run them); one
         # untimed replay uploads it, the timed replay runs the K steps.
@@ -467,9 +489,6 @@ def main():
         elapsed = time.perf_counter() - t0
         mode = "graph"
     ms_step = elapsed * 1e3 / K
-    per_call = {}
-    for j, n in enumerate(names):
-        per_call[n] = sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)) / K
     gpu_ms_step = sum(evs[i][0].elapsed_time(evs[i][-1]) for i in range(K)) / K
 
     step0 = steps[0]
