@@ -168,6 +168,47 @@ struct Src {
     }
     return j < n ? k : 0u;
   }
+  // keys of elements j0 + 64 q (q < Q), key 0 past the end.  Every load of
+  // a stage is issued before the first one is consumed: left to itself, the
+  // scheduler interleaves waits with the issue and keeps only about a dozen
+  // loads in flight per wave.  Needs n >= 1.
+  template <int Q>
+  __device__ __forceinline__ void keys_c(int j0, uint32_t (&k)[Q]) const {
+    float x[Q];
+    if constexpr (KIND == SRC_TOKEN_FULL || KIND == SRC_BLOCK) {
+#pragma unroll
+      for (int q = 0; q < Q; ++q) x[q] = sc[min(j0 + 64 * q, n - 1)];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < Q; ++q) k[q] = j0 + 64 * q < n ? order_key(x[q]) : 0u;
+    } else if constexpr (KIND == SRC_TOKEN_CAND) {
+      int p[Q];
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int jc = min(j0 + 64 * q, n - 1);
+        p[q] = list[jc];
+        x[q] = sc[jc];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        k[q] = (j0 + 64 * q < n && p[q] >= 0 && p[q] < win_lo) ? order_key(x[q]) : 0u;
+    } else {
+      int p[Q];
+#pragma unroll
+      for (int q = 0; q < Q; ++q) p[q] = list[min(j0 + 64 * q, n - 1)];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const bool ok = p[q] >= 0 && p[q] < win_lo;
+        x[q] = sc[ok ? p[q] : 0];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        k[q] = (j0 + 64 * q < n && p[q] >= 0 && p[q] < win_lo) ? order_key(x[q]) : 0u;
+    }
+  }
   static constexpr bool may_be_invalid() {
     return KIND == SRC_TOKEN_CAND || KIND == SRC_POOL;
   }
@@ -663,17 +704,23 @@ constexpr int kRowW = kRowT / 64;     // waves per row workgroup
 constexpr int kRowBins = 4096;        // histogram bins per pass
 constexpr int kRowBpt = kRowBins / kRowT;
 
-constexpr int kRowFew = 64;           // threshold-bin members resolved by one wave
+constexpr int kRowFew = 64;           // threshold-bin members ranked directly
+// Word 3 of a raw buffer resource on CDNA (32-bit dword loads, range-checked
+// against the resource's byte size: loads past it return 0).
+constexpr int kBufWord3 = 0x00020000;
 
 struct __align__(16) RowShared {
   uint32_t h[kRowBins];
   int wi[kRowW][2];
   uint32_t wu[kRowW][2];
   int wscan[kRowW];
+  int wc[kRowW][2];          // per-wave kept counts
   uint32_t u[4];
-  uint32_t mkeys[kRowFew];
+  uint32_t mkeys[kRowFew];  // 16-byte aligned: read as u32x4
+  int rk[kRowFew][2];       // per member: members above it, at least it
   uint32_t mcount;
 };
+static_assert(offsetof(RowShared, mkeys) % 16 == 0, "aligned member keys");
 
 // The bin holding the rank-th (1-based) element counting from the top bin;
 // returns (bin, elements in higher bins, elements in the bin).  Thread t owns
@@ -713,60 +760,113 @@ __device__ __forceinline__ void row_locate(RowShared& sh, int rank, uint32_t& bi
     sh.u[2] = (uint32_t)cb;
   }
   __syncthreads();
-  bin = sh.u[0];
-  above_bin = (int)sh.u[1];
-  in_bin = (int)sh.u[2];
+  bin = __builtin_amdgcn_readfirstlane(sh.u[0]);
+  above_bin = __builtin_amdgcn_readfirstlane((int)sh.u[1]);
+  in_bin = __builtin_amdgcn_readfirstlane((int)sh.u[2]);
 }
 
+// The row kernel is bound by vector instruction issue (four waves per SIMD),
+// so every pass over the keys is kept to a few instructions per key:
+//   - scores and block maxima are read with range-checked buffer loads
+//     (immediate offsets, no address arithmetic per key);
+//   - per-wave counts come from ballots and scalar popcounts;
+//   - the threshold key's tie count comes out of the last narrowing step, so
+//     the usual case (every tie kept) needs one comparison per key to count
+//     and one to emit.
 template <int KIND, int EPT>
 __global__ __launch_bounds__(kRowT) void row_select_kernel(SelectArgs a, Ws ws, int kk) {
   constexpr bool pool_mode = KIND == SRC_BLOCK;  // blocks expand into the pool
+  // every element below n has a valid key
+  constexpr bool dense = KIND == SRC_TOKEN_FULL || KIND == SRC_BLOCK;
   __shared__ RowShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t below = lanes_below();
   const int r = blockIdx.x;
   const RowInfo ri = row_info(a.rows, r);
   const Src<KIND> s = make_src<KIND>(a, ws, r, ri);
-  const int n = s.n;
+  const int n = __builtin_amdgcn_readfirstlane(s.n);
   const int jw = wave * (64 * EPT) + lane;  // element of q = 0
+  const int wn = min(max(n - wave * 64 * EPT, 0), 64 * EPT);  // this wave's elements below n
   uint32_t keys[EPT];
   if (n > 0) {
+    if constexpr (dense) {
+      // Elements jw + 64 q of sixteen consecutive q lie in one 1024-element
+      // window; each window gets a resource of its own (base and size are
+      // scalar), so one vector offset and immediate offsets address every
+      // load, and the range check (vector plus immediate offset against the
+      // size) returns 0 past the row.
+      float x[EPT];
 #pragma unroll
-    for (int q = 0; q < EPT; ++q) keys[q] = s.key_c(jw + 64 * q);
+      for (int g = 0; g < (EPT + 15) / 16; ++g) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(s.sc) + 1024 * g, (short)0, max(n - 1024 * g, 0) * (int)sizeof(float),
+            kBufWord3);
+#pragma unroll
+        for (int q = 16 * g; q < min(16 * g + 16, EPT); ++q)
+          x[q] = __builtin_bit_cast(float,
+                                    __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * jw + 256 * (q & 15), 0, 0));
+      }
+      if (wn == 64 * EPT) {
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) keys[q] = order_key(x[q]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) keys[q] = 64 * q + lane < wn ? order_key(x[q]) : 0u;
+      }
+    } else if constexpr (EPT <= 32) {
+      s.keys_c(jw, keys);
+    } else {  // no registers to spare for a whole stage
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) keys[q] = s.key_c(jw + 64 * q);
+    }
   } else {
 #pragma unroll
     for (int q = 0; q < EPT; ++q) keys[q] = 0u;
   }
 #pragma unroll
   for (int i = 0; i < kRowBpt; ++i) sh.h[tid + i * kRowT] = 0u;
+  if (tid < 2 * kRowFew) (&sh.rk[0][0])[tid] = 0;
   if (tid == 0) sh.mcount = 0u;
 
   // Valid count, max valid key, and a lower bound on theta: with J =
   // ceil(take / kRowT) <= 2, each thread's J-th largest key (0 if it has
   // fewer) is below J * kRowT >= take keys of the row, so the smallest of
   // them cannot exceed the take-th largest.  Keys under it are never kept
-  // and stay out of the histograms.
-  const int J = (min(kk, kRowT * EPT) + kRowT - 1) / kRowT;  // uniform; the bound is used for J <= 2
-  int nv = 0;
-  uint32_t kmax = 0u, k2 = 0u;  // this thread's largest and second largest valid key
+  // and stay out of the histograms.  When every thread holds J valid keys
+  // that bound is itself a valid key, so the row's smallest key is not
+  // needed.
+  const int J = (min(kk, kRowT * EPT) + kRowT - 1) / kRowT;  // the bound is used for J <= 2
+  uint32_t kmax = 0u, k2 = 0u;  // this thread's largest and second largest key
+  if (J == 2) {
 #pragma unroll
-  for (int q = 0; q < EPT; ++q) {
-    const uint32_t k = keys[q];
-    nv += k != 0u;
-    k2 = max(k2, min(kmax, k));
-    kmax = max(kmax, k);
+    for (int q = 0; q < EPT; ++q) {
+      k2 = max(k2, min(kmax, keys[q]));
+      kmax = max(kmax, keys[q]);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) kmax = max(kmax, keys[q]);
   }
-  uint32_t kmin = 0xFFFFFFFFu;  // smallest valid key
-#pragma unroll
-  for (int q = 0; q < EPT; ++q) kmin = keys[q] ? min(kmin, keys[q]) : kmin;
   uint32_t lb = J == 1 ? kmax : (J == 2 ? k2 : 0u);
-  nv = wave_sum_i32(nv);
-  kmin = ~wave_max_u32(~kmin);
+  const bool need_min = !dense || J > 2 || n - (kRowW - 1) * 64 * EPT < 64 * J;  // uniform
+  uint32_t kmin1 = 0xFFFFFFFFu;  // smallest valid key - 1 (a zero key wraps to the top)
+  if (need_min) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) kmin1 = min(kmin1, keys[q] - 1u);
+  }
+  int nv = 0;  // valid keys of the wave (uniform)
+  if constexpr (dense) {
+    nv = wn;
+  } else {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) nv += (int)__popcll(__ballot(keys[q] != 0u));
+  }
+  kmin1 = ~wave_max_u32(~kmin1);
   kmax = wave_max_u32(kmax);
   lb = ~wave_max_u32(~lb);
   if (lane == 0) {
     sh.wi[wave][1] = nv;
-    sh.wu[wave][0] = kmin;
+    sh.wu[wave][0] = kmin1;
     sh.wu[wave][1] = kmax;
     sh.wscan[wave] = (int)lb;
   }
@@ -775,96 +875,121 @@ __global__ __launch_bounds__(kRowT) void row_select_kernel(SelectArgs a, Ws ws, 
 #pragma unroll
   for (int w = 0; w < kRowW; ++w) {
     n_valid += sh.wi[w][1];
-    kmin = min(kmin, sh.wu[w][0]);
+    kmin1 = min(kmin1, sh.wu[w][0]);
     kmax = max(kmax, sh.wu[w][1]);
     lb = min(lb, (uint32_t)sh.wscan[w]);
   }
+  n_valid = __builtin_amdgcn_readfirstlane(n_valid);
+  kmax = __builtin_amdgcn_readfirstlane(kmax);
+  lb = __builtin_amdgcn_readfirstlane(lb);
+  const uint32_t kmin = need_min ? __builtin_amdgcn_readfirstlane(kmin1) + 1u : lb;
   const int take = min(kk, n_valid);
   const int mode = take == 0 ? 0 : (take == n_valid ? 1 : 2);
 
-  // theta: narrow [lo, hi] (keys in it rank need-th from its top) to one key
+  // theta: narrow [lo, hi] (keys in it rank need-th from its top) to one key;
+  // e_cnt = keys equal to theta, when the narrowing step yields it
   uint32_t theta = 0u;
-  int t_eq = 0;
+  int t_eq = 0, e_cnt = -1;
   if (mode == 2) {
     uint32_t lo = max(kmin, lb), hi = kmax;  // theta is in [lo, hi], rank take from the top
     int need = take;
     // 4096-fold narrowing: 32-bit keys need at most three passes (the cap
     // only bounds the loop).  Once the range holds at most kRowFew keys,
-    // one wave ranks them directly.
+    // they are ranked directly: wave w compares members 4w .. 4w+3 with
+    // every member, and the counts meet in LDS.
     int m = n_valid;
     for (int pass = 0; pass < 4 && lo != hi; ++pass) {
+      const uint32_t span = hi - lo;
       if (m <= kRowFew) {
 #pragma unroll
         for (int q = 0; q < EPT; ++q) {
           const uint32_t k = keys[q];
-          if (k >= lo && k <= hi) sh.mkeys[atomicAdd(&sh.mcount, 1u)] = k;
+          if (k - lo <= span) sh.mkeys[atomicAdd(&sh.mcount, 1u)] = k;
         }
         __syncthreads();
-        if (wave == 0) {
-          // lane l < m: keys above and at least its own among the m
-          const uint32_t mine = lane < m ? sh.mkeys[lane] : 0u;
-          int gt = 0, ge = 0;
-          for (int i = 0; i < m; ++i) {
-            const uint32_t ki = sh.mkeys[i];
-            gt += ki > mine;
-            ge += ki >= mine;
-          }
-          if (lane < m && gt < need && need <= ge) {  // every such lane holds the same key
+        const int mc = __builtin_amdgcn_readfirstlane((int)sh.mcount);
+        const uint32_t mine = sh.mkeys[lane];  // meaningful for lane < mc
+        const u32x4 k4 = *reinterpret_cast<const u32x4*>(&sh.mkeys[4 * wave]);
+        int gt = 0, ge = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bool in = 4 * wave + c < mc;
+          gt += in && k4[c] > mine;
+          ge += in && k4[c] >= mine;
+        }
+        if (lane < mc && ge > 0) {
+          if (gt > 0) atomicAdd(&sh.rk[lane][0], gt);
+          atomicAdd(&sh.rk[lane][1], ge);
+        }
+        __syncthreads();
+        if (wave == 0 && lane < mc) {
+          const int g_ = sh.rk[lane][0], e_ = sh.rk[lane][1];
+          if (g_ < need && need <= e_) {  // every such lane holds the same key
             sh.u[0] = mine;
-            sh.u[1] = (uint32_t)(need - gt);
+            sh.u[1] = (uint32_t)(need - g_);
+            sh.u[2] = (uint32_t)(e_ - g_);
           }
         }
         __syncthreads();
-        lo = hi = sh.u[0];
-        need = (int)sh.u[1];
+        lo = hi = __builtin_amdgcn_readfirstlane(sh.u[0]);
+        need = __builtin_amdgcn_readfirstlane((int)sh.u[1]);
+        e_cnt = __builtin_amdgcn_readfirstlane((int)sh.u[2]);
         break;
       }
-      const uint32_t span1 = hi - lo;
-      int sft = 0;
-      while ((span1 >> sft) >= (uint32_t)kRowBins) ++sft;
+      const int sft = max(0, 20 - (int)__builtin_clz(span | 1u));  // span >> sft < kRowBins
 #pragma unroll
       for (int q = 0; q < EPT; ++q) {
-        const uint32_t k = keys[q];
-        if (k >= lo && k <= hi) atomicAdd(&sh.h[(k - lo) >> sft], 1u);
+        const uint32_t d = keys[q] - lo;
+        if (d <= span) atomicAdd(&sh.h[d >> sft], 1u);
       }
       __syncthreads();
       uint32_t b;
       int ab;
       row_locate(sh, need, b, ab, m);
       lo += b << sft;
-      hi = (uint32_t)min((uint64_t)hi, (uint64_t)lo + ((1ull << sft) - 1));
+      const uint32_t wbin = (1u << sft) - 1u;
+      hi = hi - lo > wbin ? lo + wbin : hi;
       need -= ab;
+      if (lo == hi) e_cnt = m;  // the bin holds a single key value
     }
     theta = lo;
     t_eq = need;  // theta-ties to keep, in index order
   }
 
   // kept: key > theta (mode 1: every valid key), or one of the first t_eq
-  // theta-ties in index order.  Per-thread counts, then per wave.
-  int c_gt = 0, c_eq = 0;
+  // theta-ties in index order.  Per-wave counts from ballots.
+  const bool all_ties = mode == 1 || (mode == 2 && e_cnt == t_eq);
+  const uint32_t kmin_kept = mode == 1 ? 1u : theta;  // when every tie is kept
+  int c_gt = 0, c_eq = 0;  // uniform
+  if (all_ties) {
 #pragma unroll
-  for (int q = 0; q < EPT; ++q) {
-    c_gt += keys[q] > theta;
-    c_eq += mode == 2 && keys[q] == theta;
+    for (int q = 0; q < EPT; ++q) c_gt += (int)__popcll(__ballot(keys[q] >= kmin_kept));
+  } else if (mode == 2) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      c_gt += (int)__popcll(__ballot(keys[q] > theta));
+      c_eq += (int)__popcll(__ballot(keys[q] == theta));
+    }
   }
-  c_gt = wave_sum_i32(c_gt);
-  c_eq = wave_sum_i32(c_eq);
-  __syncthreads();  // sh.wi is reused
   if (lane == 0) {
-    sh.wi[wave][0] = c_gt;
-    sh.wi[wave][1] = c_eq;
+    sh.wc[wave][0] = c_gt;
+    sh.wc[wave][1] = c_eq;
   }
   __syncthreads();
   int o = 0, eseen = 0, e_total = 0;
 #pragma unroll
   for (int w = 0; w < kRowW; ++w) {
-    const int eq = sh.wi[w][1];
+    const int eq = sh.wc[w][1];
     if (w < wave) {
-      o += sh.wi[w][0] + max(0, min(eq, t_eq - eseen));
+      o += sh.wc[w][0] + max(0, min(eq, t_eq - eseen));
       eseen += eq;
     }
     e_total += eq;
   }
+  o = __builtin_amdgcn_readfirstlane(o);
+  eseen = __builtin_amdgcn_readfirstlane(eseen);
+  e_total = __builtin_amdgcn_readfirstlane(e_total);
+  const bool simple = all_ties || e_total <= t_eq;  // every kept key is >= kmin_kept
 
   // padding and count (only the last block can be partial)
   const int bs = a.block;
@@ -873,7 +998,7 @@ __global__ __launch_bounds__(kRowT) void row_select_kernel(SelectArgs a, Ws ws, 
     bool last_kept = false;
     if (mode != 0) {
       const uint32_t kl = s.key(n - 1);  // the highest-index block: a tie is kept iff all are
-      last_kept = mode == 1 ? kl != 0u : (kl > theta || (kl == theta && e_total <= t_eq));
+      last_kept = mode == 1 ? kl != 0u : (kl > theta || (kl == theta && simple));
     }
     const int pool_n = take * bs - (last_kept ? n * bs - ri.n_avail : 0);
     for (int i = pool_n + tid; i < a.max_blocks * bs; i += kRowT) out[i] = -1;
@@ -892,10 +1017,7 @@ __global__ __launch_bounds__(kRowT) void row_select_kernel(SelectArgs a, Ws ws, 
       out[rank] = s.position(j);
     }
   };
-  // Every theta-tie is kept (the usual case): one ballot per element.
-  // Otherwise the ties also need their rank among the row's ties.
-  const uint32_t kmin_kept = (mode == 2 && e_total <= t_eq) ? theta : theta + 1u;
-  if (mode == 1 || e_total <= t_eq) {
+  if (simple) {
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
       const bool keep = keys[q] >= kmin_kept;
@@ -905,6 +1027,7 @@ __global__ __launch_bounds__(kRowT) void row_select_kernel(SelectArgs a, Ws ws, 
     }
     return;
   }
+  // only some theta-ties are kept: they also need their rank among the ties
 #pragma unroll
   for (int q = 0; q < EPT; ++q) {
     const uint32_t k = keys[q];
