@@ -134,9 +134,10 @@ __device__ __forceinline__ float relu(float x) {
 // the key of +0 so the two tie.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // adding +0 turns -0 into +0 and keeps every other value (f32 denormals
+  // are not flushed); then negatives flip all bits, the rest the sign bit
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 // ---------------------------------------------------------------------------

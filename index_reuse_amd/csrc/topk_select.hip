@@ -81,6 +81,26 @@ __device__ __forceinline__ uint64_t lanes_below() {
   const int lane = threadIdx.x & 63;
   return lane ? (~0ull >> (64 - lane)) : 0ull;
 }
+// Lanes 0..15 (one DPP row) hold one value per wave of a 16-wave workgroup:
+// the row reduces on its own, and lane 0's result is made uniform.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, dpp<0x121>(v));
+  v = max(v, dpp<0x122>(v));
+  v = max(v, dpp<0x124>(v));
+  v = max(v, dpp<0x128>(v));
+  return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ uint32_t row16_min_u32(uint32_t v) {
+  return ~row16_max_u32(~v);
+}
+// inclusive prefix sum inside each 16-lane row
+__device__ __forceinline__ int row16_incl_scan(int x) {
+  x += dpp_z<0x111>(x);
+  x += dpp_z<0x112>(x);
+  x += dpp_z<0x114>(x);
+  x += dpp_z<0x118>(x);
+  return x;
+}
 
 // ------------------------------------------------------------------ layout
 constexpr int kL1Bits = 12;            // level-1 digit: key bits 31..20
@@ -738,9 +758,9 @@ __device__ __forceinline__ void row_locate(RowShared& sh, int rank, uint32_t& bi
   if (lane == 63) sh.wscan[wave] = incl;
   __syncthreads();
   *reinterpret_cast<u32x4*>(&sh.h[lo]) = u32x4{0u, 0u, 0u, 0u};
-  int above = incl - mine;
-#pragma unroll
-  for (int w = 0; w < kRowW - 1; ++w) above += w < wave ? sh.wscan[w] : 0;
+  static_assert(kRowW == 16, "one DPP row of wave totals");
+  const int wtot = row16_incl_scan(lane < kRowW ? sh.wscan[lane] : 0);
+  int above = incl - mine + (wave ? __builtin_amdgcn_readlane(wtot, wave - 1) : 0);
   if (above < rank && rank <= above + mine) {
     int acc = above, b = lo, at = above, cb = 0;
     bool found = false;
@@ -809,9 +829,12 @@ __global__ __launch_bounds__(kRowT) void row_select_kernel(SelectArgs a, Ws ws, 
       if (wn == 64 * EPT) {
 #pragma unroll
         for (int q = 0; q < EPT; ++q) keys[q] = order_key(x[q]);
-      } else {
+      } else {  // the row ends in this wave: a select per key, no branches
 #pragma unroll
-        for (int q = 0; q < EPT; ++q) keys[q] = 64 * q + lane < wn ? order_key(x[q]) : 0u;
+        for (int q = 0; q < EPT; ++q) {
+          const uint32_t k = order_key(x[q]);
+          keys[q] = lane < wn - 64 * q ? k : 0u;
+        }
       }
     } else if constexpr (EPT <= 32) {
       s.keys_c(jw, keys);
@@ -861,7 +884,7 @@ __global__ __launch_bounds__(kRowT) void row_select_kernel(SelectArgs a, Ws ws, 
 #pragma unroll
     for (int q = 0; q < EPT; ++q) nv += (int)__popcll(__ballot(keys[q] != 0u));
   }
-  kmin1 = ~wave_max_u32(~kmin1);
+  if (need_min) kmin1 = ~wave_max_u32(~kmin1);
   kmax = wave_max_u32(kmax);
   lb = ~wave_max_u32(~lb);
   if (lane == 0) {
@@ -871,18 +894,15 @@ __global__ __launch_bounds__(kRowT) void row_select_kernel(SelectArgs a, Ws ws, 
     sh.wscan[wave] = (int)lb;
   }
   __syncthreads();
-  int n_valid = 0;
-#pragma unroll
-  for (int w = 0; w < kRowW; ++w) {
-    n_valid += sh.wi[w][1];
-    kmin1 = min(kmin1, sh.wu[w][0]);
-    kmax = max(kmax, sh.wu[w][1]);
-    lb = min(lb, (uint32_t)sh.wscan[w]);
+  // lane w < 16 reads wave w's values; one DPP row combines them
+  const bool wl = lane < kRowW;
+  int n_valid = n;
+  if constexpr (!dense) {
+    n_valid = __builtin_amdgcn_readlane(row16_incl_scan(wl ? sh.wi[lane][1] : 0), kRowW - 1);
   }
-  n_valid = __builtin_amdgcn_readfirstlane(n_valid);
-  kmax = __builtin_amdgcn_readfirstlane(kmax);
-  lb = __builtin_amdgcn_readfirstlane(lb);
-  const uint32_t kmin = need_min ? __builtin_amdgcn_readfirstlane(kmin1) + 1u : lb;
+  kmax = row16_max_u32(wl ? sh.wu[lane][1] : 0u);
+  lb = row16_min_u32(wl ? (uint32_t)sh.wscan[lane] : 0xFFFFFFFFu);
+  const uint32_t kmin = need_min ? row16_min_u32(wl ? sh.wu[lane][0] : 0xFFFFFFFFu) + 1u : lb;
   const int take = min(kk, n_valid);
   const int mode = take == 0 ? 0 : (take == n_valid ? 1 : 2);
 
@@ -976,19 +996,22 @@ __global__ __launch_bounds__(kRowT) void row_select_kernel(SelectArgs a, Ws ws, 
     sh.wc[wave][1] = c_eq;
   }
   __syncthreads();
+  // lane w < 16 takes wave w: kept ties of wave w are the first of the
+  // t_eq - (ties in earlier waves) still to keep; offsets are the exclusive
+  // prefix of the kept counts
   int o = 0, eseen = 0, e_total = 0;
-#pragma unroll
-  for (int w = 0; w < kRowW; ++w) {
-    const int eq = sh.wc[w][1];
-    if (w < wave) {
-      o += sh.wc[w][0] + max(0, min(eq, t_eq - eseen));
-      eseen += eq;
-    }
-    e_total += eq;
+  if (all_ties) {
+    const int incl = row16_incl_scan(lane < kRowW ? sh.wc[lane][0] : 0);
+    o = wave ? __builtin_amdgcn_readlane(incl, wave - 1) : 0;
+  } else {
+    const int cg = lane < kRowW ? sh.wc[lane][0] : 0, ce = lane < kRowW ? sh.wc[lane][1] : 0;
+    const int e_incl = row16_incl_scan(ce);
+    const int kept = cg + max(0, min(ce, t_eq - (e_incl - ce)));
+    const int k_incl = row16_incl_scan(kept);
+    o = wave ? __builtin_amdgcn_readlane(k_incl, wave - 1) : 0;
+    eseen = wave ? __builtin_amdgcn_readlane(e_incl, wave - 1) : 0;
+    e_total = __builtin_amdgcn_readlane(e_incl, kRowW - 1);
   }
-  o = __builtin_amdgcn_readfirstlane(o);
-  eseen = __builtin_amdgcn_readfirstlane(eseen);
-  e_total = __builtin_amdgcn_readfirstlane(e_total);
   const bool simple = all_ties || e_total <= t_eq;  // every kept key is >= kmin_kept
 
   // padding and count (only the last block can be partial)
