@@ -171,14 +171,28 @@ __device__ __forceinline__ RangeTable build_range_table(const AttnArgs& a, int r
       const int sel = i0 == 0 ? sel_pre[j] : (idx ? idx[min(e, a.idx_stride - 1)] : -1);
       pos[j] = i < rt.ne ? (e < cnt ? sel : ri.win_lo + (e - cnt)) : -1;
     }
+    // block-table reads of the kPT entries, all issued before the first is
+    // used (entries without a position read page 0 of the row's table)
+    int pg[kPT], off[kPT];
+#pragma unroll
+    for (int j = 0; j < kPT; ++j) {
+      const int e = max(pos[j], 0);
+      pg[j] = a.k.page_shift >= 0 ? e >> a.k.page_shift : e / a.k.page_size;
+      off[j] = e - pg[j] * a.k.page_size;
+    }
+    const int64_t row_pages = (int64_t)max(ri.b, 0) * a.k.max_pages;
+    int64_t page[kPT];
+    if (a.k.block_table) {
+#pragma unroll
+      for (int j = 0; j < kPT; ++j) page[j] = a.k.block_table[row_pages + pg[j]];
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPT; ++j) page[j] = row_pages + pg[j];
+    }
 #pragma unroll
     for (int j = 0; j < kPT; ++j) {
       const int i = i0 + j * NTH + tid;
-      int slot = -1;
-      if (ri.b >= 0) {
-        const int sl = (int)cache_slot(a.k, ri.b, max(pos[j], 0));
-        slot = pos[j] >= 0 ? sl : -1;
-      }
+      const int slot = (ri.b >= 0 && pos[j] >= 0) ? (int)(page[j] * a.k.page_size + off[j]) : -1;
       if (i < n_tab) slot_tab[i] = slot;
       // the wave's lowest entry with a slot
       const uint64_t has = __builtin_amdgcn_ballot_w64(slot >= 0);
@@ -218,27 +232,30 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
   const int qrow0 = (blockIdx.z * W + wq) * 16;
   const bool active = qrow0 < Mq;
 
-  // Query rows of this wave as the B operand (query row = col); issued first,
-  // they depend on nothing else.
-  u32x4 qv[QV];
-  {
-    const int qr = qrow0 + col;
-    if (active && qr < Mq) {
-      const int set = qr / G, h = g * G + qr % G;
-      const u32x4* qp = reinterpret_cast<const u32x4*>(
-          reinterpret_cast<const uint16_t*>(a.q) +
-          (((int64_t)set * a.rows.n_rows + r) * a.hq + h) * DQK + gq * (DQK / 4));
-#pragma unroll
-      for (int i = 0; i < QV; ++i) qv[i] = qp[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < QV; ++i) qv[i] = u32x4{0, 0, 0, 0};
-    }
-  }
-
+  // The row's first indices, then the query rows of this wave as the B
+  // operand (query row = col).  Loads complete in issue order, so the range
+  // table, which needs the indices, does not wait for the queries.
   int sel_pre[kPT];
   issue_index_loads<NTH>(a, r, sp * per_split, sel_pre);
-  const RowInfo ri = row_info(a.rows, r);
+  const RowInfo ri = row_info(a.rows, r);  // scalar loads, before any divergent code
+  u32x4 qv[QV];
+  {
+    // unconditional loads (a row past the end reads row 0 and is zeroed), so
+    // the wait for the indices below does not have to cover them
+    const bool ok = active && qrow0 + col < Mq;
+    const int qr = ok ? qrow0 + col : 0;
+    const int set = qr / G, h = g * G + qr % G;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const uint16_t*>(a.q) +
+        (((int64_t)set * a.rows.n_rows + r) * a.hq + h) * DQK + gq * (DQK / 4));
+#pragma unroll
+    for (int i = 0; i < QV; ++i) qv[i] = qp[i];
+#pragma unroll
+    for (int i = 0; i < QV; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qv[i][c] = ok ? qv[i][c] : 0u;
+  }
+
   const RangeTable rt = build_range_table<NTH, NG, D>(a, r, sp * per_split, per_split, ri, sel_pre,
                                                       lds.slot, lds.wfirst);
   const int ne = rt.ne, nsteps = rt.nsteps, nsteps_run = rt.nsteps_run;
