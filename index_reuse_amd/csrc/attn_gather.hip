@@ -125,12 +125,19 @@ struct TileRegs {
 // sequence length; they are issued before anything else.
 constexpr int kPT = 4;  // table entries per thread per pass
 
+// Range order: the window entries first, then the selected ones, so a row's
+// first step can be gathered before its indices are read.  Table entry i
+// (entry e = e0 + i) is window position win_lo + e for e < n_w, else the
+// selected index idx[e - n_w].  The first pass of index loads assumes n_w
+// equals the window parameter (every row with at least that many visible
+// entries) and is redone when it does not.
 template <int NTH>
 __device__ __forceinline__ void issue_index_loads(const AttnArgs& a, int r, int e0, int (&sel_pre)[kPT]) {
   const int32_t* idx = a.idx ? a.idx + (int64_t)r * a.idx_stride : nullptr;
 #pragma unroll
   for (int j = 0; j < kPT; ++j)
-    sel_pre[j] = idx ? idx[min(e0 + j * NTH + (int)threadIdx.x, a.idx_stride - 1)] : -1;
+    sel_pre[j] = idx ? idx[min(max(e0 + j * NTH + (int)threadIdx.x - a.rows.window, 0), a.idx_stride - 1)]
+                     : -1;
 }
 
 struct RangeTable {
@@ -138,38 +145,51 @@ struct RangeTable {
   int nsteps;      // steps of NG tiles covering them
   int nsteps_run;  // nsteps, or 0 when no entry of the range has a slot
   uint32_t dummy;  // slot read by padding entries
+  int n_w;         // window entries of the row
+  int n_tab;       // table entries (steps plus the D read ahead)
 };
 
-// Cache slot of every entry of the range, once, through the block table,
-// into slot[] (LDS).  Padding to whole steps, and the D steps past the end
-// that a prefetch ring reads, are -1.  Loads are clamped rather than guarded
-// so that a thread's loads all issue before the first wait.  Padding entries
-// later read the rows of the range's first real entry: finite data that the
-// mask gives weight exactly 0.  Ends with a barrier.
-template <int NTH, int NG, int D>
-__device__ __forceinline__ RangeTable build_range_table(const AttnArgs& a, int r, int e0, int per_split,
-                                                        const RowInfo& ri, const int (&sel_pre)[kPT],
-                                                        int32_t* slot_tab, int32_t* wfirst_tab) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t* idx = a.idx ? a.idx + (int64_t)r * a.idx_stride : nullptr;
-  const int n_w = ri.n_avail - ri.win_lo;
-  const int cnt = (idx && ri.b >= 0) ? a.count[r] : 0;
-  const int n_e = ri.b < 0 ? 0 : n_w + cnt;
-  const int e1 = min(n_e, e0 + per_split);
+template <int NG, int D>
+__device__ __forceinline__ RangeTable range_header(const AttnArgs& a, int r, int e0, int per_split,
+                                                   const RowInfo& ri) {
   RangeTable rt;
+  rt.n_w = ri.n_avail - ri.win_lo;
+  const int cnt = (a.idx && ri.b >= 0) ? a.count[r] : 0;
+  const int n_e = ri.b < 0 ? 0 : rt.n_w + cnt;
+  const int e1 = min(n_e, e0 + per_split);
   rt.ne = max(0, e1 - e0);
   const int ntiles = (rt.ne + kTile - 1) / kTile;
   rt.nsteps = (ntiles + NG - 1) / NG;
+  rt.n_tab = (rt.nsteps + D) * NG * kTile;
+  rt.nsteps_run = 0;
+  rt.dummy = 0u;
+  return rt;
+}
+
+// Cache slot of every entry of the range, once, through the block table,
+// into slot[] (LDS), entries from `from` on.  Padding to whole steps, and the
+// D steps past the end that a prefetch ring reads, are -1.  Loads are
+// clamped rather than guarded so that a thread's loads all issue before the
+// first wait.  Padding entries later read the rows of the range's first real
+// entry: finite data that the mask gives weight exactly 0 (with from > 0 the
+// caller has set rt.dummy and rt.nsteps_run already).  Ends with a barrier.
+template <int NTH>
+__device__ __forceinline__ void fill_range_table(const AttnArgs& a, int r, int e0, const RowInfo& ri,
+                                                 RangeTable& rt, const int (&sel_pre)[kPT], int from,
+                                                 int32_t* slot_tab, int32_t* wfirst_tab) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t* idx = a.idx ? a.idx + (int64_t)r * a.idx_stride : nullptr;
+  const bool pre_ok = rt.n_w == a.rows.window;
   int wfirst = 0x7FFFFFFF;
-  const int n_tab = (rt.nsteps + D) * NG * kTile;
-  for (int i0 = 0; i0 < n_tab; i0 += kPT * NTH) {
+  for (int i0 = 0; i0 < rt.n_tab; i0 += kPT * NTH) {
     int pos[kPT];
 #pragma unroll
     for (int j = 0; j < kPT; ++j) {
       const int i = i0 + j * NTH + tid;
       const int e = e0 + i;
-      const int sel = i0 == 0 ? sel_pre[j] : (idx ? idx[min(e, a.idx_stride - 1)] : -1);
-      pos[j] = i < rt.ne ? (e < cnt ? sel : ri.win_lo + (e - cnt)) : -1;
+      const int sel = (i0 == 0 && pre_ok) ? sel_pre[j]
+                                          : (idx ? idx[min(max(e - rt.n_w, 0), a.idx_stride - 1)] : -1);
+      pos[j] = i < rt.ne ? (e < rt.n_w ? ri.win_lo + e : sel) : -1;
     }
     // block-table reads of the kPT entries, all issued before the first is
     // used (entries without a position read page 0 of the row's table)
@@ -193,11 +213,15 @@ __device__ __forceinline__ RangeTable build_range_table(const AttnArgs& a, int r
     for (int j = 0; j < kPT; ++j) {
       const int i = i0 + j * NTH + tid;
       const int slot = (ri.b >= 0 && pos[j] >= 0) ? (int)(page[j] * a.k.page_size + off[j]) : -1;
-      if (i < n_tab) slot_tab[i] = slot;
+      if (i >= from && i < rt.n_tab) slot_tab[i] = slot;
       // the wave's lowest entry with a slot
       const uint64_t has = __builtin_amdgcn_ballot_w64(slot >= 0);
       if (has) wfirst = min(wfirst, i0 + j * NTH + (tid & ~63) + (int)__builtin_ctzll(has));
     }
+  }
+  if (from > 0) {
+    __syncthreads();
+    return;
   }
   if (lane == 0) wfirst_tab[wave] = wfirst;
   __syncthreads();
@@ -206,7 +230,40 @@ __device__ __forceinline__ RangeTable build_range_table(const AttnArgs& a, int r
   for (int w = 0; w < NTH / 64; ++w) first = min(first, wfirst_tab[w]);
   rt.nsteps_run = first < rt.ne ? rt.nsteps : 0;
   rt.dummy = first < rt.ne ? (uint32_t)slot_tab[first] : 0u;
+}
+
+template <int NTH, int NG, int D>
+__device__ __forceinline__ RangeTable build_range_table(const AttnArgs& a, int r, int e0, int per_split,
+                                                        const RowInfo& ri, const int (&sel_pre)[kPT],
+                                                        int32_t* slot_tab, int32_t* wfirst_tab) {
+  RangeTable rt = range_header<NG, D>(a, r, e0, per_split, ri);
+  fill_range_table<NTH>(a, r, e0, ri, rt, sel_pre, 0, slot_tab, wfirst_tab);
   return rt;
+}
+
+// The first step of a range that starts with at least a step of window
+// entries, from scalar block-table reads only (a step of 32 NG entries spans
+// at most three pages of 64 or more): its rows can be gathered while the
+// indices and their pages are still on the way.  Ends with a barrier.
+template <int NTH, int NG>
+__device__ __forceinline__ void fill_window_step(const AttnArgs& a, const RowInfo& ri, int32_t* slot_tab) {
+  static_assert(NTH >= NG * kTile, "one entry per thread");
+  const int pf = ri.win_lo >> a.k.page_shift;
+  const int64_t row_pages = (int64_t)ri.b * a.k.max_pages;
+  int64_t pgs[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int pk = min(pf + k, a.k.max_pages - 1);
+    pgs[k] = a.k.block_table ? (int64_t)a.k.block_table[row_pages + pk] : row_pages + pk;
+  }
+  const int tid = threadIdx.x;
+  if (tid < NG * kTile) {
+    const int pos = ri.win_lo + tid;
+    const int k = (pos >> a.k.page_shift) - pf;
+    const int64_t page = k == 0 ? pgs[0] : (k == 1 ? pgs[1] : pgs[2]);
+    slot_tab[tid] = (int)(page * a.k.page_size + (pos & (a.k.page_size - 1)));
+  }
+  __syncthreads();
 }
 
 template <int DQK, int DV, int KV, int W, int NG, int D>
@@ -256,8 +313,19 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
       for (int c = 0; c < 4; ++c) qv[i][c] = ok ? qv[i][c] : 0u;
   }
 
-  const RangeTable rt = build_range_table<NTH, NG, D>(a, r, sp * per_split, per_split, ri, sel_pre,
-                                                      lds.slot, lds.wfirst);
+  // A range that opens with a whole step of window entries (decode rows
+  // with a window) gathers that step before the selected entries' table is
+  // built; otherwise the whole table comes first.
+  RangeTable rt = range_header<NG, D>(a, r, sp * per_split, per_split, ri);
+  const bool early =
+      sp == 0 && ri.b >= 0 && rt.n_w >= NG * kTile && rt.ne >= NG * kTile && a.k.page_shift >= 6;
+  if (early) {
+    fill_window_step<NTH, NG>(a, ri, lds.slot);
+    rt.dummy = (uint32_t)lds.slot[0];
+    rt.nsteps_run = rt.nsteps;
+  } else {
+    fill_range_table<NTH>(a, r, sp * per_split, ri, rt, sel_pre, 0, lds.slot, lds.wfirst);
+  }
   const int ne = rt.ne, nsteps = rt.nsteps, nsteps_run = rt.nsteps_run;
   const uint32_t dummy = rt.dummy;
 
@@ -422,11 +490,18 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
   // of each unrolled step is static); the last partial group is guarded.
   static_assert(D == 1 || D % 2 == 0, "prefetch depth must be 1 or even");
   T ring[D];
+  if (early) {
+    // step 0 (window rows) is on its way while the rest of the table is
+    // built; the steps after it wait for the table
+    load_step(0, ring[0]);
+    fill_range_table<NTH>(a, r, sp * per_split, ri, rt, sel_pre, NG * kTile, lds.slot, lds.wfirst);
+  }
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < D; ++u) load_step(u, ring[u]);
+    for (int u = 0; u < D; ++u)
+      if (u > 0 || pass > 0 || !early) load_step(u, ring[u]);
     int s0 = 0;
     for (; s0 + D <= nsteps_run; s0 += D) {
 #pragma unroll
