@@ -77,28 +77,28 @@ __device__ __forceinline__ f32x4 mfma_slice(const LaneSlice<DIM, true>& a,
   return acc;
 }
 
-// acc[t][mt] += Q[mt] . K[t] for the four key tiles of a group, k-step
+// acc[t][mt] += Q[mt] . K[t] for NT key tiles, k-step
 // outermost so the 4*NMT accumulator chains interleave.
-template <int NMT, int DIM>
+template <int NMT, int DIM, int NT>
 __device__ __forceinline__ void mfma_tiles(const LaneSlice<DIM, false> (&q)[NMT],
-                                           const LaneSlice<DIM, false> (&k)[4], f32x4 (&acc)[4][NMT]) {
+                                           const LaneSlice<DIM, false> (&k)[NT], f32x4 (&acc)[NT][NMT]) {
 #pragma unroll
   for (int ks = 0; ks < LaneSlice<DIM, false>::KS; ++ks)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
         acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             __builtin_bit_cast(bf16x8, q[mt].v[ks]), __builtin_bit_cast(bf16x8, k[t].v[ks]),
             acc[t][mt], 0, 0, 0);
 }
-template <int NMT, int DIM>
+template <int NMT, int DIM, int NT>
 __device__ __forceinline__ void mfma_tiles(const LaneSlice<DIM, true> (&q)[NMT],
-                                           const LaneSlice<DIM, true> (&k)[4], f32x4 (&acc)[4][NMT]) {
+                                           const LaneSlice<DIM, true> (&k)[NT], f32x4 (&acc)[NT][NMT]) {
 #pragma unroll
   for (int ks = 0; ks < LaneSlice<DIM, true>::KS; ++ks)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) {
         const uint32_t* pa = reinterpret_cast<const uint32_t*>(&q[mt].v[0]) + 2 * ks;
@@ -143,19 +143,20 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
   const int ngrp = min(gpw, (n_slots - wbase + 63) / 64);  // groups of this wave
   if (ngrp <= 0) return;
 
-  // Without a candidate list, a group's 64 slots are consecutive; when a
-  // paged cache's pages hold whole groups, the group lies in one page.  The
-  // pages of all the wave's groups are read up front with one vector load
-  // (lane i: group i's page, ngrp <= 16), before any key load, and each
-  // group takes its page with a lane read: no table load waits in the loop.
-  // Slots past the row stay inside that page.
-  const bool page_per_group =
-      !cand_mode && a.k.block_table != nullptr && a.k.page_shift >= 6;
+  // Without a candidate list, a group's 64 slots are consecutive; when the
+  // cache's pages (a contiguous cache: one page per sequence) hold whole
+  // groups, the group lies in one page.  The pages of all the wave's groups
+  // are read up front with one vector load (lane i: group i's page, ngrp <=
+  // 16), before any key load, and each group takes its page with a lane
+  // read: no table load waits in the loop.  Slots past the row stay inside
+  // that page.
+  const bool page_per_group = !cand_mode && a.k.page_shift >= 6;
   const int wbase_u = __builtin_amdgcn_readfirstlane(wbase);
   int pg_lane = 0;
   if (page_per_group) {
     const int gl = lane < ngrp ? lane : 0;
-    pg_lane = a.k.block_table[(int64_t)ri.b * a.k.max_pages + ((wbase_u + 64 * gl) >> a.k.page_shift)];
+    const int64_t lp = (int64_t)ri.b * a.k.max_pages + ((wbase_u + 64 * gl) >> a.k.page_shift);
+    pg_lane = a.k.block_table ? a.k.block_table[lp] : (int)lp;
   }
   auto load_group = [&](int gi, Group<DIM, FP8>& G) {
 #pragma unroll
@@ -180,29 +181,33 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
       }
     }
   };
-  // Rows of 128 bytes stored back to back (one page holds the group as 8 KB
-  // of contiguous memory): load each group as eight 1 KB wave-contiguous
+  // Rows stored back to back (one page holds the group as 64 contiguous
+  // rows): load the group in 8 KB units, each as eight 1 KB wave-contiguous
   // pieces (whole cache lines per instruction; the MFMA lane layout would
-  // read sixteen half lines per instruction, about 15% slower from HBM) and
-  // reshape it through a wave-private LDS tile (rows padded to 144 bytes:
-  // the MFMA-layout reads are then free of bank conflicts).
-  // (STAGED: the host checked every condition: pages of whole groups,
-  // 128-byte rows back to back, no candidate list)
+  // read sixteen half lines per instruction, about 15% slower from HBM), and
+  // reshape each unit through a wave-private LDS tile (rows padded by 16
+  // bytes: the MFMA-layout reads are then free of bank conflicts).
+  // (STAGED: the host checked every condition: pages of whole groups, rows
+  // of 128 or 256 bytes back to back, no candidate list)
   constexpr int ROWB = DIM * ElemTraits<FP8>::bytes;
-  static_assert(!STAGED || ROWB == 128, "staged groups are 64 rows of 128 bytes");
+  static_assert(!STAGED || ROWB == 128 || ROWB == 256, "staged rows are 128 or 256 bytes");
   constexpr bool staged = STAGED;
+  constexpr int UNITS = ROWB >= 128 ? ROWB / 128 : 1;  // 8 KB units per group
+  constexpr int RU = 64 / UNITS;     // rows per unit
+  constexpr int PPR = ROWB / 16;     // 16-byte pieces per row
+  constexpr int TPU = 4 / UNITS;     // MFMA tiles per unit
   u32x4 raw[8];
-  auto load_raw = [&](int gi) {
+  auto load_raw = [&](int gi, int un) {
     const int s0 = wbase_u + 64 * gi;
     const int64_t page = __builtin_amdgcn_readlane(pg_lane, gi);
     const u32x4* gb = reinterpret_cast<const u32x4*>(
-        a.k.data + (page * a.k.page_size + (s0 & (a.k.page_size - 1))) * (int64_t)ROWB);
+        a.k.data + (page * a.k.page_size + (s0 & (a.k.page_size - 1))) * (int64_t)ROWB + 8192 * un);
 #pragma unroll
     for (int u = 0; u < 8; ++u) raw[u] = __builtin_nontemporal_load(gb + 64 * u + lane);
   };
   Group<DIM, FP8> buf[2];
   if constexpr (staged)
-    load_raw(0);
+    load_raw(0, 0);
   else
     load_group(0, buf[0]);
 
@@ -227,14 +232,8 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
 
   // The four tiles' MFMA chains and epilogues are independent: interleave
   // them (k-step outermost) so the chains overlap.
-  auto score_group = [&](int gi, const Group<DIM, FP8>& G) {
+  auto epilogue = [&](int gi, const f32x4 (&acc)[4][NMT], const int (&pos)[4]) {
     const int base = wbase + 64 * gi;
-    f32x4 acc[4][NMT];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mfma_tiles<NMT, DIM>(qs, G.ks, acc);
     float res[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -251,27 +250,54 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
     // would put the whole group in scratch memory)
     unsigned vb = 0;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) vb |= (unsigned)(G.pos[t] >= 0 && G.pos[t] < ri.n_avail) << t;
+    for (int t = 0; t < 4; ++t) vb |= (unsigned)(pos[t] >= 0 && pos[t] < ri.n_avail) << t;
     if (base + lane < n_slots) out[base + lane] = (vb >> g) & 1u ? sum : -__builtin_huge_valf();
+  };
+  auto score_group = [&](int gi, const Group<DIM, FP8>& G) {
+    f32x4 acc[4][NMT];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mfma_tiles<NMT, DIM, 4>(qs, G.ks, acc);
+    epilogue(gi, acc, G.pos);
   };
 
   if constexpr (staged) {
-    {
-      __shared__ u32x4 stage[kWaves][64][9];
-      u32x4(&tile)[64][9] = stage[wave];
-      for (int gi = 0; gi < ngrp; ++gi) {
+    __shared__ u32x4 stage[kWaves][RU][PPR + 1];
+    u32x4(&tile)[RU][PPR + 1] = stage[wave];
+    for (int gi = 0; gi < ngrp; ++gi) {
+      f32x4 acc[4][NMT];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) tile[8 * u + (lane >> 3)][lane & 7] = raw[u];
-        if (gi + 1 < ngrp) load_raw(gi + 1);
-        Group<DIM, FP8> G;
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          G.pos[t] = wbase + 64 * gi + 16 * t + col;
+        for (int mt = 0; mt < NMT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < LaneSlice<DIM, FP8>::VEC; ++i) G.ks[t].v[i] = tile[16 * t + col][4 * i + g];
-        }
-        score_group(gi, G);
+      for (int un = 0; un < UNITS; ++un) {
+        // The tile passes rows between lanes of the wave: LDS runs a wave's
+        // accesses in order, so only the compiler must keep them in program
+        // order (it would otherwise move the reads above the other lanes'
+        // writes, or the next unit's writes above these reads).
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int u = 0; u < 8; ++u) tile[(64 * u + lane) / PPR][(64 * u + lane) % PPR] = raw[u];
+        asm volatile("" ::: "memory");
+        if (un + 1 < UNITS)
+          load_raw(gi, un + 1);
+        else if (gi + 1 < ngrp)
+          load_raw(gi + 1, 0);
+        LaneSlice<DIM, FP8> ks[TPU];
+#pragma unroll
+        for (int tl = 0; tl < TPU; ++tl)
+#pragma unroll
+          for (int i = 0; i < LaneSlice<DIM, FP8>::VEC; ++i) ks[tl].v[i] = tile[16 * tl + col][4 * i + g];
+        asm volatile("" ::: "memory");
+        mfma_tiles<NMT, DIM, TPU>(qs, ks, *reinterpret_cast<f32x4(*)[TPU][NMT]>(&acc[un * TPU]));
       }
+      int pos[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) pos[t] = wbase + 64 * gi + 16 * t + col;
+      epilogue(gi, acc, pos);
     }
   } else {
     // two groups per iteration so the buffer index stays static
@@ -486,9 +512,9 @@ hipError_t launch_mfma(const IndexArgs& a, hipStream_t s) {
   int gpw = 2;
   while (gpw < 16 && (int64_t)((groups + 2 * gpw - 1) / (2 * gpw)) * a.rows.n_rows >= 1024) gpw *= 2;
   dim3 grid((groups + gpw - 1) / gpw, a.rows.n_rows);
-  constexpr bool stageable = DIM * (FP8 ? 1 : 2) == 128;
-  const bool staged = stageable && a.cand == nullptr && a.k.block_table != nullptr &&
-                      a.k.page_shift >= 6 && a.k.row_stride == 128;
+  constexpr int rowb = DIM * (FP8 ? 1 : 2);
+  constexpr bool stageable = rowb == 128 || rowb == 256;
+  const bool staged = stageable && a.cand == nullptr && a.k.page_shift >= 6 && a.k.row_stride == rowb;
   if (staged)
     hipLaunchKernelGGL((index_score_mfma<NMT, DIM, FP8, stageable>), grid, dim3(64 * kWaves), 0, s, a, gpw);
   else
