@@ -119,10 +119,7 @@ struct TileRegs {
 };
 
 // ------------------------------------------------------ entry range table
-// A workgroup serves entries [e0, e0 + per_split) of its row, in this order:
-// the selected ones (idx[0 .. count)), then the window.  Selected entries
-// come first so that their index loads depend only on the row, not on the
-// sequence length; they are issued before anything else.
+// A workgroup serves entries [e0, e0 + per_split) of its row.
 constexpr int kPT = 4;  // table entries per thread per pass
 
 // Range order: the window entries first, then the selected ones, so a row's
