@@ -129,6 +129,65 @@ def test_attention_given_oracle_indices(name, dev):
                         what="%s call %d" % (name, c))
 
 
+# Decode-indexer layouts: groups of 64 entries in pages of 64, 128 or 256
+# (at offsets inside a page), pages of 32 (per-tile page reads), 128- and
+# 256-byte bf16 rows, FP8 rows, and contiguous caches; ragged lengths.
+INDEX_LAYOUTS = {
+    "bf16_d64_page128": dict(page_size=128),
+    "bf16_d128_page256": dict(idx_dim=128, idx_heads=32, page_size=256),
+    "bf16_d64_page32": dict(page_size=32),
+    "fp8_d128_h64_page64": dict(idx_dtype=torch.float8_e4m3fn, idx_dim=128, idx_heads=64),
+    "bf16_d64_contiguous": dict(page_size=0),
+}
+
+
+@pytest.mark.parametrize("layout", list(INDEX_LAYOUTS))
+@pytest.mark.parametrize("integer", [True, False])
+def test_decode_indexer_layouts(layout, integer, dev):
+    wl = synth.HYSPARSE2.replace(n_seqs=4, seq_lens_override=(3000, 1151, 130, 2049),
+                                 **INDEX_LAYOUTS[layout])
+    prob = synth.make_problem(wl, device="cpu", integer=integer)
+    _flush("case %s integer=%s" % (layout, integer))
+    p, step = _step(prob, dev)
+    step.run_index()
+    torch.cuda.synchronize()
+    sc = H.oracle_scores(prob, 0)
+    g = step.scores[0].cpu().double().numpy()
+    valid = ~np.isnan(sc)
+    if integer:
+        assert np.array_equal(g[valid], sc[valid])
+    else:
+        tau = H.fp32_score_bound(prob, 0)
+        err = np.abs(g - np.nan_to_num(sc))
+        assert np.all(err[valid] <= np.broadcast_to(tau[:, None], sc.shape)[valid])
+
+
+# Window-first attention ranges: a window that is not a whole number of
+# steps (rows with fewer visible entries than the window, between one step
+# and the window, and longer), and a single row, which the launch splits
+# over many workgroups (only the first split opens with the window step).
+WINDOW_CASES = {
+    "window200": dict(window=200, n_seqs=4, seq_lens_override=(3000, 150, 90, 1500)),
+    "single_row_split": dict(n_seqs=1, seq_lens_override=(5000,)),
+}
+
+
+@pytest.mark.parametrize("case", list(WINDOW_CASES))
+def test_attention_window_ranges(case, dev):
+    wl = synth.HYSPARSE2.replace(**WINDOW_CASES[case])
+    prob = synth.make_problem(wl, device="cpu")
+    _flush("case %s" % case)
+    p, step = _step(prob, dev)
+    sc = H.oracle_scores(prob, 0)
+    idx, cnt = H.oracle_select(prob, sc, wl.k)
+    step.run_attention(idx=[torch.from_numpy(idx).to(dev)], count=[torch.from_numpy(cnt).to(dev)])
+    torch.cuda.synchronize()
+    for c in range(len(prob.q)):
+        o_ref, l_ref = H.oracle_attention(prob, c, idx, cnt)
+        H.check_outputs(step.o[c], o_ref, step.lse[c], l_ref, wl.attn_dtype,
+                        what="%s call %d" % (case, c))
+
+
 ATTN_SHAPES = {
     # 10 query sets x 8 heads per KV head: 80 rows, two row groups per KV head
     "sep128_q10": dict(n_qsets=10),
