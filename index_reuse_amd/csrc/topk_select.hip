@@ -273,8 +273,16 @@ __global__ __launch_bounds__(256) void block_max_kernel(SelectArgs a, Ws ws) {
   if (j >= nb) return;
   const float* sc = a.scores + (int64_t)r * a.score_stride;
   const int lo = j * a.block, hi = min(lo + a.block, ri.n_avail);
-  float m = sc[lo];
-  for (int s = lo + 1; s < hi; ++s) m = fmaxf(m, sc[s]);
+  float m;
+  if (a.block == 8 && hi - lo == 8 && (reinterpret_cast<uintptr_t>(sc + lo) & 15) == 0) {
+    // a whole block of 8 as two 16-byte loads
+    const f32x4 u = reinterpret_cast<const f32x4*>(sc + lo)[0];
+    const f32x4 v = reinterpret_cast<const f32x4*>(sc + lo)[1];
+    m = fmaxf(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])), fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+  } else {
+    m = sc[lo];
+    for (int s = lo + 1; s < hi; ++s) m = fmaxf(m, sc[s]);
+  }
   ws.beta[(int64_t)r * a.beta_stride + j] = m;
 }
 
@@ -1032,10 +1040,18 @@ __global__ __launch_bounds__(kRowT) void row_select_kernel(SelectArgs a, Ws ws, 
   }
   if (mode == 0) return;
 
+  // pool rows of whole 8-entry blocks go out as two 16-byte stores
+  const bool vec8 = pool_mode && bs == 8 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
   auto put = [&](int j, int rank) {
     if constexpr (pool_mode) {
       const int lo = j * bs, mm = min(bs, ri.n_avail - lo);
-      for (int u = 0; u < mm; ++u) out[rank * bs + u] = lo + u;
+      if (vec8 && mm == 8) {
+        int32_t* o8 = out + rank * 8;
+        reinterpret_cast<i32x4*>(o8)[0] = i32x4{lo, lo + 1, lo + 2, lo + 3};
+        reinterpret_cast<i32x4*>(o8)[1] = i32x4{lo + 4, lo + 5, lo + 6, lo + 7};
+      } else {
+        for (int u = 0; u < mm; ++u) out[rank * bs + u] = lo + u;
+      }
     } else {
       out[rank] = s.position(j);
     }
