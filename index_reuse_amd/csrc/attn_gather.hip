@@ -505,8 +505,10 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
       for (int u = 0; u < D; ++u) {
         const int sb = D % 2 == 0 ? (u & 1) : ((s0 + u) & 1);
         store_step(ring[u], sb);
-        __syncthreads();
+        // the next loads go out before the barrier: the stores above have
+        // read these registers, and the slot table does not change
         load_step(s0 + u + D, ring[u]);
+        __syncthreads();
         if (active) compute(sb * NG + grp, (s0 + u) * NG + grp);
       }
     }
