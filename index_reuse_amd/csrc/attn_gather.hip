@@ -1166,8 +1166,10 @@ void attn_plan(AttnArgs& a) {
   const int max_split = (a.max_entries + kTile - 1) / kTile;
   // enough entry ranges to occupy the chip, each within the slot table
   int ns = (a.max_entries + kMaxEntries - 1) / kMaxEntries;
-  // wide value rows make split partials expensive: stop earlier
-  const int cap = a.dv >= 512 ? 4 : max_split;
+  // wide value rows make split partials expensive: stop at about 64
+  // workgroups, but take at least 4 splits (measured on 8 and 16 rows of 64
+  // heads over 512 entries)
+  const int cap = a.dv >= 512 ? (int)max((int64_t)4, (64 + base - 1) / base) : max_split;
   while (ns < max_split && ns < cap && base * ns < 256) ++ns;
   a.n_split = ns < 1 ? 1 : ns;
 }
