@@ -983,24 +983,35 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   if (row >= nrows) return;
   const int DV = a.dv, ns = a.n_split;
   const float* ml = a.part + (int64_t)ns * nrows * DV;
-  float m = -__builtin_huge_valf(), l = 0.0f, lx = 0.0f;
-  if (lane < ns) {
-    m = ml[((int64_t)lane * nrows + row) * 3];
-    l = ml[((int64_t)lane * nrows + row) * 3 + 1];
-    lx = ml[((int64_t)lane * nrows + row) * 3 + 2];
+  // Up to 8 splits of 512 channels: every partial load is issued before the
+  // split weights are known (one memory round trip instead of two).  Splits
+  // past ns re-read split 0 and get weight 0.
+  constexpr int kS = 8;
+  const bool pre = ns <= kS && DV == 512;
+  f32x4 v[kS][2];
+  if (pre) {
+#pragma unroll
+    for (int sp = 0; sp < kS; ++sp)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        v[sp][h] = *reinterpret_cast<const f32x4*>(
+            a.part + ((int64_t)(sp < ns ? sp : 0) * nrows + row) * DV + 4 * lane + 256 * h);
+  }
+  // lanes past ns read split 0's statistics (unconditional loads) and drop them
+  const int sl = lane < ns ? lane : 0;
+  float m = ml[((int64_t)sl * nrows + row) * 3];
+  float l = ml[((int64_t)sl * nrows + row) * 3 + 1];
+  float lx = ml[((int64_t)sl * nrows + row) * 3 + 2];
+  if (lane >= ns) {
+    m = -__builtin_huge_valf();
+    l = 0.0f;
+    lx = 0.0f;
   }
   const float M = wave_max(m);
   const float f = (l > 0.0f && M != -__builtin_huge_valf()) ? exp2f(m - M) : 0.0f;
   const float L = wave_sum(f * l), Lx = wave_sum(f * lx);
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  for (int c0 = 4 * lane; c0 < DV; c0 += 256) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int sp = 0; sp < ns; ++sp) {
-      const float fs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), sp));
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.part + ((int64_t)sp * nrows + row) * DV + c0);
-      acc += fs * v;
-    }
+  auto put = [&](f32x4 acc, int c0) {
     acc *= inv;
     if (a.o_dtype == 1) {
       uint2 pk;
@@ -1010,6 +1021,28 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
     } else {
       *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + row * DV + c0) = acc;
     }
+  };
+  if (pre) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sp = 0; sp < kS; ++sp) {
+        const float fs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), sp));
+        acc += fs * v[sp][h];
+      }
+      put(acc, 4 * lane + 256 * h);
+    }
+  }
+  for (int c0 = 4 * lane; !pre && c0 < DV; c0 += 256) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int sp = 0; sp < ns; ++sp) {
+      const float fs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), sp));
+      const f32x4 w = *reinterpret_cast<const f32x4*>(a.part + ((int64_t)sp * nrows + row) * DV + c0);
+      acc += fs * w;
+    }
+    put(acc, c0);
   }
   if (a.lse && lane == 0)
     a.lse[row] = Lx > 0.0f ? (M + __log2f(Lx)) * 0.6931471805599453f : -__builtin_huge_valf();
