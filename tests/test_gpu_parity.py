@@ -578,3 +578,140 @@ def test_padding_rows_and_empty(dev):
     idx, c = H.oracle_select(prob, sc, wl.k)
     o_ref, l_ref = H.oracle_attention(prob, 0, idx, c)
     H.check_outputs(step.o[0], o_ref, step.lse[0], l_ref, torch.bfloat16, what="padding")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, drawn with the benchmark's seeds (its first input
+# replica) and launched through the same prepared call list, so every kernel
+# runs in the launch configuration the benchmark times.  Decode: scores and
+# selections of every row against the oracle; outputs end to end on sampled
+# rows whose oracle index sets the GPU reproduced.  Prefill: sampled rows.
+# ---------------------------------------------------------------------------
+
+
+def _row_subset(prob, rows):
+    import dataclasses
+
+    r = torch.as_tensor(rows, dtype=torch.long, device=prob.seq_of_row.device)
+    return dataclasses.replace(prob, seq_of_row=prob.seq_of_row[r], pos_of_row=prob.pos_of_row[r],
+                               idx_q=[x[r] for x in prob.idx_q], idx_w=[x[r] for x in prob.idx_w],
+                               q=[x[:, r] for x in prob.q])
+
+
+def _same_rows(gi, gc, oi, oc):
+    gi, gc = np.asarray(gi), np.asarray(gc)
+    return [r for r in range(len(oc))
+            if gc[r] == oc[r] and np.array_equal(gi[r, :gc[r]], oi[r, :oc[r]])]
+
+
+def _spread(rows, n=4):
+    if len(rows) <= n:
+        return list(rows)
+    return [rows[int(round(i * (len(rows) - 1) / (n - 1)))] for i in range(n)]
+
+
+@pytest.mark.parametrize("integer", [True, False])
+@pytest.mark.parametrize("name", ["hysparse2", "csa", "csa2"])
+def test_full_size_decode(name, integer, dev):
+    from index_reuse_amd.pipeline import Step
+
+    wl = synth.WORKLOADS[name]
+    _flush("case full-size %s integer=%s" % (name, integer))
+    prob = synth.make_problem(wl, device=dev, integer=integer)
+    step = Step(prob)
+    stream = torch.cuda.current_stream().cuda_stream
+    for _, c in step.prepare():
+        c(stream)
+    torch.cuda.synchronize()
+    cpu = H.move(prob, "cpu")
+    R = cpu.n_rows
+
+    sc = H.oracle_scores(cpu, 0)
+    g = step.scores[0].cpu().double().numpy()
+    valid = ~np.isnan(sc)
+    tau = None if integer else H.fp32_score_bound(cpu, 0)
+    if integer:
+        assert np.array_equal(g[valid], sc[valid])
+    else:
+        err = np.abs(g - np.nan_to_num(sc))
+        assert np.all(err[valid] <= np.broadcast_to(tau[:, None], sc.shape)[valid])
+    gi = [t.cpu().numpy() for t in step.idx]
+    gc = [t.cpu().numpy() for t in step.count]
+    if wl.block:
+        idx, cnt, pool, pc = H.oracle_select(cpu, sc, wl.k, block=wl.block,
+                                             max_blocks=wl.max_blocks)
+        H.check_indices(gi[0], gc[0], idx, cnt, sc, tau)
+        gpool, gpc = step.pool.cpu().numpy(), step.pool_count.cpu().numpy()
+        pool_same = [r for r in range(R) if gpc[r] == pc[r] and np.array_equal(gpool[r], pool[r])]
+        if integer:
+            assert len(pool_same) == R
+        assert pool_same, "no row reproduced the oracle's block pool"
+        rs = H.oracle_scores(cpu, 1, cand=pool, cand_count=pc)
+        gr = step.scores[1].cpu().double().numpy()
+        tau1 = None if integer else H.fp32_score_bound(cpu, 1)
+        for r in pool_same:
+            v = ~np.isnan(rs[r])
+            if integer:
+                assert np.array_equal(gr[r, v], rs[r, v])
+            else:
+                assert np.all(np.abs(gr[r, v] - rs[r, v]) <= tau1[r])
+        ridx, rcnt = H.oracle_select(cpu, rs, wl.k, cand=pool, cand_count=pc)
+        H.check_indices(gi[1], gc[1], ridx, rcnt, rs, tau1, rows=pool_same, positions=pool)
+        oidx, ocnt = [idx, ridx], [cnt, rcnt]
+        same = [sorted(set(_same_rows(gi[0], gc[0], idx, cnt))),
+                sorted(set(_same_rows(gi[1], gc[1], ridx, rcnt)) & set(pool_same))]
+    else:
+        idx, cnt = H.oracle_select(cpu, sc, wl.k)
+        H.check_indices(gi[0], gc[0], idx, cnt, sc, tau)
+        oidx, ocnt = [idx], [cnt]
+        same = [_same_rows(gi[0], gc[0], idx, cnt)]
+    for c in range(len(cpu.q)):
+        if integer:
+            assert len(same[c]) == R
+        assert same[c], "call %d: no row reproduced the oracle's index set" % c
+        rows = _spread(same[c])
+        o_ref, l_ref = H.oracle_attention(cpu, c, oidx[c], ocnt[c], rows=rows)
+        H.check_outputs(step.o[c][:, rows], o_ref, step.lse[c][:, rows], l_ref, wl.attn_dtype,
+                        what="%s call %d rows %s" % (name, c, rows))
+
+
+DSA_FULL_ROWS = [0, 1, 2046, 2047, 2048, 8191, 8192, 30001, 49152, 65535]
+
+
+@pytest.mark.parametrize("integer", [True, False])
+def test_full_size_prefill(integer, dev):
+    """DSA prefill over the whole 64K-token sequence in the benchmark's row
+    blocks; sampled rows (both sides of the budget edge, of a block edge, and
+    the last row) against the oracle."""
+    from index_reuse_amd.pipeline import PrefillStep
+
+    wl = synth.DSA
+    _flush("case full-size dsa integer=%s" % integer)
+    prob = synth.make_problem(wl, device=dev, integer=integer)
+    step = PrefillStep(prob, row_block=8192)
+    step.run()
+    torch.cuda.synchronize()
+    rows = DSA_FULL_ROWS
+    sub = H.move(_row_subset(prob, rows), "cpu")
+    del prob
+    sc = H.oracle_scores(sub, 0)
+    tau = None if integer else H.fp32_score_bound(sub, 0)
+    idx, cnt = H.oracle_select(sub, sc, wl.k)
+    assert list(cnt) == [min(wl.k, t + 1) for t in rows]
+    assert max(rows) < step.idx.shape[0] == step.count.shape[0] == step.R
+    gi = step.idx.cpu().numpy()[rows]
+    gc = step.count.cpu().numpy()[rows]
+    H.check_indices(gi, gc, idx, cnt, sc, tau)
+    same = _same_rows(gi, gc, idx, cnt)
+    if integer:
+        assert len(same) == len(rows)
+    assert same
+    o_ref, l_ref = H.oracle_attention(sub, 0, idx, cnt, rows=same)
+    # PrefillStep keeps one [n_sets, R, hq, dv] output (and [n_sets, R, hq]
+    # LSE) for all rows: pick the sampled rows on dimension 1.
+    pick = [rows[i] for i in same]
+    assert step.o.dim() == 4 and step.lse.dim() == 3
+    assert max(pick) < step.o.shape[1] == step.lse.shape[1] == step.R
+    sel = torch.tensor(pick, dtype=torch.long, device=step.o.device)
+    H.check_outputs(step.o.index_select(1, sel), o_ref, step.lse.index_select(1, sel), l_ref,
+                    wl.attn_dtype, what="dsa rows %s" % pick)
