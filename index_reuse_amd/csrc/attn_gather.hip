@@ -1138,8 +1138,11 @@ struct AttnShape {
 
 AttnShape attn_shape(const AttnArgs& a) {
   const int tiles = (a.n_qsets * (a.hq / a.hkv) + 15) / 16;
-  if (a.kv_kind == KV_SEPARATE && a.dqk == 128 && tiles <= 3) return {3, 4};
-  if (a.kv_kind == KV_SHARED && a.dqk == 128 && tiles <= 3) return {3, 4};
+  // at most 3 query tiles of 128-wide rows: 2 groups of 3 waves with two
+  // 2-tile steps in flight beat 4 groups with one 4-tile step (a lighter
+  // group merge, and a finer pipeline)
+  if (a.kv_kind == KV_SEPARATE && a.dqk == 128 && tiles <= 3) return {3, 2};
+  if (a.kv_kind == KV_SHARED && a.dqk == 128 && tiles <= 3) return {3, 2};
   if (a.dqk >= 256) return {4, 1};
   return {4, 2};
 }
@@ -1176,8 +1179,8 @@ hipError_t launch_mla(const AttnArgs& a, hipStream_t s) {
 template <int DQK, int DV, int KV, int D>
 hipError_t launch_shaped(const AttnArgs& a, hipStream_t s) {
   const AttnShape sh = attn_shape(a);
-  if (sh.w == 3 && sh.ng == 4) {
-    if constexpr (DQK == 128) return launch_mfma_attn<DQK, DV, KV, 3, 4, 1>(a, s);
+  if (sh.w == 3 && sh.ng == 2) {
+    if constexpr (DQK == 128) return launch_mfma_attn<DQK, DV, KV, 3, 2, D>(a, s);
   } else if (sh.ng == 1) {
     if constexpr (DQK >= 256) return launch_mfma_attn<DQK, DV, KV, 4, 1, D>(a, s);
   } else {
