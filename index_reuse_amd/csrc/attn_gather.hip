@@ -20,14 +20,16 @@
 //   2. each wave computes S^T = K . Q^T for its 16 query rows with
 //      v_mfma_f32_16x16x32_bf16 (entries on M, query rows on N), so each lane
 //      ends up holding 8 logits of ONE query row;
-//   3. softmax in fp32 (exp2 domain) against a per-row reference max that
-//      only moves when a tile exceeds it by 2^8 (lazy rescale);
+//   3. softmax in fp32 (exp2 domain) against a per-row reference max fixed
+//      by the first tile with a finite logit (a range whose logits outgrow
+//      it by 2^64 runs a second time with the true max);
 //   4. O^T += V^T . P^T with the contraction order permuted so that the
-//      lane's 8 probabilities are directly its B operand; the V^T operand is
-//      built from 16-byte LDS reads by an in-register 8x8 bf16 transpose
-//      (v_perm).  O^T keeps each lane on one query row, so rescales and the
-//      final normalisation need no cross-lane traffic; row statistics are
-//      reduced with the gfx950 lane-swap instructions.
+//      lane's 8 probabilities are directly its B operand; the V^T operand
+//      comes straight from LDS through the gfx950 transpose read
+//      (ds_read_b64_tr_b16; the latent kernel below transposes 16-byte
+//      reads in registers with v_perm).  O^T keeps each lane on one query
+//      row, so the final normalisation needs no cross-lane traffic; row
+//      statistics are reduced with the gfx950 lane-swap instructions.
 // Long entry lists are split across workgroups; a combine kernel merges the
 // (max, sum, unnormalised O) partials.  F32 inputs use a plain VALU kernel.
 #include "kernels.hpp"
@@ -52,6 +54,16 @@ __device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) {
 // 2^x on the hardware exp unit (v_exp_f32): exact at 0, 0 at -inf; results
 // below 2^-126 flush to zero, which softmax weights can afford.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// gfx950 LDS transpose read of 8 bytes (ds_read_b64_tr_b16) at an LDS
+// address (8-byte aligned); the lane exchange is described at its use.
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
 
 
 // Dequantise 32 FP4 channels (16 code bytes, 2 E4M3 scales) into 16 packed
@@ -458,26 +470,24 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
     const bf16x8 pab = __builtin_bit_cast(bf16x8, pa);
     const uint16_t* vbase = KV == KV_SEPARATE ? lds.u.t.v[buf] : kb;
     constexpr int VR = KV == KV_SEPARATE ? L::VROW : L::KROW;
+    // V^T as the A operand, straight from LDS with the gfx950 transpose read
+    // (ds_read_b64_tr_b16): inside each 16-lane block, lane i receives
+    // element i % 4 of the 8 bytes fetched by lanes 4j + i / 4 as its
+    // element j.  Lane 4jj + q of k-group gq fetches channels
+    // [32q + 4t, 32q + 4t + 4) of entry 4gq + jj (then 16 + 4gq + jj), so
+    // lane col gets channel 32(col / 4) + 4t + col % 4 of its k-slots'
+    // entries: M-tile 8jb + t row m is channel 128jb + 32(m / 4) + 4t + m % 4.
+    const uint16_t* vr0 = vbase + (4 * gq + ((lane >> 2) & 3)) * VR + 32 * (lane & 3);
+    const uint16_t* vr1 = vr0 + 16 * VR;
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
-      // V^T as the A operand: lane col takes channels 128jb + 8col + j of the
-      // 8 entries of its k-slots (an 8x8 bf16 transpose in registers), so
-      // M-tile 8jb + j row m is channel 128jb + 8m + j.
-      u32x4 R[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int e = i < 4 ? 4 * gq + i : 16 + 4 * gq + (i - 4);
-        R[i] = *reinterpret_cast<const u32x4*>(vbase + e * VR + jb * 128 + col * 8);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        u32x4 b;
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          b[qd] = (j & 1) ? hi16x2(R[2 * qd][j >> 1], R[2 * qd + 1][j >> 1])
-                          : lo16x2(R[2 * qd][j >> 1], R[2 * qd + 1][j >> 1]);
-        O[jb * 8 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, b), pab, O[jb * 8 + j], 0, 0, 0);
+      for (int t = 0; t < 8; ++t) {
+        const s16x4 lo = lds_read_tr16(vr0 + jb * 128 + 4 * t);
+        const s16x4 hi = lds_read_tr16(vr1 + jb * 128 + 4 * t);
+        const s16x8 b = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        O[jb * 8 + t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, b), pab, O[jb * 8 + t], 0, 0, 0);
       }
     }
   };
@@ -543,12 +553,10 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
       lds.ml[grp][wq][col][2] = l_lse;
     }
     {
+      // O[t] holds channels 32gq + 4t + (0..3): the lane's 32 channels in order
       f32x4* dst = reinterpret_cast<f32x4*>(&lds.u.comb[((grp * W + wq) * 64 + lane) * L::CSTRIDE]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dst[2 * i] = f32x4{O[0][i], O[1][i], O[2][i], O[3][i]};
-        dst[2 * i + 1] = f32x4{O[4][i], O[5][i], O[6][i], O[7][i]};
-      }
+      for (int t = 0; t < 8; ++t) dst[t] = O[t];
     }
     __syncthreads();
     if (!active) return;
@@ -613,8 +621,9 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
   }
 
   if (!active) return;
-  // Output: lane holds O^T for query row qrow0 + col: O[8jb + j][i] is channel
-  // 128jb + 8(4gq + i) + j, so each (jb, i) is 8 contiguous channels.
+  // Output: lane holds O^T for query row qrow0 + col: O[8jb + t][i] is channel
+  // 128jb + 32gq + 4t + i, so O[8jb + 2h] and O[8jb + 2h + 1] are the 8
+  // contiguous channels from 128jb + 32gq + 8h.
   const int qr = qrow0 + col;
   if (qr >= Mq) return;
   const int R = a.rows.n_rows;
@@ -625,20 +634,18 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c0 = jb * 128 + 32 * gq + 8 * i;
+      for (int hh = 0; hh < 4; ++hh) {
+        const int c0 = jb * 128 + 32 * gq + 8 * hh;
+        const f32x4 v0 = O[jb * 8 + 2 * hh] * inv, v1 = O[jb * 8 + 2 * hh + 1] * inv;
         if (a.o_dtype == 1) {
           u32x4 pk;
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-            pk[qd] = pack_bf16x2(O[jb * 8 + 2 * qd][i] * inv, O[jb * 8 + 2 * qd + 1][i] * inv);
+          pk[0] = pack_bf16x2(v0[0], v0[1]);
+          pk[1] = pack_bf16x2(v0[2], v0[3]);
+          pk[2] = pack_bf16x2(v1[0], v1[1]);
+          pk[3] = pack_bf16x2(v1[2], v1[3]);
           *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.o) + orow * DV + c0) = pk;
         } else {
           float* op = reinterpret_cast<float*>(a.o) + orow * DV + c0;
-          f32x4 v0 = {O[jb * 8 + 0][i] * inv, O[jb * 8 + 1][i] * inv, O[jb * 8 + 2][i] * inv,
-                      O[jb * 8 + 3][i] * inv};
-          f32x4 v1 = {O[jb * 8 + 4][i] * inv, O[jb * 8 + 5][i] * inv, O[jb * 8 + 6][i] * inv,
-                      O[jb * 8 + 7][i] * inv};
           reinterpret_cast<f32x4*>(op)[0] = v0;
           reinterpret_cast<f32x4*>(op)[1] = v1;
         }
@@ -652,12 +659,10 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float* op = po + jb * 128 + 32 * gq + 8 * i;
-        f32x4 v0 = {O[jb * 8 + 0][i], O[jb * 8 + 1][i], O[jb * 8 + 2][i], O[jb * 8 + 3][i]};
-        f32x4 v1 = {O[jb * 8 + 4][i], O[jb * 8 + 5][i], O[jb * 8 + 6][i], O[jb * 8 + 7][i]};
-        reinterpret_cast<f32x4*>(op)[0] = v0;
-        reinterpret_cast<f32x4*>(op)[1] = v1;
+      for (int hh = 0; hh < 4; ++hh) {
+        float* op = po + jb * 128 + 32 * gq + 8 * hh;
+        reinterpret_cast<f32x4*>(op)[0] = O[jb * 8 + 2 * hh];
+        reinterpret_cast<f32x4*>(op)[1] = O[jb * 8 + 2 * hh + 1];
       }
     if (gq == 0) {
       float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 3;
