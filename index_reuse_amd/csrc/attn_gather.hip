@@ -181,24 +181,45 @@ __device__ __forceinline__ RangeTable range_header(const AttnArgs& a, int r, int
 // clamped rather than guarded so that a thread's loads all issue before the
 // first wait.  Padding entries later read the rows of the range's first real
 // entry: finite data that the mask gives weight exactly 0 (with from > 0 the
-// caller has set rt.dummy and rt.nsteps_run already).  Ends with a barrier.
-template <int NTH>
+// caller has set rt.dummy and rt.nsteps_run already).  `mid` runs once,
+// between the issue of the first chunk's block-table reads and their use (a
+// caller issues its first gathers there: those reads then go out ahead of
+// the gathers and are not held behind them).  Ends with a barrier.
+struct NoMid {
+  __device__ __forceinline__ void operator()() const {}
+};
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
+template <int NTH, typename Mid = NoMid>
 __device__ __forceinline__ void fill_range_table(const AttnArgs& a, int r, int e0, const RowInfo& ri,
                                                  RangeTable& rt, const int (&sel_pre)[kPT], int from,
-                                                 int32_t* slot_tab, int32_t* wfirst_tab) {
+                                                 int32_t* slot_tab, int32_t* wfirst_tab,
+                                                 Mid mid = Mid()) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t* idx = a.idx ? a.idx + (int64_t)r * a.idx_stride : nullptr;
   const bool pre_ok = rt.n_w == a.rows.window;
   int wfirst = 0x7FFFFFFF;
-  for (int i0 = 0; i0 < rt.n_tab; i0 += kPT * NTH) {
+  // selected index of table entry i0 + j NTH + tid (clamped loads)
+  auto sel_of = [&](int i0, int (&sel)[kPT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kPT; ++j)
+      sel[j] = idx ? idx[min(max(e0 + i0 + j * NTH + tid - rt.n_w, 0), a.idx_stride - 1)] : -1;
+  };
+  // One chunk of kPT * NTH table entries.  The block-table case is a
+  // compile-time choice and the first chunk is written out apart, so the
+  // code from the block-table reads through `hook` to their use has no
+  // branch, and the wait for those reads counts exactly the loads `hook`
+  // issued after them.
+  auto chunk = [&](int i0, const int (&sel)[kPT], auto hook, auto bt) __attribute__((always_inline)) {
     int pos[kPT];
 #pragma unroll
     for (int j = 0; j < kPT; ++j) {
       const int i = i0 + j * NTH + tid;
       const int e = e0 + i;
-      const int sel = (i0 == 0 && pre_ok) ? sel_pre[j]
-                                          : (idx ? idx[min(max(e - rt.n_w, 0), a.idx_stride - 1)] : -1);
-      pos[j] = i < rt.ne ? (e < rt.n_w ? ri.win_lo + e : sel) : -1;
+      pos[j] = i < rt.ne ? (e < rt.n_w ? ri.win_lo + e : sel[j]) : -1;
     }
     // block-table reads of the kPT entries, all issued before the first is
     // used (entries without a position read page 0 of the row's table)
@@ -210,13 +231,25 @@ __device__ __forceinline__ void fill_range_table(const AttnArgs& a, int r, int e
       off[j] = e - pg[j] * a.k.page_size;
     }
     const int64_t row_pages = (int64_t)max(ri.b, 0) * a.k.max_pages;
+    int32_t pv[kPT];
+    if constexpr (decltype(bt)::value) {
+#pragma unroll
+      for (int j = 0; j < kPT; ++j) pv[j] = a.k.block_table[row_pages + pg[j]];
+    }
+    hook();
+    // every read is taken here, after all the hook's loads went out (left to
+    // itself the compiler sinks a read into the guarded store below, where
+    // its wait would cover the hook's loads as well)
+    __builtin_amdgcn_sched_barrier(0);
     int64_t page[kPT];
-    if (a.k.block_table) {
 #pragma unroll
-      for (int j = 0; j < kPT; ++j) page[j] = a.k.block_table[row_pages + pg[j]];
-    } else {
-#pragma unroll
-      for (int j = 0; j < kPT; ++j) page[j] = row_pages + pg[j];
+    for (int j = 0; j < kPT; ++j) {
+      if constexpr (decltype(bt)::value) {
+        asm volatile("" ::"v"(pv[j]));
+        page[j] = pv[j];
+      } else {
+        page[j] = row_pages + pg[j];
+      }
     }
 #pragma unroll
     for (int j = 0; j < kPT; ++j) {
@@ -227,7 +260,25 @@ __device__ __forceinline__ void fill_range_table(const AttnArgs& a, int r, int e
       const uint64_t has = __builtin_amdgcn_ballot_w64(slot >= 0);
       if (has) wfirst = min(wfirst, i0 + j * NTH + (tid & ~63) + (int)__builtin_ctzll(has));
     }
-  }
+  };
+  auto run = [&](auto bt) __attribute__((always_inline)) {
+    int sel[kPT];
+    if (pre_ok) {
+#pragma unroll
+      for (int j = 0; j < kPT; ++j) sel[j] = sel_pre[j];
+    } else {
+      sel_of(0, sel);
+    }
+    chunk(0, sel, mid, bt);
+    for (int i0 = kPT * NTH; i0 < rt.n_tab; i0 += kPT * NTH) {
+      sel_of(i0, sel);
+      chunk(i0, sel, NoMid(), bt);
+    }
+  };
+  if (a.k.block_table)
+    run(BoolC<true>());
+  else
+    run(BoolC<false>());
   if (from > 0) {
     __syncthreads();
     return;
@@ -250,13 +301,15 @@ __device__ __forceinline__ RangeTable build_range_table(const AttnArgs& a, int r
   return rt;
 }
 
-// The first step of a range that starts with at least a step of window
-// entries, from scalar block-table reads only (a step of 32 NG entries spans
-// at most three pages of 64 or more): its rows can be gathered while the
-// indices and their pages are still on the way.  Ends with a barrier.
-template <int NTH, int NG>
-__device__ __forceinline__ void fill_window_step(const AttnArgs& a, const RowInfo& ri, int32_t* slot_tab) {
-  static_assert(NTH >= NG * kTile, "one entry per thread");
+// The first n (<= 128) entries of a range that starts with at least that
+// many window entries, from scalar block-table reads only (128 consecutive
+// entries span at most three pages of 64 or more): their rows can be
+// gathered while the indices and their pages are still on the way.  Ends
+// with a barrier.
+template <int NTH>
+__device__ __forceinline__ void fill_window_steps(const AttnArgs& a, const RowInfo& ri, int n,
+                                                  int32_t* slot_tab) {
+  static_assert(NTH >= 128, "one entry per thread");
   const int pf = ri.win_lo >> a.k.page_shift;
   const int64_t row_pages = (int64_t)ri.b * a.k.max_pages;
   int64_t pgs[3];
@@ -266,7 +319,7 @@ __device__ __forceinline__ void fill_window_step(const AttnArgs& a, const RowInf
     pgs[k] = a.k.block_table ? (int64_t)a.k.block_table[row_pages + pk] : row_pages + pk;
   }
   const int tid = threadIdx.x;
-  if (tid < NG * kTile) {
+  if (tid < n) {
     const int pos = ri.win_lo + tid;
     const int k = (pos >> a.k.page_shift) - pf;
     const int64_t page = k == 0 ? pgs[0] : (k == 1 ? pgs[1] : pgs[2]);
@@ -323,13 +376,16 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
   }
 
   // A range that opens with a whole step of window entries (decode rows
-  // with a window) gathers that step before the selected entries' table is
-  // built; otherwise the whole table comes first.
+  // with a window) gathers that step while the selected entries' table is
+  // built; otherwise the whole table comes first.  (Gathering two window
+  // steps early was slower: the larger first burst delays the first data.)
   RangeTable rt = range_header<NG, D>(a, r, sp * per_split, per_split, ri);
+  constexpr int SE = NG * kTile;  // entries per step
+  static_assert(SE <= 128, "a window step spans at most three pages");
   const bool early =
-      sp == 0 && ri.b >= 0 && rt.n_w >= NG * kTile && rt.ne >= NG * kTile && a.k.page_shift >= 6;
+      sp == 0 && ri.b >= 0 && a.k.page_shift >= 6 && rt.n_w >= SE && rt.ne >= SE;
   if (early) {
-    fill_window_step<NTH, NG>(a, ri, lds.slot);
+    fill_window_steps<NTH>(a, ri, SE, lds.slot);
     rt.dummy = (uint32_t)lds.slot[0];
     rt.nsteps_run = rt.nsteps;
   } else {
@@ -498,10 +554,12 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
   static_assert(D == 1 || D % 2 == 0, "prefetch depth must be 1 or even");
   T ring[D];
   if (early) {
-    // step 0 (window rows) is on its way while the rest of the table is
-    // built; the steps after it wait for the table
-    load_step(0, ring[0]);
-    fill_range_table<NTH>(a, r, sp * per_split, ri, rt, sel_pre, NG * kTile, lds.slot, lds.wfirst);
+    // The window step goes out right after the block-table reads of the
+    // selected entries (loads complete in issue order, so those reads are
+    // not held behind the gathers) and is on its way while the rest of the
+    // table is built; the steps after it wait for the table.
+    fill_range_table<NTH>(a, r, sp * per_split, ri, rt, sel_pre, SE, lds.slot, lds.wfirst,
+                          [&]() { load_step(0, ring[0]); });
   }
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
