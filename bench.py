@@ -1,20 +1,22 @@
 #!/usr/bin/env python3
 """Throughput of one step of indexer-driven top-k sparse attention on one GPU.
 
-Default workload (the one the headline metric is quoted on): HySparse2-style
-decode, 32 sequences x 32768 tokens, paged KV (64-token pages, shuffled page
-table), 8 KV heads x 128, 64 query heads, indexer 16 heads x 64 (bf16),
-forced window 128 + top-1024, 6 query sets (1 FA + 5 SA) reusing one index
-tensor.  A step = index score -> window + top-k -> gather attention for all
-6 query sets; 192 queries per step.
+Headline workload (the one the metric is quoted on): HySparse2-style decode,
+32 sequences x 32768 tokens, paged KV (64-token pages, shuffled page table),
+8 KV heads x 128, 64 query heads, indexer 16 heads x 64 (bf16), forced window
+128 + top-1024, 6 query sets (1 FA + 5 SA) reusing one index tensor.  A step
+= index score -> window + top-k -> gather attention for all 6 query sets; 192
+queries per step.  The default run (--workload all) also measures, as extra
+records in the same JSON line: CSA compressed decode (queries/s), the CSA2
+FP4 layer group (queries/s) and the 64K-row DSA prefill (rows/s).
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
-Steps rotate over several independent input replicas so that a step's
+Decode steps rotate over several independent input replicas so that a step's
 working set is not already resident in the 256 MB last-level cache.  Each
 entry-point call is bracketed by HIP events on the launch stream for the
 per-kernel breakdown and the roofline of the dominant kernel.
 
-    python bench.py [--gpus 1] [--steps 30] [--warmup 5] [--workload hysparse2]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload all]
 """
 from __future__ import annotations
 
@@ -162,6 +164,21 @@ def calibration_copy(mib: int):
     del src, dst
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), for the baseline's
+    record."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(step, n_rows: int, min_seconds: float):
     """The fp64 oracle on the first ``n_rows`` decode rows of the same inputs
     (whole step: score, select, and attention for every query set; with a
@@ -229,7 +246,7 @@ def cpu_baseline(step, n_rows: int, min_seconds: float):
             break
     queries = reps * n_rows * sum(x.shape[0] for x in q)
     return {"value": round(queries / dt, 3), "unit": "queries/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu": cpu_model(), "kind": "oracle",
             "sample": "%d pass(es) over %d of %d decode rows of one replica (whole step: score "
                       "%d entries/row, select, attention for %d query sets), %.1f s" % (
                           reps, n_rows, p.n_rows, int(sl.max()) // wl.stride,
@@ -239,14 +256,32 @@ def cpu_baseline(step, n_rows: int, min_seconds: float):
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}  # MI355X dense
 
 
+def layer_group_index_work(n_entries: int, pool: int, n_full: int, n_reindex: int,
+                           n_reuse: int):
+    """Entries scored per query by one layer group ("CSA, HCA and CSA2",
+    sections 3.1 and 6.2): a flat design runs the full-domain indexer in every
+    layer; the hierarchical one scans the whole domain once (Full), each
+    Reindex layer scores only its pool, and Reuse layers score nothing.
+    Returns (flat, hierarchical)."""
+    flat = (n_full + n_reindex + n_reuse) * n_entries
+    hier = n_full * n_entries + n_reindex * pool
+    return flat, hier
+
+
 def prefill_work(wl, prob):
     """Algorithmic work of one pass over every row of a prefill workload:
     indexer flops (causal pairs x heads x dim x 2), attention flops (gathered
     pairs x heads x (d_qk + d_v) x 2), and selection bytes."""
+    return prefill_work_rows(wl, prob.pos_of_row.cpu().numpy(), int(prob.seq_len.max()))
+
+
+def prefill_work_rows(wl, pos, seq_len: int):
+    """prefill_work for query rows at token positions ``pos`` of one sequence
+    of ``seq_len`` tokens."""
     import numpy as np
 
-    pos = prob.pos_of_row.cpu().numpy().astype(np.int64)
-    n = np.minimum(pos + 1, int(prob.seq_len.max())) // wl.stride
+    pos = np.asarray(pos).astype(np.int64)
+    n = np.minimum(pos + 1, seq_len) // wl.stride
     pairs = int(n.sum())
     cand = np.maximum(n - wl.window, 0)
     sel = np.minimum(cand, wl.k)
@@ -295,7 +330,7 @@ def prefill_cpu_baseline(prob, n_rows: int, min_seconds: float):
         if dt >= min_seconds:
             break
     return {"value": round(reps * n_rows / dt, 3), "unit": "rows/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu": cpu_model(), "kind": "oracle",
             "sample": "%d pass(es) over %d rows spread evenly over the %d-row prefill (score, "
                       "select, attention), %.1f s" % (reps, n_rows, R, dt)}
 
@@ -374,50 +409,20 @@ def run_prefill(args, wl):
     }
     if not args.no_cpu:
         out["cpu_baseline"] = prefill_cpu_baseline(prob, args.cpu_rows or 16, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    del step, prob, calls
+    torch.cuda.empty_cache()
+    return out
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="hysparse2")
-    ap.add_argument("--replicas", type=int, default=4)
-    ap.add_argument("--cpu-rows", type=int, default=0,
-                    help="decode rows for the oracle baseline (default: all rows of a step)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="minimum host time of the oracle baseline")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    ap.add_argument("--row-block", type=int, default=8192,
-                    help="prefill: query rows per block (the score buffer holds one block)")
-    ap.add_argument("--copy-mib", type=int, default=0,
-                    help="run a plain copy of this size first (counter calibration)")
-    ap.add_argument("--eager", action="store_true",
-                    help="decode: launch every call from the host in the timed region instead of "
-                         "replaying one captured graph of the K steps")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(decode shards by sequence with no exchange; see the design notes). "
-              "Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
+def run_decode(args, wl):
+    """Decode: one step = every call of the workload's layer group on all its
+    rows; returns the JSON record."""
     import torch
 
-    import index_reuse_amd
     import synth
     from index_reuse_amd.pipeline import Step
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    index_reuse_amd.load()
     dev = torch.device("cuda:0")
-    if args.copy_mib > 0:
-        calibration_copy(args.copy_mib)
-    wl = synth.WORKLOADS[args.workload]
-    if wl.prefill:
-        return run_prefill(args, wl)
     steps = []
     for i in range(args.replicas):
         prob = synth.make_problem(wl, device=dev, seed_base=1000 * (wl.cfg_id + 1) + 100 * i)
@@ -472,6 +477,7 @@ def main():
             e1.record()
             torch.cuda.synchronize()
             per_call[n] = e0.elapsed_time(e1) / K
+            del gc
         # Throughput: the same K steps captured once as a HIP graph (no host
         # launches between calls, as a serving loop would run them); one
         # untimed replay uploads it, the timed replay runs the K steps.
@@ -488,6 +494,7 @@ def main():
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         mode = "graph"
+        del g
     ms_step = elapsed * 1e3 / K
     gpu_ms_step = sum(evs[i][0].elapsed_time(evs[i][-1]) for i in range(K)) / K
 
@@ -502,6 +509,7 @@ def main():
         b = algorithmic_bytes(step0, n)
         kernels[n] = {"ms": round(per_call[n], 5), "alg_bytes": int(b),
                       "GB/s": round(b / (per_call[n] * 1e-3) / 1e9, 1)}
+    step_bytes = sum(algorithmic_bytes(step0, n) for n in names)
     out = {
         "metric": METRIC,
         "value": round(queries * K / elapsed, 1),
@@ -513,7 +521,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp4 kv, bf16" if wl.kv_mode == "fp4" else "bf16",
         "data": "synthetic",
         "config": {"workload": "%s_decode" % wl.name, "batch": wl.n_seqs,
                    "context": wl.seq_len, "window": wl.window, "topk": wl.k,
@@ -525,12 +533,88 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else int(traffic),
                      "alg_bytes": int(bytes_dom)},
+        "step_roofline": {"alg_bytes": int(step_bytes),
+                          "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "gpu_ms_per_step": round(gpu_ms_step, 5),
         "kernels": kernels,
     }
+    if wl.block:
+        # entries scored per query by the layer group (Full + Reindex; the
+        # Reuse layers score none), against one full-domain indexer per layer
+        n_full = sum(g[0] for g in row_geometry(step0)) / step0.prob.n_rows
+        pool = float(step0.pool_count.float().mean())
+        flat, hier = layer_group_index_work(n_full, pool, 1, 1, len(step0.prob.q[1]) - 1)
+        out["index_comparisons_per_query"] = {"hierarchical": int(hier), "flat": int(flat)}
     if not args.no_cpu:
         n = args.cpu_rows if args.cpu_rows > 0 else step0.prob.n_rows
         out["cpu_baseline"] = cpu_baseline(step0, min(n, step0.prob.n_rows), args.cpu_seconds)
+    del steps, calls, step0
+    torch.cuda.empty_cache()
+    return out
+
+
+# Extra workloads measured by the default run, next to the headline decode.
+EXTRA = ("csa", "csa2", "dsa")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="all",
+                    help="hysparse2, csa, csa2, dsa, or all (the headline HySparse2 decode, with "
+                         "the other workloads as extra records)")
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="decode rows for the oracle baseline (default: all rows of a step)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum host time of the oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--row-block", type=int, default=8192,
+                    help="prefill: query rows per block (the score buffer holds one block)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run a plain copy of this size first (counter calibration)")
+    ap.add_argument("--eager", action="store_true",
+                    help="decode: launch every call from the host in the timed region instead of "
+                         "replaying one captured graph of the K steps")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(decode shards by sequence with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import index_reuse_amd
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    index_reuse_amd.load()
+    if args.copy_mib > 0:
+        calibration_copy(args.copy_mib)
+
+    def run(name):
+        wl = synth.WORKLOADS[name]
+        t = time.perf_counter()
+        rec = run_prefill(args, wl) if wl.prefill else run_decode(args, wl)
+        print("# %s done in %.1f s" % (name, time.perf_counter() - t), file=sys.stderr, flush=True)
+        return rec
+
+    if args.workload != "all":
+        print(json.dumps(run(args.workload)), flush=True)
+        return
+    out = run("hysparse2")
+    extra = {}
+    for name in EXTRA:
+        rec = run(name)
+        for k in ("metric", "n_gpus", "steps", "warmup", "higher_is_better", "scaling",
+                  "vs_baseline", "data"):
+            rec.pop(k, None)
+        extra[rec["config"]["workload"]] = rec
+    out["workloads"] = extra
     print(json.dumps(out), flush=True)
 
 

@@ -38,7 +38,8 @@
  *  - No exception crosses the ABI.  Host-side validation failures return a
  *    negative sa_status and leave outputs untouched; sa_last_error() gives a
  *    thread-local message.  Index CONTENTS are trusted: -1 means padding, any
- *    other value must be a visible entry of the row.
+ *    other value must be a visible entry of the row (sparse_check_indices
+ *    verifies a tensor on the device when a caller wants it checked).
  *  - The library keeps no state between calls and is reentrant; concurrent
  *    calls must use distinct workspaces.
  *
@@ -197,10 +198,10 @@ typedef struct {
  *               pool_count [R] out
  * Scores must not be NaN.
  *
- * Workspace: sa_workspace_size(SA_OP_TOPK_SELECT, desc) bytes that must be
- * zero-filled before the first call and are not shared with other entry
- * points; every call leaves its histogram area zero-filled again.  Calls that
- * overlap in time need distinct workspaces.
+ * Workspace: sa_workspace_size(SA_OP_TOPK_SELECT, desc) bytes.  Its contents
+ * on entry are ignored (the call clears what it counts into), so one
+ * workspace may serve any sequence of calls, of any entry point and any row
+ * count, as long as no two of them overlap in time.
  */
 typedef struct {
   sa_rows rows;
@@ -276,6 +277,29 @@ sa_status sparse_index_score(const sa_index_desc* desc, void* ws, size_t ws_byte
 sa_status sparse_topk_select(const sa_topk_desc* desc, void* ws, size_t ws_bytes, void* stream);
 sa_status sparse_attn_gather_fwd(const sa_attn_desc* desc, void* ws, size_t ws_bytes,
                                  void* stream);
+
+/*
+ * sparse_check_indices -- device-side check of an index tensor before it is
+ * reused ("CSA, HCA and CSA2", section 5.1, fault injection: a Reuse layer's
+ * indices shifted by one token, or a leaked row, must be caught by an
+ * assertion rather than by an output that merely looks plausible).
+ *
+ * Reads desc->rows, k, idx, idx_stride, count and cand (only whether it is
+ * NULL); every other field is ignored.  Row r passes when 0 <= count[r] <= k,
+ * idx[r][0 .. count) is strictly ascending and lies among the row's
+ * candidates -- token mode (cand == NULL): [0, win_lo); candidate mode:
+ * [0, n_avail) outside the window -- and idx[r][count .. k) == -1.  A padding
+ * row passes only with count 0.
+ *
+ *   err  one device uint32 (caller-owned), written on `stream`: 0xFFFFFFFF if
+ *        every row passes, else (r << 3) | code for the smallest failing row r
+ *        and its smallest code: 1 count out of range, 2 index outside the
+ *        candidates, 3 not strictly ascending, 4 padding slot not -1.
+ *
+ * Only idx, count and the row geometry are read, so any contents are safe to
+ * check.  Returns SA_ERR_* for an invalid descriptor (err untouched).
+ */
+sa_status sparse_check_indices(const sa_topk_desc* desc, uint32_t* err, void* stream);
 
 /* Workspace bytes `op` (SA_OP_*) needs for `desc` (a pointer to the matching
  * descriptor); 0 if none.  Returns (size_t)-1 if the descriptor is invalid. */

@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     SAError,
     abi_version,
     attn_gather_fwd,
+    check_indices,
     index_score,
     load,
     topk_select,

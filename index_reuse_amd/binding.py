@@ -57,7 +57,7 @@ class sa_attn_desc(ctypes.Structure):
 
 
 EXPORTS = ("sparse_index_score", "sparse_topk_select", "sparse_attn_gather_fwd",
-           "sa_workspace_size", "sa_last_error", "sa_abi_version")
+           "sparse_check_indices", "sa_workspace_size", "sa_last_error", "sa_abi_version")
 
 _lib = None
 
@@ -81,6 +81,8 @@ def load(path: str = LIB_PATH):
     L.sparse_index_score.argtypes = [ctypes.POINTER(sa_index_desc), _P, ctypes.c_size_t, _P]
     L.sparse_topk_select.argtypes = [ctypes.POINTER(sa_topk_desc), _P, ctypes.c_size_t, _P]
     L.sparse_attn_gather_fwd.argtypes = [ctypes.POINTER(sa_attn_desc), _P, ctypes.c_size_t, _P]
+    L.sparse_check_indices.restype = _i32
+    L.sparse_check_indices.argtypes = [ctypes.POINTER(sa_topk_desc), _P, _P]
     L.sa_workspace_size.restype = ctypes.c_size_t
     L.sa_workspace_size.argtypes = [_i32, _P]
     L.sa_last_error.restype = ctypes.c_char_p
@@ -115,6 +117,18 @@ def _ptr(t: Optional[torch.Tensor]):
 
 def _stream():
     return torch.cuda.current_stream().cuda_stream
+
+
+def _dense(t: Optional[torch.Tensor], name: str, rows: bool = False):
+    """The descriptors pass a base pointer (plus a row stride for ``rows``
+    tensors): the tensor must be contiguous (``rows``: each row contiguous)."""
+    if t is None:
+        return
+    ok = t.stride(-1) == 1 if rows and t.dim() >= 1 else t.is_contiguous()
+    if rows and t.dim() > 2:
+        ok = ok and t[0].is_contiguous()
+    if not ok:
+        raise SAError("%s must be %s" % (name, "row-contiguous" if rows else "contiguous"))
 
 
 # ---------------------------------------------------------------------------
@@ -173,16 +187,15 @@ _ws_cache = {}
 
 
 def workspace(nbytes: int, device, op: int) -> Optional[torch.Tensor]:
-    """A cached, zero-filled-at-allocation device workspace of at least
-    ``nbytes`` bytes, private to entry point ``op`` (the selection keeps its
-    workspace zero-filled between calls; other ops leave scratch behind)."""
+    """A cached device workspace of at least ``nbytes`` bytes for entry point
+    ``op`` (no entry point reads what an earlier call left in it; calls on
+    the current stream run one after another, so they can share it)."""
     if nbytes == 0:
         return None
-    # the selection's layout depends on its descriptor: one buffer per size
-    key = (torch.device(device).index, op, nbytes if op == SA_OP_TOPK_SELECT else 0)
+    key = (torch.device(device).index, op)
     t = _ws_cache.get(key)
     if t is None or t.numel() < nbytes:
-        t = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        t = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _ws_cache[key] = t
     return t
 
@@ -193,6 +206,11 @@ def workspace(nbytes: int, device, op: int) -> Optional[torch.Tensor]:
 
 
 def index_desc(rows: Rows, q, w, k: Cache, scores, cand=None, cand_count=None) -> sa_index_desc:
+    _dense(q, "q")
+    _dense(w, "w")
+    _dense(scores, "scores", rows=True)
+    _dense(cand, "cand", rows=True)
+    _dense(cand_count, "cand_count")
     return sa_index_desc(rows.c(), _ptr(q), _ptr(w), k.c(), int(q.shape[1]), int(q.shape[2]),
                          _ptr(cand), _ptr(cand_count), 0 if cand is None else int(cand.stride(0)),
                          0, _ptr(scores), int(scores.stride(0)))
@@ -213,6 +231,11 @@ def index_score(rows: Rows, q: torch.Tensor, w: torch.Tensor, k: Cache,
 
 def topk_desc(rows: Rows, scores, k: int, idx, count, cand=None, cand_count=None, block=0,
               max_blocks=0, pool=None, pool_count=None) -> sa_topk_desc:
+    _dense(scores, "scores", rows=True)
+    for t, n in ((idx, "idx"), (cand, "cand"), (pool, "pool")):
+        _dense(t, n, rows=True)
+    for t, n in ((count, "count"), (cand_count, "cand_count"), (pool_count, "pool_count")):
+        _dense(t, n)
     return sa_topk_desc(rows.c(), _ptr(scores), int(scores.stride(0)), _ptr(cand), _ptr(cand_count),
                         0 if cand is None else int(cand.stride(0)), int(k), _ptr(idx), _ptr(count),
                         0 if idx is None else int(idx.stride(0)), int(block), int(max_blocks),
@@ -244,6 +267,28 @@ def topk_select(rows: Rows, scores: torch.Tensor, k: int, cand=None, cand_count=
     return idx, count
 
 
+CHECK_CODES = {1: "count out of range", 2: "index outside the row's candidates",
+               3: "indices not strictly ascending", 4: "padding slot not -1"}
+
+
+def check_indices(rows: Rows, idx: torch.Tensor, count: torch.Tensor, k: Optional[int] = None,
+                  candidate_mode: bool = False):
+    """Check an index tensor on the device (sparse_check_indices) and raise
+    SAError naming the first failing row; synchronises the stream."""
+    L = load()
+    k = int(idx.shape[1]) if k is None else int(k)
+    _dense(idx, "idx", rows=True)
+    _dense(count, "count")
+    cand = count if candidate_mode else None  # only its presence is read
+    d = topk_desc(rows, idx, k, idx, count, cand=cand, cand_count=count)
+    err = torch.empty(1, dtype=torch.int32, device=idx.device)
+    _check(L.sparse_check_indices(ctypes.byref(d), _ptr(err), _stream()))
+    word = int(err.item()) & 0xFFFFFFFF
+    if word != 0xFFFFFFFF:
+        raise SAError("index check failed at row %d: %s" % (word >> 3,
+                                                           CHECK_CODES.get(word & 7, "?")))
+
+
 def attn_desc(rows: Rows, q, k: Cache, v: Optional[Cache], idx, count, o, lse=None,
               scale: Optional[float] = None, d_v: Optional[int] = None) -> sa_attn_desc:
     n_qsets, R, hq, dqk = (int(x) for x in q.shape)
@@ -251,6 +296,9 @@ def attn_desc(rows: Rows, q, k: Cache, v: Optional[Cache], idx, count, o, lse=No
         d_v = v.width if v is not None else k.width
     if scale is None:
         scale = dqk ** -0.5
+    for t, n in ((q, "q"), (o, "o"), (lse, "lse"), (count, "count")):
+        _dense(t, n)
+    _dense(idx, "idx", rows=True)
     vc = v.c() if v is not None else sa_cache()
     return sa_attn_desc(rows.c(), n_qsets, hq, _ptr(q), _dt(q), int(d_v), k.c(), vc,
                         1 if v is None else 0, 0 if idx is None else int(idx.stride(0)), _ptr(idx),
@@ -300,11 +348,10 @@ class Prepared:
         if need == ctypes.c_size_t(-1).value:
             _check(-2)
         if need and workspace is not None and workspace.numel() >= need:
-            # shared with calls of the same entry point that never overlap in time
+            # shared with calls that never overlap in time
             self.ws = workspace
         else:
-            # zero-filled: the selection requires it on first use
-            self.ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=device) if need else None
+            self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device) if need else None
         self.ws_ptr = _ptr(self.ws)
         self.need = need
         self.keep = keep

@@ -338,6 +338,28 @@ sa_status sparse_attn_gather_fwd(const sa_attn_desc* desc, void* ws, size_t ws_b
   return hip_status(sa::launch_attn_gather(a, (hipStream_t)stream), "sparse_attn_gather_fwd");
 }
 
+sa_status sparse_check_indices(const sa_topk_desc* desc, uint32_t* err, void* stream) {
+  const char* op = "sparse_check_indices";
+  CHECK(desc, SA_ERR_NULL, "%s: desc is NULL", op);
+  CHECK(err, SA_ERR_NULL, "%s: err is NULL", op);
+  sa_status st = check_rows(desc->rows, op);
+  if (st) return st;
+  CHECK(desc->k >= 1, SA_ERR_SHAPE, "%s: k must be >= 1", op);
+  if (desc->rows.n_rows > 0) {
+    CHECK(desc->idx && desc->count, SA_ERR_NULL, "%s: idx and count are required", op);
+    CHECK(desc->idx_stride >= desc->k, SA_ERR_SHAPE, "%s: idx_stride < k", op);
+  }
+  sa::CheckArgs a;
+  a.rows = to_dev(desc->rows);
+  a.idx = desc->idx;
+  a.count = desc->count;
+  a.err = err;
+  a.idx_stride = desc->idx_stride;
+  a.k = desc->k;
+  a.candidate_mode = desc->cand != nullptr;
+  return hip_status(sa::launch_check_indices(a, (hipStream_t)stream), op);
+}
+
 size_t sa_workspace_size(int32_t op, const void* desc) {
   switch (op) {
     case SA_OP_INDEX_SCORE:

@@ -87,6 +87,9 @@ __device__ __forceinline__ void fp4_dequant32(u32x4 codes, uint32_t s0, uint32_t
 }
 
 constexpr int kMaxEntries = 2048;  // entries per workgroup (slot table size)
+// Splits per row: attn_combine gives each split one lane of a wave.  The
+// entry limit of a call (131072 = 64 x kMaxEntries) never needs more.
+constexpr int kMaxSplits = 64;
 
 // Work shape of one workgroup: W waves per entry group, each owning one
 // 16-row query tile, and NG entry groups that walk disjoint tiles of the
@@ -1269,7 +1272,7 @@ void attn_plan(AttnArgs& a) {
   // workgroups, but take at least 4 splits (measured on 8 and 16 rows of 64
   // heads over 512 entries)
   const int cap = a.dv >= 512 ? (int)max((int64_t)4, (64 + base - 1) / base) : max_split;
-  while (ns < max_split && ns < cap && base * ns < 256) ++ns;
+  while (ns < max_split && ns < cap && ns < kMaxSplits && base * ns < 256) ++ns;
   a.n_split = ns < 1 ? 1 : ns;
 }
 

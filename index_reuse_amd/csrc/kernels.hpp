@@ -79,4 +79,17 @@ size_t attn_workspace_bytes(const AttnArgs& a);
 void attn_plan(AttnArgs& a);  // fills n_split
 hipError_t launch_attn_gather(const AttnArgs& a, hipStream_t s);
 
+// ------------------------------------------------------------ index check
+enum : uint32_t { kCheckCount = 1, kCheckDomain = 2, kCheckOrder = 3, kCheckPadding = 4 };
+struct CheckArgs {
+  RowsDev rows;
+  const int32_t* idx;   // [R][idx_stride]
+  const int32_t* count; // [R]
+  uint32_t* err;        // one word: (row << 3) | code of the first failure, or ~0
+  int32_t idx_stride;
+  int32_t k;
+  int32_t candidate_mode;  // 1: entries anywhere in [0, n_avail) outside the window
+};
+hipError_t launch_check_indices(const CheckArgs& a, hipStream_t s);
+
 }  // namespace sa

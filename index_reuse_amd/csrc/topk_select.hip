@@ -135,7 +135,7 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 
 // Workspace views (see topk_workspace_bytes).
 struct Ws {
-  uint32_t* hist;  // [R][kHistStride], zero on entry, left zero
+  uint32_t* hist;  // [R][kHistStride], cleared by each chunk-path call
   uint32_t* rec;   // [R][kRecWords]
   uint32_t* mkey;  // [R][kCapM] member keys
   int32_t* midx;   // [R][kCapM] member element indices
@@ -356,6 +356,16 @@ __device__ __forceinline__ int block_sum(int v, int* wred) {
   return t;
 }
 
+// ---------------------------------------------------- 0b. clear the counts
+// The row histograms (and valid counts) of the call's rows start at zero:
+// cleared here by a fill kernel rather than assumed on entry, so a workspace
+// carries nothing from one call to the next (any call may share it with any
+// other that does not overlap in time, whatever their row counts).
+__global__ __launch_bounds__(256) void zero_hist_kernel(Ws ws, int64_t n_vec) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n_vec) reinterpret_cast<u32x4*>(ws.hist)[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
 // -------------------------------------------------------------- 1. hist
 // Level-1 histogram (key bits 31..20) of one chunk, merged into the row's;
 // chunk 0 also resets the row's record for the scan step.
@@ -540,10 +550,6 @@ __global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int 
   const uint32_t mmin = rec[REC_MMIN], mmax = rec[REC_MMAX];
   const int32_t* cgt = ws.cgt + (int64_t)r * ws.chunk_stride;
   const int32_t* cm = ws.cm + (int64_t)r * ws.chunk_stride;
-  if (c == 0) {  // the histogram is not read after the scan step: leave it zero
-    uint32_t* gh = ws.hist + (int64_t)r * kHistStride;
-    for (int i = tid; i < kHistStride; i += kChunkT) gh[i] = 0u;
-  }
 
   // theta, the theta-ties to keep (t_eq) and, for this chunk, the kept
   // elements before it (offset) and the theta-ties before it (e_before)
@@ -1089,6 +1095,10 @@ void run_select_chunk(const SelectArgs& a, const Ws& ws, int64_t max_n, int kk, 
   const int R = a.rows.n_rows;
   int64_t nchunks = (max_n + CHUNK - 1) / CHUNK;
   dim3 gc((unsigned)(nchunks > 0 ? nchunks : 1), R);
+  static_assert(kHistStride % 4 == 0, "whole 16-byte vectors per row histogram");
+  const int64_t n_vec = (int64_t)R * kHistStride / 4;
+  hipLaunchKernelGGL(zero_hist_kernel, dim3((unsigned)((n_vec + 255) / 256)), dim3(256), 0, st, ws,
+                     n_vec);
   hipLaunchKernelGGL((hist_kernel<KIND, CHUNK>), gc, dim3(kChunkT), 0, st, a, ws);
   hipLaunchKernelGGL((scan_kernel<KIND, CHUNK>), gc, dim3(kChunkT), 0, st, a, ws, kk);
   hipLaunchKernelGGL((emit_kernel<KIND, CHUNK>), gc, dim3(kChunkT), 0, st, a, ws, pool_mode);
@@ -1133,7 +1143,7 @@ size_t topk_workspace_bytes(const SelectArgs& a) {
   return b;
 }
 
-// Workspace: level-1 histograms [R][kHistStride] (zero on entry, left zero),
+// Workspace: level-1 histograms [R][kHistStride] (cleared by the call),
 // per-row records, member lists, per-chunk counts, then (pool mode) block
 // maxima.
 hipError_t launch_topk_select(const SelectArgs& a, hipStream_t st) {

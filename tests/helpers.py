@@ -113,11 +113,22 @@ def fp32_score_bound(prob, layer=0, rows=None):
     return tau
 
 
+def win_lo(prob, window=None):
+    """First window entry of every row (the candidates of token-mode
+    selection are [0, win_lo)), from the oracle's domain rule."""
+    so, po, sl = rows_np(prob)
+    n = oracle.n_avail(so, po, sl, prob.wl.stride)
+    w = prob.wl.window if window is None else window
+    return np.maximum(n - w, 0)
+
+
 def check_indices(gpu_idx, gpu_cnt, ora_idx, ora_cnt, ora_scores=None, tau=None, rows=None,
-                  positions=None):
+                  positions=None, win_lo=None):
     """Index sets: bit-exact when ``tau`` is None; otherwise equal counts and
     every symmetric-difference element within 2*tau of the k-th oracle score.
-    Returns the number of boundary swaps."""
+    Every index before the count must lie in the row's candidate domain:
+    0 <= s < win_lo[r] (when given) and, in candidate mode, a member of the
+    row's list ``positions[r]``.  Returns the number of boundary swaps."""
     gi = np.asarray(gpu_idx)
     gc = np.asarray(gpu_cnt)
     oi = np.asarray(ora_idx)
@@ -125,10 +136,18 @@ def check_indices(gpu_idx, gpu_cnt, ora_idx, ora_cnt, ora_scores=None, tau=None,
     swaps = 0
     for r in range(oi.shape[0]) if rows is None else rows:
         assert gc[r] == oc[r], "row %d: count %d vs oracle %d" % (r, gc[r], oc[r])
+        assert 0 <= gc[r] <= gi.shape[1], "row %d: count %d out of range" % (r, gc[r])
         g = gi[r, :gc[r]]
         o = oi[r, :oc[r]]
         assert np.all(gi[r, gc[r]:] == -1), "row %d: padding not -1" % r
         assert np.all(np.diff(g) > 0), "row %d: not ascending/unique" % r
+        assert np.all(g >= 0), "row %d: negative index before the count" % r
+        if win_lo is not None:
+            assert np.all(g < win_lo[r]), "row %d: index outside the candidates [0, %d)" % (
+                r, win_lo[r])
+        if positions is not None:
+            members = np.asarray(positions[r])
+            assert np.all(np.isin(g, members[members >= 0])), "row %d: index not in its list" % r
         if tau is None:
             assert np.array_equal(g, o), "row %d: index sets differ" % r
             continue

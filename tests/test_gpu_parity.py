@@ -81,10 +81,12 @@ def test_index_and_select(name, dev):
         assert np.all(err[valid] <= np.broadcast_to(tau[:, None], sc.shape)[valid])
     if not wl.block:
         idx, cnt = H.oracle_select(prob, sc, wl.k)
-        H.check_indices(step.idx[0].cpu(), step.count[0].cpu(), idx, cnt, sc, tau)
+        H.check_indices(step.idx[0].cpu(), step.count[0].cpu(), idx, cnt, sc, tau,
+                        win_lo=H.win_lo(prob))
         return
     idx, cnt, pool, pc = H.oracle_select(prob, sc, wl.k, block=wl.block, max_blocks=wl.max_blocks)
-    H.check_indices(step.idx[0].cpu(), step.count[0].cpu(), idx, cnt, sc, tau)
+    H.check_indices(step.idx[0].cpu(), step.count[0].cpu(), idx, cnt, sc, tau,
+                    win_lo=H.win_lo(prob))
     gpool, gpc = step.pool.cpu().numpy(), step.pool_count.cpu().numpy()
     if integer:
         assert np.array_equal(gpc, pc)
@@ -101,7 +103,7 @@ def test_index_and_select(name, dev):
     ridx, rcnt = H.oracle_select(prob, rs, wl.k, cand=pool, cand_count=pc)
     tau1 = None if integer else H.fp32_score_bound(prob, 1)
     H.check_indices(step.idx[1].cpu(), step.count[1].cpu(), ridx, rcnt, rs, tau1, rows=same,
-                    positions=pool)
+                    positions=pool, win_lo=H.win_lo(prob))
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -272,7 +274,8 @@ def test_dsa_rows_fp8_latent(dev):
             tau = H.fp32_score_bound(prob, 0)
         idx, cnt = H.oracle_select(prob, sc, wl.k)
         assert list(cnt) == [min(2048, t + 1) for t in DSA_ROWS]
-        H.check_indices(step.idx[0].cpu(), step.count[0].cpu(), idx, cnt, sc, tau)
+        H.check_indices(step.idx[0].cpu(), step.count[0].cpu(), idx, cnt, sc, tau,
+                        win_lo=H.win_lo(prob))
         step.run_attention(idx=[torch.from_numpy(idx).to(dev)], count=[torch.from_numpy(cnt).to(dev)])
         torch.cuda.synchronize()
         o_ref, l_ref = H.oracle_attention(prob, 0, idx, cnt)
@@ -640,7 +643,7 @@ def test_full_size_decode(name, integer, dev):
     if wl.block:
         idx, cnt, pool, pc = H.oracle_select(cpu, sc, wl.k, block=wl.block,
                                              max_blocks=wl.max_blocks)
-        H.check_indices(gi[0], gc[0], idx, cnt, sc, tau)
+        H.check_indices(gi[0], gc[0], idx, cnt, sc, tau, win_lo=H.win_lo(cpu))
         gpool, gpc = step.pool.cpu().numpy(), step.pool_count.cpu().numpy()
         pool_same = [r for r in range(R) if gpc[r] == pc[r] and np.array_equal(gpool[r], pool[r])]
         if integer:
@@ -656,13 +659,14 @@ def test_full_size_decode(name, integer, dev):
             else:
                 assert np.all(np.abs(gr[r, v] - rs[r, v]) <= tau1[r])
         ridx, rcnt = H.oracle_select(cpu, rs, wl.k, cand=pool, cand_count=pc)
-        H.check_indices(gi[1], gc[1], ridx, rcnt, rs, tau1, rows=pool_same, positions=pool)
+        H.check_indices(gi[1], gc[1], ridx, rcnt, rs, tau1, rows=pool_same, positions=pool,
+                        win_lo=H.win_lo(cpu))
         oidx, ocnt = [idx, ridx], [cnt, rcnt]
         same = [sorted(set(_same_rows(gi[0], gc[0], idx, cnt))),
                 sorted(set(_same_rows(gi[1], gc[1], ridx, rcnt)) & set(pool_same))]
     else:
         idx, cnt = H.oracle_select(cpu, sc, wl.k)
-        H.check_indices(gi[0], gc[0], idx, cnt, sc, tau)
+        H.check_indices(gi[0], gc[0], idx, cnt, sc, tau, win_lo=H.win_lo(cpu))
         oidx, ocnt = [idx], [cnt]
         same = [_same_rows(gi[0], gc[0], idx, cnt)]
     for c in range(len(cpu.q)):
@@ -675,7 +679,21 @@ def test_full_size_decode(name, integer, dev):
                         what="%s call %d rows %s" % (name, c, rows))
 
 
-DSA_FULL_ROWS = [0, 1, 2046, 2047, 2048, 8191, 8192, 30001, 49152, 65535]
+def _dsa_full_rows():
+    """128 sampled rows of the 64K prefill: the first and last row of every
+    8192-row block, both sides of the budget edge (t + 1 = 2048), and rows
+    drawn uniformly from the rest (fixed seed)."""
+    rows = set()
+    for b in range(8):
+        rows |= {8192 * b, 8192 * b + 8191}
+    rows |= {1, 2, 2046, 2047, 2048, 2049, 30001, 49152}
+    rng = np.random.default_rng(2026)
+    while len(rows) < 128:
+        rows.add(int(rng.integers(0, 65536)))
+    return sorted(rows)
+
+
+DSA_FULL_ROWS = _dsa_full_rows()
 
 
 @pytest.mark.parametrize("integer", [True, False])
@@ -701,7 +719,7 @@ def test_full_size_prefill(integer, dev):
     assert max(rows) < step.idx.shape[0] == step.count.shape[0] == step.R
     gi = step.idx.cpu().numpy()[rows]
     gc = step.count.cpu().numpy()[rows]
-    H.check_indices(gi, gc, idx, cnt, sc, tau)
+    H.check_indices(gi, gc, idx, cnt, sc, tau, win_lo=H.win_lo(sub))
     same = _same_rows(gi, gc, idx, cnt)
     if integer:
         assert len(same) == len(rows)
@@ -715,3 +733,110 @@ def test_full_size_prefill(integer, dev):
     sel = torch.tensor(pick, dtype=torch.long, device=step.o.device)
     H.check_outputs(step.o.index_select(1, sel), o_ref, step.lse.index_select(1, sel), l_ref,
                     wl.attn_dtype, what="dsa rows %s" % pick)
+
+
+@pytest.mark.parametrize("hkv", [1, 2])
+def test_attention_many_splits_single_row(hkv, dev):
+    """One decode row with window + top-k far above one workgroup's 2048
+    entries and few KV heads: the planner wants more than 64 entry splits,
+    and must stop at the 64 the split merge handles."""
+    wl = synth.HYSPARSE2.replace(n_seqs=1, seq_lens_override=(9000,), k=4096, hq=8 * hkv,
+                                 hkv=hkv, n_qsets=1)
+    prob = synth.make_problem(wl, device="cpu")
+    _flush("case many splits hkv=%d" % hkv)
+    p, step = _step(prob, dev)
+    sc = H.oracle_scores(prob, 0)
+    idx, cnt = H.oracle_select(prob, sc, wl.k)
+    assert cnt[0] == 4096
+    step.run_attention(idx=[torch.from_numpy(idx).to(dev)], count=[torch.from_numpy(cnt).to(dev)])
+    torch.cuda.synchronize()
+    o_ref, l_ref = H.oracle_attention(prob, 0, idx, cnt)
+    H.check_outputs(step.o[0], o_ref, step.lse[0], l_ref, torch.bfloat16, what="splits")
+
+
+def test_reindex_leaves_caches_unchanged(dev):
+    """A Reindex layer only rescores and reselects: after a whole CSA2 layer
+    group (Full, Reindex, Reuse) the index-key cache and the main KV are
+    bitwise what they were ("CSA, HCA and CSA2", section 5.1: Reindex writes
+    no KV)."""
+    wl, _ = CASES["csa2"]
+    p, step = _step(synth.make_problem(wl, device="cpu"), dev)
+    before = [p.kidx.pool.clone(), p.k.pool.clone(), p.k.scale.clone()]
+    step.run()
+    torch.cuda.synchronize()
+    for a, b in zip(before, [p.kidx.pool, p.k.pool, p.k.scale]):
+        assert torch.equal(a, b)
+
+
+def test_select_workspace_shared_across_row_counts(dev):
+    """Chunk-path selections (rows longer than 65536 elements) of different
+    row counts share one workspace, in alternation: every result stays
+    bit-exact (nothing a call leaves in the workspace reaches the next)."""
+    from index_reuse_amd import Rows
+    from index_reuse_amd.binding import prepare_topk_select
+
+    import oracle
+
+    calls = []
+    for R, S, seed in ((5, 70000, 301), (3, 100000, 302), (2, 80000, 303)):
+        scores = synth.small_ints((R, S), seed=seed, lo=-30, hi=30)
+        scores[scores == 0] = -0.0
+        so = torch.zeros(R, dtype=torch.int32)
+        po = torch.tensor([S - 1 - 11 * r for r in range(R)], dtype=torch.int32)
+        sl = torch.tensor([S], dtype=torch.int32)
+        ref = oracle.topk_select(so, po, sl, 1, 16, scores.double().numpy(), 3000)
+        rows = Rows(so.to(dev), po.to(dev), sl.to(dev), 1, 16)
+        idx = torch.empty(R, 3000, dtype=torch.int32, device=dev)
+        cnt = torch.empty(R, dtype=torch.int32, device=dev)
+        calls.append((rows, scores.to(dev), idx, cnt, ref))
+    shared = None
+    prepared = []
+    for rows, sc, idx, cnt, ref in calls:
+        pc = prepare_topk_select(rows, sc, 3000, idx, cnt)
+        prepared.append(pc)
+        if shared is None or pc.need > shared.numel():
+            shared = torch.full((pc.need,), 0x5A, dtype=torch.uint8, device=dev)
+    for pc in prepared:
+        pc.ws, pc.ws_ptr = shared, shared.data_ptr()
+    for rep in range(2):
+        for pc, (rows, sc, idx, cnt, ref) in zip(prepared, calls):
+            idx.fill_(7)
+            pc()
+            torch.cuda.synchronize()
+            assert np.array_equal(cnt.cpu().numpy(), ref[1]), rep
+            assert np.array_equal(idx.cpu().numpy(), ref[0]), rep
+
+
+def test_check_indices_device(dev):
+    """The device-side index check passes the oracle's selections and names
+    the first bad row for planted mistakes (an index shifted into the window,
+    a descending pair, a count above k, a padding slot, a padding row that
+    leaked a count)."""
+    from index_reuse_amd import SAError, check_indices
+
+    wl, integer, prob = _problem("hysparse2_int")
+    p, step = _step(prob, dev)
+    sc = H.oracle_scores(prob, 0)
+    idx, cnt = H.oracle_select(prob, sc, wl.k)
+    rows = step.rows
+    check_indices(rows, torch.from_numpy(idx).to(dev), torch.from_numpy(cnt).to(dev))
+    wlo = H.win_lo(prob)
+    r0 = int(np.argmax(cnt))
+    cases = []
+    a = idx.copy()
+    a[r0, cnt[r0] - 1] = wlo[r0]
+    cases.append((a, cnt, r0, "outside"))
+    a = idx.copy()
+    a[r0, 0], a[r0, 1] = a[r0, 1], a[r0, 0]
+    cases.append((a, cnt, r0, "ascending"))
+    c = cnt.copy()
+    c[r0] = wl.k + 1
+    cases.append((idx, c, r0, "count"))
+    r1 = int(np.argmin(cnt))
+    a = idx.copy()
+    a[r1, wl.k - 1] = 3
+    cases.append((a, cnt, r1, "padding slot" if cnt[r1] < wl.k else "ascending"))
+    for bad_idx, bad_cnt, row, what in cases:
+        with pytest.raises(SAError, match="row %d: .*%s" % (row, what)):
+            check_indices(rows, torch.from_numpy(np.ascontiguousarray(bad_idx)).to(dev),
+                          torch.from_numpy(np.ascontiguousarray(bad_cnt)).to(dev))

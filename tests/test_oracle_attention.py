@@ -167,3 +167,50 @@ def test_window_union_counts_once(orc):
     b, _ = orc.attention(so, po, sl, 1, 3, q, K, V, np.array([[2, 5, 10, 11]], np.int32),
                          np.array([4], np.int32), scale=0.3)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("window", [0, 7])
+def test_latent_v_from_k_equals_dense(orc, window):
+    """Latent rows (MLA, "Lecture 10", section 5.1): K is the whole row of
+    d_qk channels and V its first d_v < d_qk channels.  With the budget
+    covering every candidate, the oracle's v_from_k branch must equal dense
+    causal attention whose V is the slice K[..., :d_v], here through torch's
+    SDPA in float64.  d_qk = 40 and d_v = 24 keep a row-stride mix-up between
+    the two widths visible (every row after the first would be misread)."""
+    g = torch.Generator().manual_seed(70 + window)
+    L, Hq, dqk, dv, S = 30, 4, 40, 24, 2
+    q = torch.randn(S, L, Hq, dqk, generator=g).to(torch.bfloat16)
+    K = torch.randn(1, L, 1, dqk, generator=g).to(torch.bfloat16)
+    so, po, sl = np.zeros(L, np.int32), np.arange(L, dtype=np.int32), np.array([L], np.int32)
+    idx = np.full((L, L), -1, np.int32)
+    cnt = np.zeros(L, np.int32)
+    for t in range(L):
+        c = list(range(max(0, t + 1 - window)))
+        idx[t, :len(c)] = c
+        cnt[t] = len(c)
+    scale = float(np.float32(1.0 / math.sqrt(dqk)))
+    o, lse = orc.attention(so, po, sl, 1, window, q, K, None, idx, cnt, scale=scale,
+                           v_from_k=True, dv=dv)
+    assert o.shape == (S, L, Hq, dv)
+    ref, rlse = _sdpa_dense(q.double(), K[0].double(), K[0, :, :, :dv].double().contiguous(),
+                            list(range(L)), 1, scale)
+    assert np.allclose(o, ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse, rlse, rtol=1e-12, atol=1e-12)
+
+
+def test_latent_576_512_single_entry(orc):
+    """At the C3 widths (576 / 512): a row that sees one entry returns the
+    first 512 channels of that latent row exactly, and two rows with equal
+    logits return the mean of the visible rows' first 512 channels."""
+    g = torch.Generator().manual_seed(72)
+    L, Hq = 6, 3
+    K = torch.randn(1, L, 1, 576, generator=g).to(torch.bfloat16)
+    q = torch.randn(1, 2, Hq, 576, generator=g).to(torch.bfloat16)
+    q[0, 1] = 0
+    so, po, sl = np.zeros(2, np.int32), np.array([0, L - 1], np.int32), np.array([L], np.int32)
+    o, _ = orc.attention(so, po, sl, 1, L, q, K, None, None, None, scale=576 ** -0.5,
+                         v_from_k=True, dv=512)
+    first = K[0, 0, 0, :512].double().numpy()
+    assert np.array_equal(o[0, 0], np.repeat(first[None], Hq, 0))
+    mean = K[0, :, 0, :512].double().mean(0).numpy()
+    assert np.allclose(o[0, 1], np.repeat(mean[None], Hq, 0), rtol=1e-14, atol=1e-14)
