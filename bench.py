@@ -85,10 +85,19 @@ def algorithmic_bytes(step, name: str) -> float:
         return c * 4 + R * (wl.k + 1) * 4
     if name == "topk_select_reindex":  # pool scores and positions -> top-k
         return pool_n * 8 + R * (wl.k + 1) * 4
-    if name.startswith("attn_gather_fwd"):
-        call = 0 if name == "attn_gather_fwd" else int(name.rsplit("_", 1)[1])
-        sets = p.q[call].shape[0]
+    fa = hasattr(step, "q_sa")  # HySparse2's FA layer group (FAStep)
+    if name == "attn_score":  # every visible K row, queries, lse, one score per entry
+        n = sum(g[0] for g in geo)
         ae = _elem(wl.attn_dtype)
+        return n * (wl.hkv * wl.dqk * ae + 4) + R * wl.hq * (wl.dqk * ae + 4)
+    if name.startswith("attn_gather_fwd"):
+        ae = _elem(wl.attn_dtype)
+        if fa and name == "attn_gather_fwd_fa":  # dense: every visible entry, the FA set
+            n_e = sum(g[0] for g in geo)
+            row = wl.hkv * (wl.dqk + wl.dv) * ae if p.v is not None else wl.hkv * wl.dqk * ae
+            return n_e * row + R * wl.hq * (wl.dqk + wl.dv) * ae + R * wl.hq * 4
+        call = 0 if name in ("attn_gather_fwd", "attn_gather_fwd_fa") else int(name.rsplit("_", 1)[1])
+        sets = step.q_sa.shape[0] if fa else p.q[call].shape[0]
         if wl.kv_mode == "fp4":
             row = wl.hkv * (wl.dqk // 2 + wl.dqk // 16)
         elif wl.kv_mode == "shared":
@@ -253,6 +262,51 @@ def cpu_baseline(step, n_rows: int, min_seconds: float):
                           sum(x.shape[0] for x in q), dt)}
 
 
+def fa_cpu_baseline(step, n_rows: int, min_seconds: float):
+    """The fp64 oracle for HySparse2's FA layer group on the first ``n_rows``
+    decode rows: dense attention for the FA set, its head-summed selection
+    score, window + top-k, and sparse attention for the SA sets; repeated
+    until ``min_seconds`` of host time have elapsed."""
+    import numpy as np
+
+    import oracle
+
+    wl, p = step.wl, step.prob
+    rows = list(range(n_rows))
+    seqs = sorted({int(p.seq_of_row[r]) for r in rows})
+    remap = {b: i for i, b in enumerate(seqs)}
+    so = np.array([remap[int(p.seq_of_row[r])] for r in rows], np.int32)
+    po = p.pos_of_row[rows].cpu().numpy().astype(np.int32)
+    sl = p.seq_len[seqs].cpu().numpy().astype(np.int32)
+    cap = wl.n_entries_cap
+
+    def logical(c):
+        return oracle.unpage(c.pool, c.block_table[seqs], c.page_size, len(seqs), cap)
+
+    K, V = logical(p.k), logical(p.v)
+    q = p.q[0][:, rows].cpu()
+    scale = float(np.float32(wl.dqk ** -0.5))
+    geo = (so, po, sl, wl.stride)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.attention(*geo, cap, q[0:1], K, V, None, None, scale=scale)
+        sc = oracle.fa_score(*geo, q[0:1], K, scale=scale)
+        idx, cnt = oracle.topk_select(*geo, wl.window, sc, wl.k)
+        oracle.attention(*geo, wl.window, q[1:], K, V, idx, cnt, scale=scale)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    queries = reps * n_rows * q.shape[0]
+    return {"value": round(queries / dt, 3), "unit": "queries/s", "cores": oracle.num_threads(),
+            "cpu": cpu_model(), "kind": "oracle",
+            "sample": "%d pass(es) over %d of %d decode rows of one replica (whole group: dense FA "
+                      "attention over %d entries/row, its selection score, select, sparse "
+                      "attention for %d SA sets), %.1f s" % (
+                          reps, n_rows, p.n_rows, int(sl.max()), q.shape[0] - 1, dt)}
+
+
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}  # MI355X dense
 
 
@@ -414,19 +468,20 @@ def run_prefill(args, wl):
     return out
 
 
-def run_decode(args, wl):
+def run_decode(args, wl, fa: bool = False):
     """Decode: one step = every call of the workload's layer group on all its
-    rows; returns the JSON record."""
+    rows (``fa``: HySparse2's FA layer selects from its own dense attention
+    instead of an indexer); returns the JSON record."""
     import torch
 
     import synth
-    from index_reuse_amd.pipeline import Step
+    from index_reuse_amd.pipeline import FAStep, Step
 
     dev = torch.device("cuda:0")
     steps = []
     for i in range(args.replicas):
         prob = synth.make_problem(wl, device=dev, seed_base=1000 * (wl.cfg_id + 1) + 100 * i)
-        steps.append(Step(prob))
+        steps.append(FAStep(prob) if fa else Step(prob))
     calls = [s.prepare() for s in steps]
     names = [n for n, _ in calls[0]]
     stream = torch.cuda.current_stream().cuda_stream
@@ -523,11 +578,13 @@ def run_decode(args, wl):
         "vs_baseline": None,
         "dtype": "fp4 kv, bf16" if wl.kv_mode == "fp4" else "bf16",
         "data": "synthetic",
-        "config": {"workload": "%s_decode" % wl.name, "batch": wl.n_seqs,
+        "config": {"workload": "%s%s_decode" % (wl.name, "_fa" if fa else ""), "batch": wl.n_seqs,
                    "context": wl.seq_len, "window": wl.window, "topk": wl.k,
                    "query_sets": sum(q.shape[0] for q in step0.prob.q), "kv_heads": wl.hkv,
-                   "q_heads": wl.hq, "head_dim": wl.dqk, "indexer": "%dx%d %s" % (
-                       wl.idx_heads, wl.idx_dim, str(wl.idx_dtype).replace("torch.", "")),
+                   "q_heads": wl.hq, "head_dim": wl.dqk, "indexer": (
+                       "none: the FA layer's dense attention probabilities" if fa else
+                       "%dx%d %s" % (wl.idx_heads, wl.idx_dim,
+                                     str(wl.idx_dtype).replace("torch.", ""))),
                    "page_size": wl.page_size, "replicas": args.replicas, "launch": mode},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -547,14 +604,17 @@ def run_decode(args, wl):
         out["index_comparisons_per_query"] = {"hierarchical": int(hier), "flat": int(flat)}
     if not args.no_cpu:
         n = args.cpu_rows if args.cpu_rows > 0 else step0.prob.n_rows
-        out["cpu_baseline"] = cpu_baseline(step0, min(n, step0.prob.n_rows), args.cpu_seconds)
+        if fa:
+            out["cpu_baseline"] = fa_cpu_baseline(step0, args.cpu_rows or 2, args.cpu_seconds)
+        else:
+            out["cpu_baseline"] = cpu_baseline(step0, min(n, step0.prob.n_rows), args.cpu_seconds)
     del steps, calls, step0
     torch.cuda.empty_cache()
     return out
 
 
 # Extra workloads measured by the default run, next to the headline decode.
-EXTRA = ("csa", "csa2", "dsa")
+EXTRA = ("hysparse2_fa", "csa", "csa2", "dsa")
 
 
 def main():
@@ -563,8 +623,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
-                    help="hysparse2, csa, csa2, dsa, or all (the headline HySparse2 decode, with "
-                         "the other workloads as extra records)")
+                    help="hysparse2, hysparse2_fa, csa, csa2, dsa, or all (the headline "
+                         "HySparse2 decode, with the other workloads as extra records)")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="decode rows for the oracle baseline (default: all rows of a step)")
@@ -597,9 +657,10 @@ def main():
         calibration_copy(args.copy_mib)
 
     def run(name):
-        wl = synth.WORKLOADS[name]
+        fa = name.endswith("_fa")
+        wl = synth.WORKLOADS[name[:-3] if fa else name]
         t = time.perf_counter()
-        rec = run_prefill(args, wl) if wl.prefill else run_decode(args, wl)
+        rec = run_prefill(args, wl) if wl.prefill else run_decode(args, wl, fa=fa)
         print("# %s done in %.1f s" % (name, time.perf_counter() - t), file=sys.stderr, flush=True)
         return rec
 

@@ -279,6 +279,35 @@ sa_status sparse_attn_gather_fwd(const sa_attn_desc* desc, void* ws, size_t ws_b
                                  void* stream);
 
 /*
+ * sparse_attn_score -- the selection score of a full-attention layer
+ * ["HySparse2", appendix A.1: the FA layer runs ordinary full attention and
+ * picks the important history positions from its own attention scores, and
+ * its SA layers reuse them; "Lecture 10", section 5.2: the per-position
+ * target is the main attention summed over heads]:
+ *
+ *   scores[r][s] = sum_{i < n_qsets} sum_{h < n_heads_q}
+ *                  exp( scale * q[i][r][h][:] . K[s][g][:] - lse[i][r][h] )
+ *
+ * for every visible entry s < n_avail(r) (g = h / (n_heads_q / k.heads)):
+ * the probability each head gives s in dense attention over the row's
+ * visible entries, summed over heads.  `lse` must be that dense attention's
+ * log-normaliser, e.g. from sparse_attn_gather_fwd over the same rows with
+ * rows.window >= every n_avail and idx = NULL.  The scores then feed
+ * sparse_topk_select (window + top-k) like indexer scores do.
+ *
+ * Reads desc->rows (window ignored), n_qsets, n_heads_q, q, q_dtype, k, scale
+ * and lse; the V, index and output fields are ignored.
+ *   q       [n_qsets][R][n_heads_q][k.width], dtype = k.dtype (F32 or BF16)
+ *   scores  [R][score_stride] f32 out; slots s >= n_avail(r) are not written.
+ *           score_stride >= max n_avail.
+ * BF16 needs k.width 64 or 128, k.heads dividing 8 and n_qsets * (n_heads_q /
+ * k.heads) <= 16; F32 needs n_qsets * n_heads_q * (k.width + 1) <= 16384
+ * (SA_ERR_UNSUPPORTED otherwise).  Logits and sums are fp32 (MFMA for BF16).
+ */
+sa_status sparse_attn_score(const sa_attn_desc* desc, float* scores, int64_t score_stride,
+                            void* stream);
+
+/*
  * sparse_check_indices -- device-side check of an index tensor before it is
  * reused ("CSA, HCA and CSA2", section 5.1, fault injection: a Reuse layer's
  * indices shifted by one token, or a leaked row, must be caught by an

@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     SAError,
     abi_version,
     attn_gather_fwd,
+    attn_score,
     check_indices,
     index_score,
     load,

@@ -57,7 +57,8 @@ class sa_attn_desc(ctypes.Structure):
 
 
 EXPORTS = ("sparse_index_score", "sparse_topk_select", "sparse_attn_gather_fwd",
-           "sparse_check_indices", "sa_workspace_size", "sa_last_error", "sa_abi_version")
+           "sparse_attn_score", "sparse_check_indices", "sa_workspace_size", "sa_last_error",
+           "sa_abi_version")
 
 _lib = None
 
@@ -81,6 +82,8 @@ def load(path: str = LIB_PATH):
     L.sparse_index_score.argtypes = [ctypes.POINTER(sa_index_desc), _P, ctypes.c_size_t, _P]
     L.sparse_topk_select.argtypes = [ctypes.POINTER(sa_topk_desc), _P, ctypes.c_size_t, _P]
     L.sparse_attn_gather_fwd.argtypes = [ctypes.POINTER(sa_attn_desc), _P, ctypes.c_size_t, _P]
+    L.sparse_attn_score.restype = _i32
+    L.sparse_attn_score.argtypes = [ctypes.POINTER(sa_attn_desc), _P, _i64, _P]
     L.sparse_check_indices.restype = _i32
     L.sparse_check_indices.argtypes = [ctypes.POINTER(sa_topk_desc), _P, _P]
     L.sa_workspace_size.restype = ctypes.c_size_t
@@ -329,6 +332,30 @@ def attn_gather_fwd(rows: Rows, q: torch.Tensor, k: Cache, v: Optional[Cache] = 
     return o, lse
 
 
+def score_desc(rows: Rows, q, k: Cache, lse, scale: Optional[float] = None) -> sa_attn_desc:
+    """The attention descriptor fields sparse_attn_score reads."""
+    n_qsets, R, hq, dqk = (int(x) for x in q.shape)
+    if scale is None:
+        scale = dqk ** -0.5
+    _dense(q, "q")
+    _dense(lse, "lse")
+    return sa_attn_desc(rows.c(), n_qsets, hq, _ptr(q), _dt(q), dqk, k.c(), sa_cache(), 1, 0, None,
+                        None, float(scale), _dt(q), None, _ptr(lse))
+
+
+def attn_score(rows: Rows, q: torch.Tensor, k: Cache, lse: torch.Tensor, scores=None,
+               n_slots: Optional[int] = None, scale: Optional[float] = None):
+    """Full-attention selection scores [R, S] float32 (see sparse_attn_score);
+    ``lse`` is the dense attention's [n_qsets, R, hq] log-normaliser."""
+    L = load()
+    if scores is None:
+        scores = torch.empty(int(q.shape[1]), int(n_slots), dtype=torch.float32, device=q.device)
+    _dense(scores, "scores", rows=True)
+    d = score_desc(rows, q, k, lse, scale)
+    _check(L.sparse_attn_score(ctypes.byref(d), _ptr(scores), int(scores.stride(0)), _stream()))
+    return scores
+
+
 # ---------------------------------------------------------------------------
 # Prepared calls: descriptor and workspace built once, launch-only __call__
 # ---------------------------------------------------------------------------
@@ -373,6 +400,24 @@ def prepare_topk_select(rows: Rows, scores, k, idx, count, cand=None, cand_count
     return Prepared("sparse_topk_select", d, SA_OP_TOPK_SELECT, scores.device,
                     keep=(rows, scores, idx, count, cand, cand_count, pool, pool_count),
                     workspace=workspace)
+
+
+class PreparedScore:
+    """A validated sparse_attn_score call, launch-only."""
+
+    def __init__(self, rows: Rows, q, k: Cache, lse, scores, scale=None):
+        L = load()
+        self.fn = L.sparse_attn_score
+        _dense(scores, "scores", rows=True)
+        self.desc = score_desc(rows, q, k, lse, scale)
+        self.ref = ctypes.byref(self.desc)
+        self.scores_ptr = _ptr(scores)
+        self.stride = int(scores.stride(0))
+        self.keep = (rows, q, k, lse, scores)
+
+    def __call__(self, stream=None):
+        _check(self.fn(self.ref, self.scores_ptr, self.stride,
+                       _stream() if stream is None else stream))
 
 
 def prepare_attn_gather_fwd(rows: Rows, q, k: Cache, v: Optional[Cache], idx, count, o, lse=None,

@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
 
-SOURCES = ["abi.cpp", "index_score.hip", "topk_select.hip", "attn_gather.hip", "check_idx.hip"]
+SOURCES = ["abi.cpp", "index_score.hip", "topk_select.hip", "attn_gather.hip", "attn_score.hip",
+           "check_idx.hip"]
 HEADERS = ["common.hpp", "kernels.hpp"]
 
 ARCH = "gfx950"

@@ -338,6 +338,51 @@ sa_status sparse_attn_gather_fwd(const sa_attn_desc* desc, void* ws, size_t ws_b
   return hip_status(sa::launch_attn_gather(a, (hipStream_t)stream), "sparse_attn_gather_fwd");
 }
 
+sa_status sparse_attn_score(const sa_attn_desc* d, float* scores, int64_t score_stride,
+                            void* stream) {
+  const char* op = "sparse_attn_score";
+  CHECK(d, SA_ERR_NULL, "%s: desc is NULL", op);
+  sa_status st = check_rows(d->rows, op);
+  if (st) return st;
+  CHECK(d->n_qsets >= 1, SA_ERR_SHAPE, "%s: n_qsets must be >= 1", op);
+  const int hkv = d->k.heads, dqk = d->k.width;
+  CHECK(hkv >= 1 && d->n_heads_q >= hkv && d->n_heads_q % hkv == 0, SA_ERR_SHAPE,
+        "%s: n_heads_q must be a positive multiple of k.heads", op);
+  CHECK(d->k.dtype == SA_F32 || d->k.dtype == SA_BF16, SA_ERR_DTYPE, "%s: K must be F32 or BF16",
+        op);
+  CHECK(d->q_dtype == d->k.dtype, SA_ERR_DTYPE, "%s: q_dtype must match k.dtype", op);
+  if (d->k.dtype == SA_BF16) {
+    CHECK(dqk == 64 || dqk == 128, SA_ERR_UNSUPPORTED, "%s: BF16 needs k.width 64 or 128", op);
+    CHECK(8 % hkv == 0, SA_ERR_UNSUPPORTED, "%s: BF16 needs k.heads dividing 8", op);
+    CHECK(d->n_qsets * (d->n_heads_q / hkv) <= 16, SA_ERR_UNSUPPORTED,
+          "%s: BF16 needs n_qsets * (n_heads_q / k.heads) <= 16", op);
+  } else {
+    CHECK((int64_t)d->n_qsets * d->n_heads_q * (dqk + 1) <= 16384, SA_ERR_UNSUPPORTED,
+          "%s: F32 needs n_qsets * n_heads_q * (k.width + 1) <= 16384", op);
+  }
+  if (d->rows.n_rows == 0) return SA_OK;
+  CHECK(d->q && d->lse && scores, SA_ERR_NULL, "%s: q, lse and scores are required", op);
+  CHECK(aligned16(d->q), SA_ERR_SHAPE, "%s: q must be 16-byte aligned", op);
+  CHECK(score_stride >= 1, SA_ERR_SHAPE, "%s: score_stride must be >= 1", op);
+  st = check_cache(d->k, op, "k", (int64_t)hkv * dqk * elem_bytes(d->k.dtype));
+  if (st) return st;
+  sa::ScoreArgs a;
+  a.rows = to_dev(d->rows);
+  a.k = to_dev(d->k);
+  a.q = d->q;
+  a.lse = d->lse;
+  a.scores = scores;
+  a.score_stride = score_stride;
+  a.scale_log2 = d->scale * sa::kLog2e;
+  a.n_qsets = d->n_qsets;
+  a.hq = d->n_heads_q;
+  a.hkv = hkv;
+  a.dqk = dqk;
+  a.dtype = d->k.dtype;
+  a.n_slots = (int32_t)score_stride;
+  return hip_status(sa::launch_attn_score(a, (hipStream_t)stream), op);
+}
+
 sa_status sparse_check_indices(const sa_topk_desc* desc, uint32_t* err, void* stream) {
   const char* op = "sparse_check_indices";
   CHECK(desc, SA_ERR_NULL, "%s: desc is NULL", op);

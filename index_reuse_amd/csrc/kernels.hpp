@@ -79,6 +79,24 @@ size_t attn_workspace_bytes(const AttnArgs& a);
 void attn_plan(AttnArgs& a);  // fills n_split
 hipError_t launch_attn_gather(const AttnArgs& a, hipStream_t s);
 
+// ------------------------------------------------- full-attention score
+struct ScoreArgs {
+  RowsDev rows;
+  CacheDev k;
+  const void* q;        // [n_qsets][R][hq][dqk]
+  const float* lse;     // [n_qsets][R][hq] (natural log)
+  float* scores;        // [R][score_stride]
+  int64_t score_stride;
+  float scale_log2;     // softmax scale * log2(e)
+  int32_t n_qsets;
+  int32_t hq;
+  int32_t hkv;
+  int32_t dqk;
+  int32_t dtype;        // SA_F32 or SA_BF16
+  int32_t n_slots;      // score slots per row to cover (grid extent)
+};
+hipError_t launch_attn_score(const ScoreArgs& a, hipStream_t s);
+
 // ------------------------------------------------------------ index check
 enum : uint32_t { kCheckCount = 1, kCheckDomain = 2, kCheckOrder = 3, kCheckPadding = 4 };
 struct CheckArgs {

@@ -19,8 +19,9 @@ from typing import List, Optional
 
 import torch
 
-from .binding import (Cache, Rows, attn_gather_fwd, index_score, prepare_attn_gather_fwd,
-                      prepare_index_score, prepare_topk_select, topk_select)
+from .binding import (Cache, PreparedScore, Rows, attn_gather_fwd, index_score,
+                      prepare_attn_gather_fwd, prepare_index_score, prepare_topk_select,
+                      topk_select)
 
 
 def _cache(c, heads, width, fp4=False) -> Cache:
@@ -196,6 +197,65 @@ class PrefillStep:
                 self.o[:, lo:hi], self.lse[:, lo:hi], self.scale, wl.dv)))
         self._prepared = calls
         return calls
+
+    def run(self):
+        for _, c in self.prepare():
+            c()
+
+
+class FAStep:
+    """HySparse2's own layer group ("HySparse2" page, section 5 and appendix
+    A.1): the full-attention (FA) layer runs dense attention over every
+    visible entry and selects the window + top-k from its own attention
+    probabilities summed over heads; the sparse (SA) layers of the group reuse
+    that KV and that index tensor with their own queries.
+
+    Query set 0 of the problem's first query tensor is the FA layer's query;
+    sets 1.. are the SA layers'.  Calls: dense attention (FA) ->
+    sparse_attn_score -> window + top-k -> one gather attention for every SA
+    set."""
+
+    def __init__(self, prob):
+        wl = prob.wl
+        assert not wl.block and prob.q[0].shape[0] >= 2, "an FA set and at least one SA set"
+        self.prob = prob
+        self.wl = wl
+        dev = prob.seq_of_row.device
+        R = prob.n_rows
+        cap = wl.n_entries_cap
+        self.rows_dense = Rows(prob.seq_of_row, prob.pos_of_row, prob.seq_len, wl.stride, cap)
+        self.rows = Rows(prob.seq_of_row, prob.pos_of_row, prob.seq_len, wl.stride, wl.window)
+        self.k = _cache(prob.k, wl.hkv, wl.dqk)
+        self.v = _cache(prob.v, wl.hkv, wl.dv) if prob.v is not None else None
+        q = prob.q[0]
+        self.q_fa, self.q_sa = q[0:1], q[1:]
+        f32, i32 = torch.float32, torch.int32
+        self.scores = torch.empty(R, cap, dtype=f32, device=dev)
+        self.idx = torch.empty(R, wl.k, dtype=i32, device=dev)
+        self.count = torch.empty(R, dtype=i32, device=dev)
+        self.o_fa = torch.empty(1, R, wl.hq, wl.dv, dtype=q.dtype, device=dev)
+        self.lse_fa = torch.empty(1, R, wl.hq, dtype=f32, device=dev)
+        self.o_sa = torch.empty(q.shape[0] - 1, R, wl.hq, wl.dv, dtype=q.dtype, device=dev)
+        self.lse_sa = torch.empty(q.shape[0] - 1, R, wl.hq, dtype=f32, device=dev)
+        self.scale = wl.dqk ** -0.5
+        self._prepared = None
+
+    def prepare(self):
+        if self._prepared is not None:
+            return self._prepared
+        self._prepared = [
+            ("attn_gather_fwd_fa", prepare_attn_gather_fwd(
+                self.rows_dense, self.q_fa, self.k, self.v, None, None, self.o_fa, self.lse_fa,
+                self.scale, self.wl.dv)),
+            ("attn_score", PreparedScore(self.rows_dense, self.q_fa, self.k, self.lse_fa,
+                                         self.scores, self.scale)),
+            ("topk_select", prepare_topk_select(self.rows, self.scores, self.wl.k, self.idx,
+                                                self.count)),
+            ("attn_gather_fwd", prepare_attn_gather_fwd(
+                self.rows, self.q_sa, self.k, self.v, self.idx, self.count, self.o_sa,
+                self.lse_sa, self.scale, self.wl.dv)),
+        ]
+        return self._prepared
 
     def run(self):
         for _, c in self.prepare():

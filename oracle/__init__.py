@@ -65,6 +65,10 @@ def lib():
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, P, P, P,
                                     ctypes.c_int, i64, P, i64, P, f32, P, P]
+        L.orc_fa_score.restype = ctypes.c_int
+        L.orc_fa_score.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P,
+                                   i64, f32, P, i64]
         _lib = L
     return _lib
 
@@ -233,6 +237,26 @@ def attention(seq_of_row, pos_of_row, seq_len, stride: int, window: int, q: torc
     if rc != 0:
         raise ValueError("orc_attention failed (%d)" % rc)
     return o, lse
+
+
+def fa_score(seq_of_row, pos_of_row, seq_len, stride: int, q: torch.Tensor, K: torch.Tensor,
+             scale: float = None) -> np.ndarray:
+    """Full-attention selection scores [R, Lcap] in float64: for every visible
+    entry, the dense-attention probability each query head (of every query
+    set) gives it, summed over the heads; NaN outside the domain.  q
+    [n_sets, R, Hq, dqk]; K logical [B, Lcap, Hkv, dqk]."""
+    so, po, sl = _i32(seq_of_row), _i32(pos_of_row), _i32(seq_len)
+    n_sets, R, Hq, dqk = (int(x) for x in q.shape)
+    Hkv, Lcap = int(K.shape[2]), int(K.shape[1])
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(dqk))
+    out = np.empty((R, Lcap), dtype=np.float64)
+    rc = lib().orc_fa_score(n_sets, R, _ptr(so), _ptr(po), _ptr(sl), stride, Hq, Hkv, dqk,
+                            _code(q), _ptr(_raw(q)), _code(K), _ptr(_raw(K)), Lcap,
+                            ctypes.c_float(scale), _ptr(out), Lcap)
+    if rc != 0:
+        raise ValueError("orc_fa_score failed (%d)" % rc)
+    return out
 
 
 def decode_bf16(bits: int) -> float:

@@ -23,6 +23,9 @@
  *    the union of their positions.
  *  - Joint softmax: "HySparse2" page, section 7.2: window and selected
  *    positions share one softmax normalisation and are read from one KV cache.
+ *  - Full-attention selection score: "HySparse2" page, appendix A.1 (the FA
+ *    layer selects by its own attention scores) and "Lecture 10", section 5.2
+ *    (the per-position target sums the main attention over heads).
  *  - Storage formats: bfloat16; OCP FP8 E4M3 ("e4m3fn": bias 7, subnormals,
  *    no infinities, S.1111.111 is NaN, max 448); FP4 E2M1 (bias 1, values
  *    0, 0.5, 1, 1.5, 2, 3, 4, 6) with one E4M3 scale per 16 channels ("CSA, HCA
@@ -417,6 +420,74 @@ int orc_attention(int n_sets, int R, const int32_t* seq_of_row, const int32_t* p
     }
     lse[it] = mx + log(sum);
     free(A);
+    free(logit);
+  }
+  return err;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Full-attention selection score.                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The selection signal of a full-attention layer ("HySparse2" page, appendix
+ * A.1: the FA layer computes ordinary full attention and picks the important
+ * history positions from those attention scores, which its SA layers then
+ * reuse; "Lecture 10 - Hybrid LLMs", section 5.2: the per-position target is
+ * the main attention's scores summed over heads):
+ *
+ *   score[r][s] = sum over query sets i and query heads h of p_{i,h}(s),
+ *   p_{i,h} = softmax over the row's whole visible domain of
+ *             scale * q[i][r][h] . K[s][g(h)],  g(h) = floor(h * Hkv / Hq).
+ *
+ * q [n_sets][R][Hq][dqk]; K logical [B][Lcap][Hkv][dqk].  out [R][out_stride]:
+ * out[r][s] for s < n_avail, NaN elsewhere (and for padding rows).
+ */
+int orc_fa_score(int n_sets, int R, const int32_t* seq_of_row, const int32_t* pos_of_row,
+                 const int32_t* seq_len, int stride, int Hq, int Hkv, int dqk, int q_dtype,
+                 const void* q, int kv_dtype, const void* K, int64_t Lcap, float scale,
+                 double* out, int64_t out_stride) {
+  if (n_sets <= 0 || R < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || dqk <= 0 || stride <= 0)
+    return ORC_EINVAL;
+  if (kv_dtype == ORC_E2M1) return ORC_EINVAL;
+  for (int r = 0; r < R; ++r)
+    if (n_avail(r, seq_of_row, pos_of_row, seq_len, stride) > Lcap) return ORC_EINVAL;
+  for (int64_t i = 0; i < (int64_t)R * out_stride; ++i) out[i] = NAN;
+  const double sc = (double)scale;
+  int err = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int r = 0; r < R; ++r) {
+    int64_t na = n_avail(r, seq_of_row, pos_of_row, seq_len, stride);
+    int b = seq_of_row[r];
+    if (na == 0 || b < 0) continue;
+    double* acc = (double*)calloc((size_t)na, sizeof(double));
+    double* logit = (double*)malloc(sizeof(double) * (size_t)na);
+    if (!acc || !logit) {
+      err = ORC_ENOMEM;
+      free(acc);
+      free(logit);
+      continue;
+    }
+    for (int set = 0; set < n_sets; ++set) {
+      for (int h = 0; h < Hq; ++h) {
+        int g = (int)((int64_t)h * Hkv / Hq);
+        const int64_t qrow = (((int64_t)set * R + r) * Hq + h) * dqk;
+        double mx = -INFINITY;
+        for (int64_t s = 0; s < na; ++s) {
+          int64_t row = ((int64_t)b * Lcap + s) * Hkv + g;
+          double dot = 0.0;
+          for (int c = 0; c < dqk; ++c)
+            dot += load_elem(q, q_dtype, qrow + c) * load_elem(K, kv_dtype, row * dqk + c);
+          logit[s] = sc * dot;
+          if (logit[s] > mx) mx = logit[s];
+        }
+        double sum = 0.0;
+        for (int64_t s = 0; s < na; ++s) sum += exp(logit[s] - mx);
+        for (int64_t s = 0; s < na; ++s) acc[s] += exp(logit[s] - mx) / sum;
+      }
+    }
+    for (int64_t s = 0; s < na; ++s) out[(int64_t)r * out_stride + s] = acc[s];
+    free(acc);
     free(logit);
   }
   return err;
