@@ -39,6 +39,7 @@ CALL_SOURCES = {
     "index_score": ("index_score.hip", "common.hpp", "kernels.hpp"),
     "topk_select": ("topk_select.hip", "common.hpp", "kernels.hpp"),
     "attn_gather_fwd": ("attn_gather.hip", "common.hpp", "kernels.hpp"),
+    "attn_score": ("attn_score.hip", "common.hpp", "kernels.hpp"),
 }
 METRIC = "sparse-attn decode queries/s & prefill rows/s at 1 GPU; % HBM/MFMA roofline"
 

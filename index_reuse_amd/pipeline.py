@@ -237,6 +237,7 @@ class FAStep:
         self.lse_fa = torch.empty(1, R, wl.hq, dtype=f32, device=dev)
         self.o_sa = torch.empty(q.shape[0] - 1, R, wl.hq, wl.dv, dtype=q.dtype, device=dev)
         self.lse_sa = torch.empty(q.shape[0] - 1, R, wl.hq, dtype=f32, device=dev)
+        self.pool_count = None  # no block pool in this group
         self.scale = wl.dqk ** -0.5
         self._prepared = None
 
