@@ -215,7 +215,7 @@ def cpu_baseline(step, n_rows: int, min_seconds: float):
         return oracle.unpage(t, bt, c.page_size or cap, len(seqs), cap)
 
     fp4 = wl.kv_mode == "fp4"
-    kl = logical(p.kidx)
+    kl = logical(p.kidx) if p.kidx is not None else None
     K = logical(p.k)
     KS = logical(p.k, "scale") if fp4 else None
     V = logical(p.v) if p.v is not None else None
@@ -234,6 +234,9 @@ def cpu_baseline(step, n_rows: int, min_seconds: float):
                              v_from_k=V is None, dv=wl.dv)
 
     def one_step():
+        if wl.k == 0:  # no selector: the window covers every entry
+            attend(q[0], None, None)
+            return
         sc = oracle.index_score(*geo, q_idx[0], w[0], kl)
         if not wl.block:
             idx, cnt = oracle.topk_select(*geo, wl.window, sc, wl.k)
@@ -309,6 +312,14 @@ def fa_cpu_baseline(step, n_rows: int, min_seconds: float):
 
 
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}  # MI355X dense
+
+
+def dense_crossover(row_bytes: int, index_row_bytes: int, k: int) -> float:
+    """Context length above which a decode step of top-k sparse attention reads
+    fewer bytes than dense attention ("Lecture 10", section 5.3 and exercise
+    6): dense reads row_bytes per entry; sparse reads index_row_bytes per
+    entry plus k rows, so it wins once L > k row / (row - index_row)."""
+    return k * row_bytes / (row_bytes - index_row_bytes)
 
 
 def layer_group_index_work(n_entries: int, pool: int, n_full: int, n_reindex: int,
@@ -399,7 +410,7 @@ def run_prefill(args, wl):
 
     dev = torch.device("cuda:0")
     prob = synth.make_problem(wl, device=dev)
-    step = PrefillStep(prob, row_block=args.row_block)
+    step = PrefillStep(prob, row_block=args.row_block, dense_route=True)
     calls = step.prepare()
     names = [n for n, _ in calls]
     torch.cuda.synchronize()
@@ -482,7 +493,7 @@ def run_decode(args, wl, fa: bool = False):
     steps = []
     for i in range(args.replicas):
         prob = synth.make_problem(wl, device=dev, seed_base=1000 * (wl.cfg_id + 1) + 100 * i)
-        steps.append(FAStep(prob) if fa else Step(prob))
+        steps.append(FAStep(prob) if fa else Step(prob, dense_route=True))
     calls = [s.prepare() for s in steps]
     names = [n for n, _ in calls[0]]
     stream = torch.cuda.current_stream().cuda_stream
@@ -584,6 +595,7 @@ def run_decode(args, wl, fa: bool = False):
                    "query_sets": sum(q.shape[0] for q in step0.prob.q), "kv_heads": wl.hkv,
                    "q_heads": wl.hq, "head_dim": wl.dqk, "indexer": (
                        "none: the FA layer's dense attention probabilities" if fa else
+                       "none: dense over every entry" if wl.k == 0 else
                        "%dx%d %s" % (wl.idx_heads, wl.idx_dim,
                                      str(wl.idx_dtype).replace("torch.", ""))),
                    "page_size": wl.page_size, "replicas": args.replicas, "launch": mode},
@@ -615,7 +627,7 @@ def run_decode(args, wl, fa: bool = False):
 
 
 # Extra workloads measured by the default run, next to the headline decode.
-EXTRA = ("hysparse2_fa", "csa", "csa2", "dsa")
+EXTRA = ("hysparse2_fa", "csa", "csa2", "hca", "dsa")
 
 
 def main():
@@ -624,7 +636,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
-                    help="hysparse2, hysparse2_fa, csa, csa2, dsa, or all (the headline "
+                    help="hysparse2, hysparse2_fa, csa, csa2, hca, dsa, or all (the headline "
                          "HySparse2 decode, with the other workloads as extra records)")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-rows", type=int, default=0,

@@ -152,6 +152,15 @@ typedef struct {
  *            i < cand_count[r] (-inf for a padding or invisible candidate).
  *            Other slots are not written.
  *   score_stride >= max n_avail (full) or >= cand_stride (candidate mode).
+ *   skip_k   dense route (full mode only; 0 = off): a row with at most skip_k
+ *            candidates (n_avail - window <= skip_k) is not scored -- a
+ *            window + top-k selection with k >= skip_k keeps every candidate
+ *            of such a row whatever its scores -- and gets scores[r][s] = 0
+ *            for s < n_avail instead, without reading the cache ("Lecture
+ *            10", section 5.5: when a row's context is no longer than the
+ *            budget, sparse selection only adds the indexer's cost, so it
+ *            falls back to dense attention; with k >= the candidates the
+ *            selected set IS the dense set).
  *
  * Accumulation is fp32 (MFMA for BF16/FP8, FMA for F32); the ReLU and the
  * weighted head sum are fp32.
@@ -166,7 +175,7 @@ typedef struct {
   const int32_t* cand;       /* optional [R][cand_stride], ascending, -1 pad  */
   const int32_t* cand_count; /* [R] when cand != NULL                         */
   int32_t cand_stride;
-  int32_t reserved;
+  int32_t skip_k;            /* dense route threshold (0 = off), see above     */
   float* scores;
   int64_t score_stride;
 } sa_index_desc;

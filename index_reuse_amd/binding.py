@@ -39,7 +39,7 @@ class sa_rows(ctypes.Structure):
 class sa_index_desc(ctypes.Structure):
     _fields_ = [("rows", sa_rows), ("q", _P), ("w", _P), ("k", sa_cache), ("n_heads", _i32),
                 ("dim", _i32), ("cand", _P), ("cand_count", _P), ("cand_stride", _i32),
-                ("reserved", _i32), ("scores", _P), ("score_stride", _i64)]
+                ("skip_k", _i32), ("scores", _P), ("score_stride", _i64)]
 
 
 class sa_topk_desc(ctypes.Structure):
@@ -208,7 +208,8 @@ def workspace(nbytes: int, device, op: int) -> Optional[torch.Tensor]:
 # ---------------------------------------------------------------------------
 
 
-def index_desc(rows: Rows, q, w, k: Cache, scores, cand=None, cand_count=None) -> sa_index_desc:
+def index_desc(rows: Rows, q, w, k: Cache, scores, cand=None, cand_count=None,
+               skip_k: int = 0) -> sa_index_desc:
     _dense(q, "q")
     _dense(w, "w")
     _dense(scores, "scores", rows=True)
@@ -216,18 +217,20 @@ def index_desc(rows: Rows, q, w, k: Cache, scores, cand=None, cand_count=None) -
     _dense(cand_count, "cand_count")
     return sa_index_desc(rows.c(), _ptr(q), _ptr(w), k.c(), int(q.shape[1]), int(q.shape[2]),
                          _ptr(cand), _ptr(cand_count), 0 if cand is None else int(cand.stride(0)),
-                         0, _ptr(scores), int(scores.stride(0)))
+                         int(skip_k), _ptr(scores), int(scores.stride(0)))
 
 
 def index_score(rows: Rows, q: torch.Tensor, w: torch.Tensor, k: Cache,
                 scores: Optional[torch.Tensor] = None, n_slots: Optional[int] = None,
-                cand: Optional[torch.Tensor] = None, cand_count: Optional[torch.Tensor] = None):
-    """Indexer scores [R, S] float32 (see sparse_index_score)."""
+                cand: Optional[torch.Tensor] = None, cand_count: Optional[torch.Tensor] = None,
+                skip_k: int = 0):
+    """Indexer scores [R, S] float32 (see sparse_index_score; ``skip_k``: the
+    dense route)."""
     L = load()
     if scores is None:
         S = int(cand.shape[1]) if cand is not None else int(n_slots)
         scores = torch.empty(int(q.shape[0]), S, dtype=torch.float32, device=q.device)
-    d = index_desc(rows, q, w, k, scores, cand, cand_count)
+    d = index_desc(rows, q, w, k, scores, cand, cand_count, skip_k)
     _check(L.sparse_index_score(ctypes.byref(d), None, 0, _stream()))
     return scores
 
@@ -387,8 +390,9 @@ class Prepared:
         _check(self.fn(self.ref, self.ws_ptr, self.need, _stream() if stream is None else stream))
 
 
-def prepare_index_score(rows: Rows, q, w, k: Cache, scores, cand=None, cand_count=None):
-    d = index_desc(rows, q, w, k, scores, cand, cand_count)
+def prepare_index_score(rows: Rows, q, w, k: Cache, scores, cand=None, cand_count=None,
+                        skip_k: int = 0):
+    d = index_desc(rows, q, w, k, scores, cand, cand_count, skip_k)
     return Prepared("sparse_index_score", d, SA_OP_INDEX_SCORE, q.device,
                     keep=(rows, q, w, k, scores, cand, cand_count))
 

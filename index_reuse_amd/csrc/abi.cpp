@@ -123,10 +123,12 @@ sa_status validate_index(const sa_index_desc* d, sa::IndexArgs* out) {
   CHECK(aligned16(d->q), SA_ERR_SHAPE, "%s: q must be 16-byte aligned", op);
   st = check_cache(d->k, op, "k", (int64_t)d->dim * eb);
   if (st) return st;
+  CHECK(d->skip_k >= 0, SA_ERR_SHAPE, "%s: skip_k must be >= 0", op);
   if (d->cand) {
     CHECK(d->cand_count, SA_ERR_NULL, "%s: cand_count is required with cand", op);
     CHECK(d->cand_stride >= 1 && d->score_stride >= d->cand_stride, SA_ERR_SHAPE,
           "%s: need 1 <= cand_stride <= score_stride", op);
+    CHECK(d->skip_k == 0, SA_ERR_SHAPE, "%s: skip_k (the dense route) needs full mode", op);
   } else {
     CHECK(d->score_stride >= 1, SA_ERR_SHAPE, "%s: score_stride must be >= 1", op);
   }
@@ -144,6 +146,7 @@ sa_status validate_index(const sa_index_desc* d, sa::IndexArgs* out) {
     out->dim = d->dim;
     out->dtype = d->k.dtype;
     out->n_slots = d->cand ? d->cand_stride : (int32_t)d->score_stride;
+    out->skip_k = d->skip_k;
   }
   return SA_OK;
 }

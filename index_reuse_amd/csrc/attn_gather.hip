@@ -1270,8 +1270,11 @@ void attn_plan(AttnArgs& a) {
   int ns = (a.max_entries + kMaxEntries - 1) / kMaxEntries;
   // wide value rows make split partials expensive: stop at about 64
   // workgroups, but take at least 4 splits (measured on 8 and 16 rows of 64
-  // heads over 512 entries)
-  const int cap = a.dv >= 512 ? (int)max((int64_t)4, (64 + base - 1) / base) : max_split;
+  // heads over 512 entries), and up to one split per 512 entries of a long
+  // range (the partials then cost at most half the rows they replace)
+  const int cap = a.dv >= 512
+                      ? (int)max(max((int64_t)4, (64 + base - 1) / base), (int64_t)a.max_entries / 512)
+                      : max_split;
   while (ns < max_split && ns < cap && ns < kMaxSplits && base * ns < 256) ++ns;
   a.n_split = ns < 1 ? 1 : ns;
 }

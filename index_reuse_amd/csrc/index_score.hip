@@ -133,9 +133,14 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
   const int wg_base = blockIdx.x * (64 * kWaves * gpw);
   if (wg_base >= n_slots) return;
   float* out = a.scores + (int64_t)r * a.score_stride;
-  if (ri.n_avail == 0) {  // nothing visible: every listed candidate scores -inf
+  // nothing visible: every listed candidate scores -inf; dense route (at
+  // most skip_k candidates, all of which any top-k with k >= skip_k keeps):
+  // 0 for every visible entry, without reading the cache
+  const bool dense_route = !cand_mode && a.skip_k > 0 && ri.win_lo <= a.skip_k;
+  if (ri.n_avail == 0 || dense_route) {
+    const float fill = dense_route ? 0.0f : -__builtin_huge_valf();
     for (int i = threadIdx.x; i < 64 * kWaves * gpw && wg_base + i < n_slots; i += 64 * kWaves)
-      out[wg_base + i] = -__builtin_huge_valf();
+      out[wg_base + i] = fill;
     return;
   }
   const int32_t* cand = cand_mode ? a.cand + (int64_t)r * a.cand_stride : nullptr;
@@ -332,23 +337,32 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 template <int NMT>
 __global__ __launch_bounds__(64 * kPWaves) void index_score_prefill(IndexArgs a, int n_blocks) {
   __shared__ __align__(16) char kb[2][kPChunk * kPRowB];
-  __shared__ int sb[kPRows], sn[kPRows];
+  __shared__ int sb[kPRows], sn[kPRows], sz[kPRows];
   __shared__ int wred[kPWaves][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int r0 = (n_blocks - 1 - (int)blockIdx.x) * kPRows;
   if (tid < kPRows) {
     const int r = r0 + tid;
-    int b = -1, n = 0;
+    int b = -1, n = 0, zero = 0;
     if (r < a.rows.n_rows) {
       const RowInfo ri = row_info(a.rows, r);
       b = ri.b;
       n = ri.n_avail;
+      // dense route: a row whose candidates all fit the budget gets zeros
+      if (b >= 0 && a.skip_k > 0 && ri.win_lo <= a.skip_k) {
+        zero = n;
+        n = 0;
+      }
     }
     sb[tid] = b;
     sn[tid] = b >= 0 ? n : 0;
+    sz[tid] = zero;
   }
   __syncthreads();
+  for (int j = 0; j < kPRows; ++j)
+    for (int i = tid; i < sz[j]; i += 64 * kPWaves)
+      a.scores[(int64_t)(r0 + j) * a.score_stride + i] = 0.0f;
 
   // this wave's rows: A operands (head mt*16 + col, bytes [32g, 32g+32)) and
   // head weights in the accumulator layout (head mt*16 + 4g + i)
@@ -491,7 +505,9 @@ __global__ __launch_bounds__(256) void index_score_f32(IndexArgs a) {
   if (slot >= n_slots) return;
   int pos = cand_mode ? a.cand[(int64_t)r * a.cand_stride + slot] : slot;
   float s = -__builtin_huge_valf();
-  if (pos >= 0 && pos < ri.n_avail) {
+  if (!cand_mode && a.skip_k > 0 && ri.win_lo <= a.skip_k) {
+    s = 0.0f;  // dense route: every candidate is kept whatever its score
+  } else if (pos >= 0 && pos < ri.n_avail) {
     const float* kr = reinterpret_cast<const float*>(cache_row(a.k, ri.b, pos));
     s = 0.0f;
     for (int h = 0; h < a.n_heads; ++h) {

@@ -24,6 +24,7 @@ struct IndexArgs {
   int32_t dim;
   int32_t dtype;        // SA_F32 / SA_BF16 / SA_FP8_E4M3
   int32_t n_slots;      // score slots per row to cover (grid extent)
+  int32_t skip_k;       // dense route: rows with n_avail - window <= skip_k get 0s
 };
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t s);
 

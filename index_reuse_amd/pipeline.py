@@ -48,14 +48,19 @@ class Step:
     top-k inside the pool -> attention with the Full indices (Full query) and
     with the Reindex indices (Reindex query + Reuse queries, fused)."""
 
-    def __init__(self, prob, scores_slots: Optional[int] = None):
+    def __init__(self, prob, scores_slots: Optional[int] = None, dense_route: bool = False):
         wl = prob.wl
         self.prob = prob
         self.wl = wl
         dev = prob.seq_of_row.device
         R = prob.n_rows
         self.rows = Rows(prob.seq_of_row, prob.pos_of_row, prob.seq_len, wl.stride, wl.window)
-        self.kidx = _cache(prob.kidx, 1, wl.idx_dim)
+        # a workload without a selector (k = 0, e.g. HCA) attends to its window only
+        self.selector = wl.k > 0
+        # dense route: rows whose candidates all fit the budget skip the
+        # indexer (scores 0; the selection keeps every candidate either way)
+        self.skip_k = wl.k if dense_route else 0
+        self.kidx = _cache(prob.kidx, 1, wl.idx_dim) if self.selector else None
         fp4 = wl.kv_mode == "fp4"
         self.k = _cache(prob.k, wl.hkv, wl.dqk, fp4=fp4)
         self.v = _cache(prob.v, wl.hkv, wl.dv) if prob.v is not None else None
@@ -86,8 +91,13 @@ class Step:
         if self._prepared is not None:
             return self._prepared
         p, wl = self.prob, self.wl
+        if not self.selector:
+            self._prepared = [("attn_gather_fwd", prepare_attn_gather_fwd(
+                self.rows, p.q[0], self.k, self.v, None, None, self.o[0], self.lse[0], self.scale,
+                wl.dv))]
+            return self._prepared
         calls = [("index_score", prepare_index_score(self.rows, p.idx_q[0], p.idx_w[0], self.kidx,
-                                                     self.scores[0]))]
+                                                     self.scores[0], skip_k=self.skip_k))]
         if not wl.block:
             calls.append(("topk_select", prepare_topk_select(self.rows, self.scores[0], wl.k,
                                                              self.idx[0], self.count[0])))
@@ -111,7 +121,10 @@ class Step:
 
     def run_index(self):
         p, wl = self.prob, self.wl
-        index_score(self.rows, p.idx_q[0], p.idx_w[0], self.kidx, scores=self.scores[0])
+        if not self.selector:
+            return
+        index_score(self.rows, p.idx_q[0], p.idx_w[0], self.kidx, scores=self.scores[0],
+                    skip_k=self.skip_k)
         if not wl.block:
             topk_select(self.rows, self.scores[0], wl.k, idx=self.idx[0], count=self.count[0])
             return
@@ -130,7 +143,9 @@ class Step:
         idx = idx if idx is not None else self.idx
         count = count if count is not None else self.count
         for c, q in enumerate(p.q):
-            attn_gather_fwd(self.rows, q, self.k, self.v, idx=idx[c], count=count[c],
+            attn_gather_fwd(self.rows, q, self.k, self.v,
+                            idx=idx[c] if self.selector else None,
+                            count=count[c] if self.selector else None,
                             scale=self.scale, d_v=self.wl.dv, o=self.o[c], lse=self.lse[c])
 
     def run(self):
@@ -150,9 +165,10 @@ class PrefillStep:
     top-k, and attention gathers it.  Indices, outputs and LSE cover all
     rows; the score buffer is reused from block to block."""
 
-    def __init__(self, prob, row_block: int = 8192):
+    def __init__(self, prob, row_block: int = 8192, dense_route: bool = False):
         wl = prob.wl
         assert wl.prefill and not wl.block, "prefill workloads without a block pool"
+        self.skip_k = wl.k if dense_route else 0
         self.prob = prob
         self.wl = wl
         dev = prob.seq_of_row.device
@@ -187,7 +203,8 @@ class PrefillStep:
             rows = Rows(p.seq_of_row[lo:hi], p.pos_of_row[lo:hi], p.seq_len, wl.stride, wl.window)
             sc = self.scores[: hi - lo]
             calls.append(("index_score", prepare_index_score(rows, p.idx_q[0][lo:hi],
-                                                             p.idx_w[0][lo:hi], self.kidx, sc)))
+                                                             p.idx_w[0][lo:hi], self.kidx, sc,
+                                                             skip_k=self.skip_k)))
             sel = prepare_topk_select(rows, sc, wl.k, self.idx[lo:hi], self.count[lo:hi],
                                       workspace=ws)
             ws = sel.ws if ws is None else ws

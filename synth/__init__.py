@@ -18,7 +18,9 @@ Workload shapes follow the five configurations the method is measured on:
 * ``dsa``      -- DSA-style prefill: 65536 causal rows, FP8 indexer 64x128,
   top-2048, MLA latent KV 576 wide (V = first 512), 128 query heads;
 * ``csa``      -- CSA-style decode over entries compressed at stride 4;
-* ``csa2``     -- CSA2 hierarchical decode with an FP4 (E2M1 + E4M3/16) KV.
+* ``csa2``     -- CSA2 hierarchical decode with an FP4 (E2M1 + E4M3/16) KV;
+* ``hca``      -- HCA decode: every entry compressed at stride 128, read
+  densely (no selector).
 """
 from __future__ import annotations
 
@@ -189,7 +191,14 @@ CSA2 = Workload("csa2", 4, n_seqs=8, seq_len=262144, prefill=False, stride=1, wi
                 kv_mode="fp4", attn_dtype=torch.bfloat16, n_qsets=1, page_size=0, block=8,
                 max_blocks=2048, n_reuse=3)
 
-WORKLOADS = {w.name: w for w in (TINY, HYSPARSE2, DSA, CSA, CSA2)}
+# HCA: heavily compressed entries (one per 128 tokens) read densely with no
+# selector ("CSA, HCA and CSA2", sections 1.2 and 6.2: HCA attends to every
+# entry of the shorter sequence; 8192 entries at 1M tokens).
+HCA = Workload("hca", 5, n_seqs=16, seq_len=1048576, prefill=False, stride=128, window=8192, k=0,
+               idx_heads=0, idx_dim=0, idx_dtype=torch.bfloat16, hq=64, hkv=1, dqk=512, dv=512,
+               kv_mode="shared", attn_dtype=torch.bfloat16, n_qsets=1, page_size=0)
+
+WORKLOADS = {w.name: w for w in (TINY, HYSPARSE2, DSA, CSA, CSA2, HCA)}
 
 
 # ---------------------------------------------------------------------------
@@ -273,8 +282,8 @@ def make_problem(wl: Workload, device="cpu", integer=False, seed_base=None,
     R = int(seq_of_row.numel())
     cap = wl.n_entries_cap
 
-    # --- indexer inputs -----------------------------------------------------
-    n_idx_layers = 2 if wl.block else 1
+    # --- indexer inputs (none when k = 0: the window covers every entry) ------
+    n_idx_layers = 0 if wl.k == 0 else (2 if wl.block else 1)
     idx_q, idx_w = [], []
     for layer in range(n_idx_layers):
         idx_q.append(_draw((R, wl.idx_heads, wl.idx_dim), base + 1 + 10 * layer, device,
@@ -286,12 +295,12 @@ def make_problem(wl: Workload, device="cpu", integer=False, seed_base=None,
             idx_w.append(uniform01((R, wl.idx_heads), base + 2 + 10 * layer, device=device))
 
     n_pages, max_pages = _paged_shape(B, cap, wl.page_size)
-    if wl.page_size:
-        bt = _block_table(B, max_pages, base + 7, device)
+    bt = _block_table(B, max_pages, base + 7, device) if wl.page_size else None
+    kidx = None
+    if n_idx_layers and wl.page_size:
         kpool = _draw((n_pages, wl.page_size, wl.idx_dim), base + 3, device, wl.idx_dtype, integer)
         kidx = Cache(kpool, bt, wl.page_size)
-    else:
-        bt = None
+    elif n_idx_layers:
         kpool = _draw((B, cap, wl.idx_dim), base + 3, device, wl.idx_dtype, integer)
         kidx = Cache(kpool, None, 0)
 

@@ -74,7 +74,8 @@ def oracle_attention(prob, call, idx, count, rows=None):
     q = prob.q[call].cpu()
     if rows is not None:
         so, po, q = so[rows], po[rows], q[:, rows]
-        idx, count = np.asarray(idx)[rows], np.asarray(count)[rows]
+        if idx is not None:
+            idx, count = np.asarray(idx)[rows], np.asarray(count)[rows]
     cap = wl.n_entries_cap
     scale = float(np.float32(wl.dqk ** -0.5))
     if wl.kv_mode == "fp4":

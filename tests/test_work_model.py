@@ -91,3 +91,15 @@ def test_hysparse2_decode_bytes():
     qo = 6 * 32 * 64 * (128 + 128) * 2 + 6 * 32 * 64 * 4
     assert bench.algorithmic_bytes(st, "attn_gather_fwd") == kv + qo + 32 * 1024 * 4
     assert kv == 150_994_944
+
+
+def test_dense_crossover():
+    """Exercise 6 of "Lecture 10": with 1152-byte latent rows, 128-byte FP8
+    index keys and k = 2048, sparse decode reads fewer bytes than dense once
+    L > 2304; at L = 2048 it reads about 11% more (the page's table: 10%
+    slower) and at 4096 dense reads 1.64x more."""
+    assert bench.dense_crossover(1152, 128, 2048) == 2304
+    sparse = lambda L: 128 * L + 1152 * 2048
+    dense = lambda L: 1152 * L
+    assert abs(sparse(2048) / dense(2048) - 1.111) < 0.001
+    assert abs(dense(4096) / sparse(4096) - 1.64) < 0.005
