@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 1       /* bumped on any descriptor layout change   */
+#define SA_ABI_VERSION 2       /* bumped on any descriptor layout change   */
 #define SA_INDEX_FORMAT 1      /* int32 asc, -1 pad, lowest-index tie-break */
 
 typedef int32_t sa_status;
@@ -190,12 +190,15 @@ typedef struct {
  * idx[r][0 .. count[r]), and idx[r][count[r] .. k) = -1.
  *
  * Pool mode (pool != NULL, block >= 1, max_blocks <= 2048, full-domain scores
- * only) ["CSA, HCA and CSA2", section 3.2]:
- * every aligned block j of `block` entries gets beta_j = the max score over
- * its visible members (window included); the first min(max_blocks, #blocks)
- * blocks in the order (beta descending, j ascending) are kept, and their
- * members are written ascending to pool[r][0 .. pool_count[r]),
- * pool[r][pool_count[r] .. max_blocks*block) = -1.
+ * only) ["CSA, HCA and CSA2", section 3.2; "HySparse2", appendix A.1, the
+ * first generation's 16 blocks of 64 tokens]: every aligned block j of
+ * `block` entries gets beta_j = the max score over its candidates (visible
+ * entries outside the window; with window 0, every visible member); the first
+ * min(max_blocks, #blocks) blocks in the order (beta descending, j ascending)
+ * are kept, and their candidates are written ascending to
+ * pool[r][0 .. pool_count[r]), pool[r][pool_count[r] .. max_blocks*block) =
+ * -1.  The pool is in the index format, so it can also serve directly as a
+ * block-level selection (pool as idx, pool_count as count).
  *
  * Both modes can run in one call from the same scores.
  *
@@ -239,10 +242,20 @@ typedef struct {
  * For query set i, row r, query head h with KV head g = h / (n_heads_q /
  * k.heads), over A = W(r) U {idx[r][0 .. count[r])}:
  *   logit_s = scale * q[i][r][h][:] . K[s][g][:]
- *   o[i][r][h][:] = sum_s softmax(logit)_s * V[s][g][:]
- *   lse[i][r][h]  = log sum_s exp(logit_s)       (natural log)
- * An empty A gives o = 0 and lse = -inf.  Selected entries must lie outside
- * the window (sparse_topk_select guarantees it).
+ *   Z       = sum_s exp(logit_s) + exp(sink[i][h])      (no sink: 0 for that term)
+ *   o[i][r][h][:] = sigmoid(gate[i][r][h][:]) * sum_s exp(logit_s) / Z * V[s][g][:]
+ *   lse[i][r][h]  = log Z                              (natural log)
+ * An empty A gives o = 0 and lse = sink (-inf without a sink).  Selected
+ * entries must lie outside the window (sparse_topk_select guarantees it).
+ *
+ * The optional per-head sink bias and output sigmoid gate are those the
+ * HySparse2 page lists around its core softmax ("HySparse2", section 17.1: every
+ * SA layer has an output sigmoid gate and a learnable per-head sink bias).
+ * The sink is a logit for a virtual entry whose value row is zero; the gate
+ * multiplies each output channel.
+ *   sink     optional [n_qsets][n_heads_q] f32 (each query set is a layer
+ *            with its own parameters); NULL = no sink
+ *   gate     optional [n_qsets][R][n_heads_q][d_v], dtype q_dtype; NULL = none
  *
  *   q        [n_qsets][R][n_heads_q][k.width], dtype q_dtype (F32 or BF16)
  *   k        key cache, heads = H_kv, width = d_qk; BF16, F32 or FP4_E2M1
@@ -277,6 +290,8 @@ typedef struct {
   int32_t o_dtype;
   void* o;
   float* lse;
+  const float* sink;         /* optional [n_qsets][n_heads_q], see above      */
+  const void* gate;          /* optional [n_qsets][R][n_heads_q][d_v]          */
 } sa_attn_desc;
 
 enum { SA_OP_INDEX_SCORE = 0, SA_OP_TOPK_SELECT = 1, SA_OP_ATTN_GATHER_FWD = 2 };

@@ -53,7 +53,8 @@ class sa_attn_desc(ctypes.Structure):
     _fields_ = [("rows", sa_rows), ("n_qsets", _i32), ("n_heads_q", _i32), ("q", _P),
                 ("q_dtype", _i32), ("d_v", _i32), ("k", sa_cache), ("v", sa_cache),
                 ("v_from_k", _i32), ("idx_stride", _i32), ("idx", _P), ("count", _P),
-                ("scale", _f32), ("o_dtype", _i32), ("o", _P), ("lse", _P)]
+                ("scale", _f32), ("o_dtype", _i32), ("o", _P), ("lse", _P), ("sink", _P),
+                ("gate", _P)]
 
 
 EXPORTS = ("sparse_index_score", "sparse_topk_select", "sparse_attn_gather_fwd",
@@ -296,28 +297,37 @@ def check_indices(rows: Rows, idx: torch.Tensor, count: torch.Tensor, k: Optiona
 
 
 def attn_desc(rows: Rows, q, k: Cache, v: Optional[Cache], idx, count, o, lse=None,
-              scale: Optional[float] = None, d_v: Optional[int] = None) -> sa_attn_desc:
+              scale: Optional[float] = None, d_v: Optional[int] = None, sink=None,
+              gate=None) -> sa_attn_desc:
     n_qsets, R, hq, dqk = (int(x) for x in q.shape)
     if d_v is None:
         d_v = v.width if v is not None else k.width
     if scale is None:
         scale = dqk ** -0.5
-    for t, n in ((q, "q"), (o, "o"), (lse, "lse"), (count, "count")):
+    for t, n in ((q, "q"), (o, "o"), (lse, "lse"), (count, "count"), (sink, "sink"),
+                 (gate, "gate")):
         _dense(t, n)
     _dense(idx, "idx", rows=True)
+    if sink is not None and (sink.dtype != torch.float32 or sink.numel() != n_qsets * hq):
+        raise SAError("sink must be float32 [n_qsets, n_heads_q]")
+    if gate is not None and (gate.dtype != q.dtype or tuple(gate.shape) != (n_qsets, R, hq, d_v)):
+        raise SAError("gate must be [n_qsets, R, n_heads_q, d_v] in the query dtype")
     vc = v.c() if v is not None else sa_cache()
     return sa_attn_desc(rows.c(), n_qsets, hq, _ptr(q), _dt(q), int(d_v), k.c(), vc,
                         1 if v is None else 0, 0 if idx is None else int(idx.stride(0)), _ptr(idx),
-                        _ptr(count), float(scale), _dt(o), _ptr(o), _ptr(lse))
+                        _ptr(count), float(scale), _dt(o), _ptr(o), _ptr(lse), _ptr(sink),
+                        _ptr(gate))
 
 
 def attn_gather_fwd(rows: Rows, q: torch.Tensor, k: Cache, v: Optional[Cache] = None,
                     idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
                     scale: Optional[float] = None, d_v: Optional[int] = None,
                     o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    out_dtype=None, want_lse: bool = True):
+                    out_dtype=None, want_lse: bool = True, sink=None, gate=None):
     """Joint-softmax gather attention.  ``v=None`` means V is the first d_v
-    channels of the K row.  Returns (o, lse)."""
+    channels of the K row; ``sink`` [n_qsets, hq] f32 and ``gate`` [n_qsets,
+    R, hq, d_v] are the optional per-head sink bias and output sigmoid gate.
+    Returns (o, lse)."""
     L = load()
     n_qsets, R, hq, dqk = (int(x) for x in q.shape)
     if d_v is None:
@@ -326,7 +336,7 @@ def attn_gather_fwd(rows: Rows, q: torch.Tensor, k: Cache, v: Optional[Cache] = 
         o = torch.empty(n_qsets, R, hq, d_v, dtype=out_dtype or q.dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty(n_qsets, R, hq, dtype=torch.float32, device=q.device)
-    d = attn_desc(rows, q, k, v, idx, count, o, lse, scale, d_v)
+    d = attn_desc(rows, q, k, v, idx, count, o, lse, scale, d_v, sink, gate)
     need = int(L.sa_workspace_size(SA_OP_ATTN_GATHER_FWD, ctypes.byref(d)))
     if need == ctypes.c_size_t(-1).value:
         _check(-2)
@@ -343,7 +353,7 @@ def score_desc(rows: Rows, q, k: Cache, lse, scale: Optional[float] = None) -> s
     _dense(q, "q")
     _dense(lse, "lse")
     return sa_attn_desc(rows.c(), n_qsets, hq, _ptr(q), _dt(q), dqk, k.c(), sa_cache(), 1, 0, None,
-                        None, float(scale), _dt(q), None, _ptr(lse))
+                        None, float(scale), _dt(q), None, _ptr(lse), None, None)
 
 
 def attn_score(rows: Rows, q: torch.Tensor, k: Cache, lse: torch.Tensor, scores=None,
@@ -425,7 +435,7 @@ class PreparedScore:
 
 
 def prepare_attn_gather_fwd(rows: Rows, q, k: Cache, v: Optional[Cache], idx, count, o, lse=None,
-                            scale=None, d_v=None):
-    d = attn_desc(rows, q, k, v, idx, count, o, lse, scale, d_v)
+                            scale=None, d_v=None, sink=None, gate=None):
+    d = attn_desc(rows, q, k, v, idx, count, o, lse, scale, d_v, sink, gate)
     return Prepared("sparse_attn_gather_fwd", d, SA_OP_ATTN_GATHER_FWD, q.device,
-                    keep=(rows, q, k, v, idx, count, o, lse))
+                    keep=(rows, q, k, v, idx, count, o, lse, sink, gate))

@@ -271,6 +271,8 @@ sa_status validate_attn(const sa_attn_desc* d, sa::AttnArgs* out) {
   }
   CHECK((int64_t)d->rows.window + (d->idx ? d->idx_stride : 0) <= 131072, SA_ERR_UNSUPPORTED,
         "%s: window + idx_stride above 131072 entries per row", op);
+  CHECK(!d->gate || aligned16(d->gate), SA_ERR_SHAPE, "%s: gate must be 16-byte aligned", op);
+  CHECK(!d->gate || dv % 8 == 0, SA_ERR_UNSUPPORTED, "%s: a gate needs d_v divisible by 8", op);
   if (out) {
     out->rows = to_dev(d->rows);
     out->k = to_dev(d->k);
@@ -281,6 +283,8 @@ sa_status validate_attn(const sa_attn_desc* d, sa::AttnArgs* out) {
     out->o = d->o;
     out->lse = d->lse;
     out->part = nullptr;
+    out->sink = d->sink;
+    out->gate = d->gate;
     out->scale_log2 = d->scale * sa::kLog2e;
     out->idx_stride = d->idx ? d->idx_stride : 0;
     out->n_qsets = d->n_qsets;

@@ -55,6 +55,78 @@ __device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) {
 // below 2^-126 flush to zero, which softmax weights can afford.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Sink logit of output row (set, head) in log2 units; -inf without a sink.
+__device__ __forceinline__ float sink_log2(const AttnArgs& a, int set, int h) {
+  return a.sink ? a.sink[set * a.hq + h] * kLog2e : -__builtin_huge_valf();
+}
+
+// Final statistics of one output row from its reference m (log2 units), the
+// sums l (rounded probabilities, weighting V) and lx (unrounded) relative to
+// m, and the sink logit s2 (log2 units, -inf for none): the sink is a virtual
+// entry whose value row is zero, so it only adds 2^(s2 - m) to both sums.
+// Returns the factor that turns the accumulated O into the output, and the
+// natural-log LSE.  Without a sink this is 1 / l and (m + log2 lx) ln 2.
+__device__ __forceinline__ float finish_row(float m, float l, float lx, float s2, float& lse) {
+  const float M = fmaxf(m, s2);
+  if (M == -__builtin_huge_valf()) {
+    lse = -__builtin_huge_valf();
+    return 0.0f;
+  }
+  const float f = fast_exp2(m - M), t = fast_exp2(s2 - M);
+  const float den = l * f + t, sx = lx * f + t;
+  lse = sx > 0.0f ? (M + __log2f(sx)) * kLn2 : -__builtin_huge_valf();
+  return den > 0.0f ? f / den : 0.0f;
+}
+
+// sigmoid of gate logits: the output gate of each channel
+__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + fast_exp2(-x * kLog2e)); }
+
+// Multiply n (4 or 8) consecutive output values of element offset `off` (in
+// the o layout) by the sigmoid of their gate logits.
+template <int N>
+__device__ __forceinline__ void apply_gate(const AttnArgs& a, int64_t off, float (&v)[N]) {
+  if (!a.gate) return;
+  if (a.dtype == 1) {
+    const uint16_t* g = reinterpret_cast<const uint16_t*>(a.gate) + off;
+    if constexpr (N == 8) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] *= sigmoid(__uint_as_float(w[i] << 16));
+        v[2 * i + 1] *= sigmoid(__uint_as_float(w[i] & 0xFFFF0000u));
+      }
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(g);
+      v[0] *= sigmoid(__uint_as_float(w.x << 16));
+      v[1] *= sigmoid(__uint_as_float(w.x & 0xFFFF0000u));
+      v[2] *= sigmoid(__uint_as_float(w.y << 16));
+      v[3] *= sigmoid(__uint_as_float(w.y & 0xFFFF0000u));
+    }
+  } else {
+    const float* g = reinterpret_cast<const float*>(a.gate) + off;
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] *= sigmoid(g[i]);
+  }
+}
+
+// Store 8 consecutive output channels at element offset `off`.
+__device__ __forceinline__ void store8(const AttnArgs& a, int64_t off, const float (&v)[8]) {
+  if (a.o_dtype == 1) {
+    u32x4 pk;
+    pk[0] = pack_bf16x2(v[0], v[1]);
+    pk[1] = pack_bf16x2(v[2], v[3]);
+    pk[2] = pack_bf16x2(v[4], v[5]);
+    pk[3] = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.o) + off) = pk;
+  } else {
+    float* op = reinterpret_cast<float*>(a.o) + off;
+    reinterpret_cast<f32x4*>(op)[0] = f32x4{v[0], v[1], v[2], v[3]};
+    reinterpret_cast<f32x4*>(op)[1] = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -650,21 +722,13 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
     }
     const int c0 = 32 * cb + 8 * part;
     if (a.n_split == 1) {
-      const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-      if (a.o_dtype == 1) {
-        u32x4 pk;
-        pk[0] = pack_bf16x2(acc0[0] * inv, acc0[1] * inv);
-        pk[1] = pack_bf16x2(acc0[2] * inv, acc0[3] * inv);
-        pk[2] = pack_bf16x2(acc1[0] * inv, acc1[1] * inv);
-        pk[3] = pack_bf16x2(acc1[2] * inv, acc1[3] * inv);
-        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.o) + orow * DV + c0) = pk;
-      } else {
-        float* op = reinterpret_cast<float*>(a.o) + orow * DV + c0;
-        reinterpret_cast<f32x4*>(op)[0] = acc0 * inv;
-        reinterpret_cast<f32x4*>(op)[1] = acc1 * inv;
-      }
-      if (a.lse && cb == 0 && part == 0)
-        a.lse[orow] = Lx > 0.0f ? (M + __log2f(Lx)) * 0.6931471805599453f : -__builtin_huge_valf();
+      float lse;
+      const float inv = finish_row(M, Ls, Lx, sink_log2(a, set, h), lse);
+      float v[8] = {acc0[0] * inv, acc0[1] * inv, acc0[2] * inv, acc0[3] * inv,
+                    acc1[0] * inv, acc1[1] * inv, acc1[2] * inv, acc1[3] * inv};
+      apply_gate(a, orow * DV + c0, v);
+      store8(a, orow * DV + c0, v);
+      if (a.lse && cb == 0 && part == 0) a.lse[orow] = lse;
     } else {
       const int64_t nrows = (int64_t)a.n_qsets * R * a.hq;
       float* op = a.part + ((int64_t)sp * nrows + orow) * DV + c0;
@@ -691,29 +755,19 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
   const int set = qr / G, h = g * G + qr % G;
   const int64_t orow = ((int64_t)set * R + r) * a.hq + h;
   if (a.n_split == 1) {
-    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    float lse;
+    const float inv = finish_row(m_run, l_run, l_lse, sink_log2(a, set, h), lse);
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
       for (int hh = 0; hh < 4; ++hh) {
         const int c0 = jb * 128 + 32 * gq + 8 * hh;
         const f32x4 v0 = O[jb * 8 + 2 * hh] * inv, v1 = O[jb * 8 + 2 * hh + 1] * inv;
-        if (a.o_dtype == 1) {
-          u32x4 pk;
-          pk[0] = pack_bf16x2(v0[0], v0[1]);
-          pk[1] = pack_bf16x2(v0[2], v0[3]);
-          pk[2] = pack_bf16x2(v1[0], v1[1]);
-          pk[3] = pack_bf16x2(v1[2], v1[3]);
-          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.o) + orow * DV + c0) = pk;
-        } else {
-          float* op = reinterpret_cast<float*>(a.o) + orow * DV + c0;
-          reinterpret_cast<f32x4*>(op)[0] = v0;
-          reinterpret_cast<f32x4*>(op)[1] = v1;
-        }
+        float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        apply_gate(a, orow * DV + c0, v);
+        store8(a, orow * DV + c0, v);
       }
-    if (a.lse && gq == 0)
-      a.lse[orow] = l_lse > 0.0f ? (m_run + __log2f(l_lse)) * 0.6931471805599453f
-                                 : -__builtin_huge_valf();
+    if (a.lse && gq == 0) a.lse[orow] = lse;
   } else {
     const int64_t nrows = (int64_t)a.n_qsets * R * a.hq;
     float* po = a.part + ((int64_t)sp * nrows + orow) * DV;
@@ -1000,24 +1054,18 @@ __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, in
     const float m_r = lds.ml[q][col][0], l_r = lds.ml[q][col][1], lx = lds.ml[q][col][2];
     const f32x4* o = O[q];
     if (a.n_split == 1) {
-      const float inv = l_r > 0.0f ? 1.0f / l_r : 0.0f;
+      float lse;
+      const float inv = finish_row(m_r, l_r, lx, sink_log2(a, set, h), lse);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c0 = wave * 128 + 32 * gq + 8 * i;
-        if (a.o_dtype == 1) {
-          u32x4 pk;
+        float v[8];
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-            pk[qd] = pack_bf16x2(o[2 * qd][i] * inv, o[2 * qd + 1][i] * inv);
-          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.o) + orow * DV + c0) = pk;
-        } else {
-          float* op = reinterpret_cast<float*>(a.o) + orow * DV + c0;
-          reinterpret_cast<f32x4*>(op)[0] = f32x4{o[0][i] * inv, o[1][i] * inv, o[2][i] * inv, o[3][i] * inv};
-          reinterpret_cast<f32x4*>(op)[1] = f32x4{o[4][i] * inv, o[5][i] * inv, o[6][i] * inv, o[7][i] * inv};
-        }
+        for (int j = 0; j < 8; ++j) v[j] = o[j][i] * inv;
+        apply_gate(a, orow * DV + c0, v);
+        store8(a, orow * DV + c0, v);
       }
-      if (a.lse && wave == 0 && gq == 0)
-        a.lse[orow] = lx > 0.0f ? (m_r + __log2f(lx)) * 0.6931471805599453f : -__builtin_huge_valf();
+      if (a.lse && wave == 0 && gq == 0) a.lse[orow] = lse;
     } else {
       const int64_t nrows = (int64_t)a.n_qsets * R_ * a.hq;
       float* po = a.part + ((int64_t)sp * nrows + orow) * DV;
@@ -1076,9 +1124,16 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   const float M = wave_max(m);
   const float f = (l > 0.0f && M != -__builtin_huge_valf()) ? exp2f(m - M) : 0.0f;
   const float L = wave_sum(f * l), Lx = wave_sum(f * lx);
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  const int set = (int)(row / ((int64_t)a.rows.n_rows * a.hq)), h = (int)(row % a.hq);
+  float lse;
+  const float inv = finish_row(M, L, Lx, sink_log2(a, set, h), lse);
   auto put = [&](f32x4 acc, int c0) {
     acc *= inv;
+    if (a.gate) {
+      float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+      apply_gate(a, row * DV + c0, v);
+      acc = f32x4{v[0], v[1], v[2], v[3]};
+    }
     if (a.o_dtype == 1) {
       uint2 pk;
       pk.x = pack_bf16x2(acc[0], acc[1]);
@@ -1110,8 +1165,7 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
     }
     put(acc, c0);
   }
-  if (a.lse && lane == 0)
-    a.lse[row] = Lx > 0.0f ? (M + __log2f(Lx)) * 0.6931471805599453f : -__builtin_huge_valf();
+  if (a.lse && lane == 0) a.lse[row] = lse;
 }
 
 // F32 path: one wave per (row, KV head, query set, query head); entries in
@@ -1181,18 +1235,19 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
     }
     __builtin_amdgcn_wave_barrier();
   }
-  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  float lse;
+  const float inv = finish_row(m_run, l_run, l_run, sink_log2(a, set, h), lse);
   for (int k = 0; k < 4; ++k) {
     const int c = lane + 64 * k;
     if (c >= a.dv) continue;
+    float v = acc[k] * inv;
+    if (a.gate) v *= sigmoid(reinterpret_cast<const float*>(a.gate)[orow * a.dv + c]);
     if (a.o_dtype == 1)
-      reinterpret_cast<uint16_t*>(a.o)[orow * a.dv + c] = (uint16_t)f32_to_bf16_bits(acc[k] * inv);
+      reinterpret_cast<uint16_t*>(a.o)[orow * a.dv + c] = (uint16_t)f32_to_bf16_bits(v);
     else
-      reinterpret_cast<float*>(a.o)[orow * a.dv + c] = acc[k] * inv;
+      reinterpret_cast<float*>(a.o)[orow * a.dv + c] = v;
   }
-  if (a.lse && lane == 0)
-    a.lse[orow] = l_run > 0.0f ? (m_run + __log2f(l_run)) * 0.6931471805599453f
-                               : -__builtin_huge_valf();
+  if (a.lse && lane == 0) a.lse[orow] = lse;
 }
 
 // Waves per entry group (one 16-row query tile each) and entry groups per

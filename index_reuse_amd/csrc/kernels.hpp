@@ -63,6 +63,8 @@ struct AttnArgs {
   void* o;              // [n_qsets][R][hq][dv]
   float* lse;           // [n_qsets][R][hq] or NULL
   float* part;          // split partials (workspace) or NULL
+  const float* sink;    // [n_qsets][hq] sink logits (natural units) or NULL
+  const void* gate;     // [n_qsets][R][hq][dv] output gate logits (dtype) or NULL
   float scale_log2;     // softmax scale * log2(e)
   int32_t idx_stride;
   int32_t n_qsets;

@@ -3,9 +3,11 @@
 // Token mode ("HySparse2", section 7.2): the candidates of a row are the
 // visible entries outside the forced window; keep the first min(k, n) in the
 // order (score desc, index asc).  Pool mode ("CSA, HCA and CSA2", section
-// 3.2, Hierarchical Sparse Indexer): every aligned block of `block` entries is
-// scored by its maximum over visible members, the first max_blocks blocks in
-// (max desc, block asc) order are kept and their members form the pool.
+// 3.2, Hierarchical Sparse Indexer; "HySparse2", appendix A.1, the first
+// generation's selection of 16 blocks of 64 tokens): every aligned block of
+// `block` entries is scored by its maximum over its candidates (visible
+// entries outside the window), the first max_blocks blocks in (max desc,
+// block asc) order are kept and their candidates form the pool.
 //
 // Scores become order-preserving uint32 keys (-0 folded onto +0; key 0 marks
 // a non-candidate).  The kept set is {key > theta} plus the first t elements
@@ -246,8 +248,8 @@ __device__ __forceinline__ Src<KIND> make_src(const SelectArgs& a, const Ws& ws,
   s.list = nullptr;
   if constexpr (KIND == SRC_BLOCK) {
     s.sc = ws.beta + (int64_t)r * a.beta_stride;
-    s.n = (ri.n_avail + a.block - 1) / a.block;
-    s.win_lo = ri.n_avail;
+    s.n = (ri.win_lo + a.block - 1) / a.block;  // blocks of the candidates (outside the window)
+    s.win_lo = ri.win_lo;
   } else if constexpr (KIND == SRC_POOL) {
     s.sc = a.scores + (int64_t)r * a.score_stride;
     s.list = a.pool + (int64_t)r * a.pool_stride;
@@ -269,10 +271,10 @@ __global__ __launch_bounds__(256) void block_max_kernel(SelectArgs a, Ws ws) {
   const int r = blockIdx.y;
   const int j = blockIdx.x * 256 + threadIdx.x;
   const RowInfo ri = row_info(a.rows, r);
-  const int nb = (ri.n_avail + a.block - 1) / a.block;
+  const int nb = (ri.win_lo + a.block - 1) / a.block;
   if (j >= nb) return;
   const float* sc = a.scores + (int64_t)r * a.score_stride;
-  const int lo = j * a.block, hi = min(lo + a.block, ri.n_avail);
+  const int lo = j * a.block, hi = min(lo + a.block, ri.win_lo);
   float m;
   if (a.block == 8 && hi - lo == 8 && (reinterpret_cast<uintptr_t>(sc + lo) & 15) == 0) {
     // a whole block of 8 as two 16-byte loads
@@ -668,7 +670,7 @@ __global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int 
         const uint32_t kl = s.key(n - 1);
         last_kept = mode == 1 ? kl != 0u : (kl > theta || (kl == theta && e_total - 1 < t_eq));
       }
-      const int pool_n = take * bs - (last_kept ? n * bs - ri.n_avail : 0);
+      const int pool_n = take * bs - (last_kept ? n * bs - ri.win_lo : 0);
       for (int i = pool_n + tid; i < a.max_blocks * bs; i += kChunkT) out[i] = -1;
       if (tid == 0) a.pool_count[r] = pool_n;
     } else {
@@ -709,7 +711,7 @@ __global__ __launch_bounds__(kChunkT) void emit_kernel(SelectArgs a, Ws ws, int 
       const int j = j0 + chunk_elem<CHUNK>(q);
       const int rank = o + (int)__popcll(mk & below);
       if (pool_mode) {
-        const int lo = j * bs, mm = min(bs, ri.n_avail - lo);
+        const int lo = j * bs, mm = min(bs, ri.win_lo - lo);
         for (int u = 0; u < mm; ++u) out[rank * bs + u] = lo + u;
       } else {
         out[rank] = s.position(j);
@@ -1037,7 +1039,7 @@ __global__ __launch_bounds__(kRowT) void row_select_kernel(SelectArgs a, Ws ws, 
       const uint32_t kl = s.key(n - 1);  // the highest-index block: a tie is kept iff all are
       last_kept = mode == 1 ? kl != 0u : (kl > theta || (kl == theta && simple));
     }
-    const int pool_n = take * bs - (last_kept ? n * bs - ri.n_avail : 0);
+    const int pool_n = take * bs - (last_kept ? n * bs - ri.win_lo : 0);
     for (int i = pool_n + tid; i < a.max_blocks * bs; i += kRowT) out[i] = -1;
     if (tid == 0) a.pool_count[r] = pool_n;
   } else {
@@ -1050,7 +1052,7 @@ __global__ __launch_bounds__(kRowT) void row_select_kernel(SelectArgs a, Ws ws, 
   const bool vec8 = pool_mode && bs == 8 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
   auto put = [&](int j, int rank) {
     if constexpr (pool_mode) {
-      const int lo = j * bs, mm = min(bs, ri.n_avail - lo);
+      const int lo = j * bs, mm = min(bs, ri.win_lo - lo);
       if (vec8 && mm == 8) {
         int32_t* o8 = out + rank * 8;
         reinterpret_cast<i32x4*>(o8)[0] = i32x4{lo, lo + 1, lo + 2, lo + 3};
@@ -1167,11 +1169,11 @@ hipError_t launch_topk_select(const SelectArgs& a, hipStream_t st) {
     run_select<SRC_BLOCK>(a, ws, a.beta_stride, a.max_blocks, 1, st);
   }
   if (a.k > 0) {
-    // The pool holds the whole token top-k when there is no window and at
-    // least k blocks are kept: a block left out has max_blocks blocks before
-    // it in (max desc, block asc) order, and each of their maxima ranks
-    // before every token of the left-out block.
-    if (a.pool && a.rows.window == 0 && a.max_blocks >= a.k)
+    // The pool holds the whole token top-k when at least k blocks are kept
+    // (blocks and tokens both range over the candidates): a block left out
+    // has max_blocks blocks before it in (max desc, block asc) order, and each
+    // of their maxima ranks before every token of the left-out block.
+    if (a.pool && a.max_blocks >= a.k)
       run_select<SRC_POOL>(a, ws, (int64_t)a.max_blocks * a.block, a.k, 0, st);
     else if (a.cand)
       run_select<SRC_TOKEN_CAND>(a, ws, a.cand_stride, a.k, 0, st);

@@ -48,8 +48,15 @@ class Step:
     top-k inside the pool -> attention with the Full indices (Full query) and
     with the Reindex indices (Reindex query + Reuse queries, fused)."""
 
-    def __init__(self, prob, scores_slots: Optional[int] = None, dense_route: bool = False):
+    def __init__(self, prob, scores_slots: Optional[int] = None, dense_route: bool = False,
+                 block_select=None):
+        """``block_select`` = (block, n_blocks): select whole aligned blocks of
+        candidates by their best score instead of single entries (HySparse's
+        first generation: 16 blocks of 64 tokens next to the window); the
+        pool of kept blocks is the index tensor."""
         wl = prob.wl
+        assert block_select is None or not wl.block, "block selection replaces the token top-k"
+        self.block_select = block_select
         self.prob = prob
         self.wl = wl
         dev = prob.seq_of_row.device
@@ -59,7 +66,8 @@ class Step:
         self.selector = wl.k > 0
         # dense route: rows whose candidates all fit the budget skip the
         # indexer (scores 0; the selection keeps every candidate either way)
-        self.skip_k = wl.k if dense_route else 0
+        budget = wl.k if block_select is None else block_select[0] * block_select[1]
+        self.skip_k = budget if dense_route else 0
         self.kidx = _cache(prob.kidx, 1, wl.idx_dim) if self.selector else None
         fp4 = wl.kv_mode == "fp4"
         self.k = _cache(prob.k, wl.hkv, wl.dqk, fp4=fp4)
@@ -68,7 +76,8 @@ class Step:
         f32 = torch.float32
         i32 = torch.int32
         self.scores = [torch.empty(R, self.S, dtype=f32, device=dev)]
-        self.idx = [torch.empty(R, wl.k, dtype=i32, device=dev)]
+        width = wl.k if block_select is None else block_select[0] * block_select[1]
+        self.idx = [torch.empty(R, width, dtype=i32, device=dev)]
         self.count = [torch.empty(R, dtype=i32, device=dev)]
         self.pool = self.pool_count = None
         if wl.block:
@@ -98,7 +107,12 @@ class Step:
             return self._prepared
         calls = [("index_score", prepare_index_score(self.rows, p.idx_q[0], p.idx_w[0], self.kidx,
                                                      self.scores[0], skip_k=self.skip_k))]
-        if not wl.block:
+        if self.block_select is not None:
+            bs, nb = self.block_select
+            calls.append(("topk_select", prepare_topk_select(
+                self.rows, self.scores[0], 0, None, None, block=bs, max_blocks=nb,
+                pool=self.idx[0], pool_count=self.count[0])))
+        elif not wl.block:
             calls.append(("topk_select", prepare_topk_select(self.rows, self.scores[0], wl.k,
                                                              self.idx[0], self.count[0])))
         else:
@@ -125,6 +139,11 @@ class Step:
             return
         index_score(self.rows, p.idx_q[0], p.idx_w[0], self.kidx, scores=self.scores[0],
                     skip_k=self.skip_k)
+        if self.block_select is not None:
+            bs, nb = self.block_select
+            topk_select(self.rows, self.scores[0], 0, block=bs, max_blocks=nb,
+                        pool=self.idx[0], pool_count=self.count[0])
+            return
         if not wl.block:
             topk_select(self.rows, self.scores[0], wl.k, idx=self.idx[0], count=self.count[0])
             return

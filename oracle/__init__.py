@@ -64,7 +64,7 @@ def lib():
         L.orc_attention.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P, P, P, P,
-                                    ctypes.c_int, i64, P, i64, P, f32, P, P]
+                                    ctypes.c_int, i64, P, i64, P, f32, P, ctypes.c_int, P, P, P]
         L.orc_fa_score.restype = ctypes.c_int
         L.orc_fa_score.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int, P,
@@ -195,8 +195,9 @@ def topk_select(seq_of_row, pos_of_row, seq_len, stride: int, window: int, score
 def attention(seq_of_row, pos_of_row, seq_len, stride: int, window: int, q: torch.Tensor,
               K: torch.Tensor, V=None, idx=None, count=None, scale: float = None, hkv: int = None,
               k_scale: torch.Tensor = None, v_scale: torch.Tensor = None, v_from_k: bool = False,
-              dv: int = None, fp4: bool = False):
-    """Joint softmax over window + selected positions.
+              dv: int = None, fp4: bool = False, sink=None, gate: torch.Tensor = None):
+    """Joint softmax over window + selected positions (``sink`` [n_sets, Hq]
+    and ``gate`` [n_sets, R, Hq, dv]: the optional sink bias and output gate).
 
     q [n_sets, R, Hq, dqk]; K logical [B, Lcap, Hkv, dqk] (or FP4 codes
     [B, Lcap, Hkv, dqk/2] uint8 with ``k_scale`` [B, Lcap, Hkv, dqk/16]).
@@ -230,10 +231,17 @@ def attention(seq_of_row, pos_of_row, seq_len, stride: int, window: int, q: torc
         scale = 1.0 / float(np.sqrt(dqk))
     o = np.empty((n_sets, R, Hq, dv), dtype=np.float64)
     lse = np.empty((n_sets, R, Hq), dtype=np.float64)
+    sa = None
+    if sink is not None:
+        sink = sink.detach().cpu() if isinstance(sink, torch.Tensor) else torch.as_tensor(sink)
+        sa = np.ascontiguousarray(sink.float().numpy().reshape(n_sets, Hq))
+    ga, gd = None, F32
+    if gate is not None:
+        ga, gd = _raw(gate), _code(gate)
     rc = lib().orc_attention(n_sets, R, _ptr(so), _ptr(po), _ptr(sl), stride, window, Hq, Hkv, dqk,
                              dv, _code(q), _ptr(qa), kd, _ptr(ka), _ptr(ksa), _ptr(va), _ptr(vsa),
                              1 if v_from_k else 0, Lcap, _ptr(ia), istride, _ptr(ca),
-                             ctypes.c_float(scale), _ptr(o), _ptr(lse))
+                             ctypes.c_float(scale), _ptr(sa), gd, _ptr(ga), _ptr(o), _ptr(lse))
     if rc != 0:
         raise ValueError("orc_attention failed (%d)" % rc)
     return o, lse

@@ -230,10 +230,14 @@ static int cmp_i64_asc(const void* a, const void* b) {
  * idx[r][count..k) = -1.
  *
  * Pool mode (block > 0, full mode only): blocks j = floor(s / block) over the
- * whole domain (window included), beta_j = max score of the block's domain
- * members; the first min(max_blocks, n_blocks) blocks under (beta desc, j asc)
- * are kept and the ascending union of their members is written to
- * pool[r][0..pool_count), pool[r][pool_count..max_blocks*block) = -1.
+ * candidates C_t = [0, win_lo) (the visible positions outside the window;
+ * with window 0 the whole domain), beta_j = max score of the block's
+ * candidates; the first min(max_blocks, n_blocks) blocks under (beta desc,
+ * j asc) are kept and the ascending union of their candidates is written to
+ * pool[r][0..pool_count), pool[r][pool_count..max_blocks*block) = -1.  The
+ * pool is therefore also a block-level selection in the index format ("HySparse2"
+ * page, appendix A.1: the first generation selects 16 blocks of 64 tokens
+ * next to a 128-token window).
  */
 int orc_topk_select(int R, const int32_t* seq_of_row, const int32_t* pos_of_row,
                     const int32_t* seq_len, int stride, int window, const double* scores,
@@ -273,11 +277,11 @@ int orc_topk_select(int R, const int32_t* seq_of_row, const int32_t* pos_of_row,
       free(c);
     }
     if (block > 0) {
-      int64_t nb = (na + block - 1) / block;
+      int64_t nb = (win_lo + block - 1) / block;
       scored_pos* bl = (scored_pos*)malloc(sizeof(scored_pos) * (size_t)(nb > 0 ? nb : 1));
       for (int64_t j = 0; j < nb; ++j) {
         double m = -INFINITY;
-        for (int64_t s = j * block; s < (j + 1) * block && s < na; ++s) {
+        for (int64_t s = j * block; s < (j + 1) * block && s < win_lo; ++s) {
           double v = scores[(int64_t)r * S + s];
           if (v > m) m = v;
         }
@@ -291,7 +295,7 @@ int orc_topk_select(int R, const int32_t* seq_of_row, const int32_t* pos_of_row,
       qsort(kb, (size_t)keep, sizeof(int64_t), cmp_i64_asc);
       int64_t cap = (int64_t)max_blocks * block, n = 0;
       for (int64_t i = 0; i < keep; ++i)
-        for (int64_t s = kb[i] * block; s < (kb[i] + 1) * block && s < na; ++s)
+        for (int64_t s = kb[i] * block; s < (kb[i] + 1) * block && s < win_lo; ++s)
           pool[(int64_t)r * cap + n++] = (int32_t)s;
       pool_count[r] = (int32_t)n;
       for (; n < cap; ++n) pool[(int64_t)r * cap + n] = -1;
@@ -320,13 +324,23 @@ int orc_topk_select(int R, const int32_t* seq_of_row, const int32_t* pos_of_row,
  * head h reads KV head floor(h * Hkv / Hq). logit_s = scale * q . K_s; one
  * softmax over A_t; o = sum p_s V_s; lse = log sum exp(logit). Empty A_t gives
  * o = 0 and lse = -inf.
+ *
+ * Optional per-head sink bias and output sigmoid gate ("HySparse2" page,
+ * section 17.1: every SA layer has an output sigmoid gate and a learnable
+ * per-head sink bias): sink [n_sets][Hq] (float, may be NULL) is the logit of
+ * one more entry whose value row is zero, so it joins the normaliser only:
+ * p_s = exp(logit_s) / (exp(sink) + sum exp(logit)), lse = log(exp(sink) +
+ * sum exp(logit)), and an empty A_t gives o = 0, lse = sink.  gate
+ * [n_sets][R][Hq][dv] (gate_dtype, may be NULL) multiplies output channel c by
+ * 1 / (1 + exp(-gate[c])).
  */
 int orc_attention(int n_sets, int R, const int32_t* seq_of_row, const int32_t* pos_of_row,
                   const int32_t* seq_len, int stride, int window, int Hq, int Hkv, int dqk,
                   int dv, int q_dtype, const void* q, int kv_dtype, const void* K,
                   const uint8_t* k_scale, const void* V, const uint8_t* v_scale, int v_from_k,
                   int64_t Lcap, const int32_t* idx, int64_t idx_stride, const int32_t* count,
-                  float scale, double* o, double* lse) {
+                  float scale, const float* sink, int gate_dtype, const void* gate, double* o,
+                  double* lse) {
   if (n_sets <= 0 || R < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || dqk <= 0 || dv <= 0)
     return ORC_EINVAL;
   if (v_from_k && dv > dqk) return ORC_EINVAL;
@@ -375,8 +389,9 @@ int orc_attention(int n_sets, int R, const int32_t* seq_of_row, const int32_t* p
       if (m == 0 || A[i] != A[m - 1]) A[m++] = A[i];
     n = m;
 
+    const double sk = sink ? (double)sink[(int64_t)set * Hq + h] : -INFINITY;
     if (n == 0 || b < 0) {
-      lse[it] = -INFINITY;
+      lse[it] = sk;
       free(A);
       free(logit);
       continue;
@@ -397,7 +412,8 @@ int orc_attention(int n_sets, int R, const int32_t* seq_of_row, const int32_t* p
       logit[i] = sc * dot;
       if (logit[i] > mx) mx = logit[i];
     }
-    double sum = 0.0;
+    if (sk > mx) mx = sk;
+    double sum = sink ? exp(sk - mx) : 0.0;
     for (int64_t i = 0; i < n; ++i) sum += exp(logit[i] - mx);
     for (int64_t i = 0; i < n; ++i) {
       double p = exp(logit[i] - mx) / sum;
@@ -419,6 +435,9 @@ int orc_attention(int n_sets, int R, const int32_t* seq_of_row, const int32_t* p
       }
     }
     lse[it] = mx + log(sum);
+    if (gate)
+      for (int c = 0; c < dv; ++c)
+        orow[c] *= 1.0 / (1.0 + exp(-load_elem(gate, gate_dtype, it * dv + c)));
     free(A);
     free(logit);
   }

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_abi_version(lib):
     v = ira.abi_version()
-    assert v >> 16 == 1 and v & 0xFFFF == 1
+    assert v >> 16 == 2 and v & 0xFFFF == 1
 
 
 def test_struct_layout_matches_c_compiler(tmp_path):

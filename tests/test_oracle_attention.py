@@ -214,3 +214,74 @@ def test_latent_576_512_single_entry(orc):
     assert np.array_equal(o[0, 0], np.repeat(first[None], Hq, 0))
     mean = K[0, :, 0, :512].double().mean(0).numpy()
     assert np.allclose(o[0, 1], np.repeat(mean[None], Hq, 0), rtol=1e-14, atol=1e-14)
+
+
+def test_sink_is_a_zero_valued_entry(orc):
+    """A sink logit s joins the normaliser like one more entry whose value row
+    is zero ("HySparse2", section 17.1: a learnable per-head sink bias): the
+    oracle with sink s equals the oracle without a sink over the same set
+    plus an extra entry built so that its logit is exactly s (q[0] = 1,
+    k*[0] = s / scale, every other channel zero) and its value row is 0."""
+    g = torch.Generator().manual_seed(90)
+    L, Hq, d = 20, 3, 8
+    scale, s = 0.25, 1.5
+    K = torch.randn(1, L + 1, Hq, d, generator=g)
+    V = torch.randn(1, L + 1, Hq, d, generator=g)
+    q = torch.randn(1, 1, Hq, d, generator=g)
+    q[..., 0] = 1.0
+    K[0, L] = 0.0
+    K[0, L, :, 0] = s / scale
+    V[0, L] = 0.0
+    so = np.zeros(1, np.int32)
+    sl_small, sl_big = np.array([L], np.int32), np.array([L + 1], np.int32)
+    a, la = orc.attention(so, np.array([L - 1], np.int32), sl_small, 1, L, q, K, V, None, None,
+                          scale=scale, sink=torch.full((1, Hq), s))
+    b, lb = orc.attention(so, np.array([L], np.int32), sl_big, 1, L + 1, q, K, V, None, None,
+                          scale=scale)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-15)
+    assert np.allclose(la, lb, rtol=1e-13, atol=1e-15)
+    # a sink far below every logit changes nothing
+    c, lc = orc.attention(so, np.array([L - 1], np.int32), sl_small, 1, L, q, K, V, None, None,
+                          scale=scale, sink=torch.full((1, Hq), -1e30))
+    d0, ld = orc.attention(so, np.array([L - 1], np.int32), sl_small, 1, L, q, K, V, None, None,
+                           scale=scale)
+    assert np.array_equal(c, d0) and np.array_equal(lc, ld)
+
+
+def test_sink_single_entry_and_empty(orc):
+    """One visible entry with logit l and sink s: o = v / (1 + exp(s - l)) and
+    lse = log(exp(l) + exp(s)); an empty set gives o = 0 and lse = s."""
+    K = torch.tensor([[[[2.0, 0.0]]]])            # [1, 1, 1, 2]
+    V = torch.tensor([[[[3.0, -1.0]]]])
+    q = torch.tensor([[[[1.0, 5.0]]]])            # logit = scale * 2
+    so = np.array([0, -1], np.int32)
+    po = np.array([0, 0], np.int32)
+    sl = np.array([1], np.int32)
+    q2 = torch.cat([q, q], dim=1)
+    o, lse = orc.attention(so, po, sl, 1, 1, q2, K, V, None, None, scale=0.5,
+                           sink=torch.tensor([[0.25]]))
+    lg = 1.0
+    assert np.allclose(o[0, 0, 0], np.array([3.0, -1.0]) / (1 + math.exp(0.25 - lg)), rtol=1e-15)
+    assert abs(lse[0, 0, 0] - math.log(math.exp(lg) + math.exp(0.25))) < 1e-15
+    assert np.all(o[0, 1] == 0) and lse[0, 1, 0] == 0.25
+
+
+def test_output_gate_closed_forms(orc):
+    """The output gate multiplies each channel by 1 / (1 + exp(-g)): g = 0
+    halves it exactly, g = ln 3 scales it by 3/4, and a very negative g
+    zeroes it; the LSE does not depend on the gate."""
+    g_ = torch.Generator().manual_seed(91)
+    L, Hq, d = 9, 2, 4
+    K = torch.randn(1, L, 1, d, generator=g_)
+    V = torch.randn(1, L, 1, d, generator=g_)
+    q = torch.randn(1, 1, Hq, d, generator=g_)
+    so, po, sl = np.zeros(1, np.int32), np.array([L - 1], np.int32), np.array([L], np.int32)
+    base, lb = orc.attention(so, po, sl, 1, L, q, K, V, None, None, scale=0.3)
+    gate = torch.zeros(1, 1, Hq, d, dtype=torch.float64)
+    gate[..., 1] = math.log(3.0)
+    gate[..., 2] = -1e4
+    o, lse = orc.attention(so, po, sl, 1, L, q, K, V, None, None, scale=0.3, gate=gate.float())
+    assert np.array_equal(o[..., 0], base[..., 0] / 2)
+    assert np.allclose(o[..., 1], base[..., 1] * 0.75, rtol=1e-7)
+    assert np.all(o[..., 2] == 0.0)
+    assert np.array_equal(lse, lb)

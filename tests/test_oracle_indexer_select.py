@@ -241,3 +241,30 @@ def test_reindex_with_own_query_returns_full_topk(orc):
         for r in range(R):
             assert set(idx[r, :cnt[r]]) <= set(pool[r, :pc[r]])
         assert np.array_equal(idx, ridx)
+
+
+@pytest.mark.parametrize("window", [5, 64, 200])
+def test_block_pool_with_window_is_block_selection(orc, window):
+    """With a forced window the blocks range over the candidates only (the
+    visible positions before the window): the pool equals the brute-force
+    block choice over [0, win_lo), never holds a window position, and with
+    max_blocks covering every block it is exactly [0, win_lo).  This is the
+    first-generation HySparse block selection ("HySparse2", appendix A.1: 16
+    blocks of 64 tokens next to a window of 128) in the index format; with
+    max_blocks >= k the token top-k lies inside it."""
+    rng = np.random.default_rng(300 + window)
+    L, R, block, mb = 700, 5, 64, 4
+    po = np.array([699, 400, 250, 64, 3], np.int32)
+    so, sl = np.zeros(R, np.int32), np.array([L], np.int32)
+    scores = rng.integers(0, 9, (R, L)).astype(np.float64)
+    idx, cnt, pool, pc = orc.topk_select(so, po, sl, 1, window, scores, mb, block=block,
+                                         max_blocks=mb)
+    _, _, full, fc = orc.topk_select(so, po, sl, 1, window, scores, 1, block=block,
+                                     max_blocks=1000)
+    for r in range(R):
+        win_lo = max(0, po[r] + 1 - window)
+        want = _brute_pool(scores[r], win_lo, block, mb)
+        assert list(pool[r, :pc[r]]) == want
+        assert np.all(pool[r, pc[r]:] == -1) and (pc[r] == 0 or pool[r, pc[r] - 1] < win_lo)
+        assert list(full[r, :fc[r]]) == list(range(win_lo))
+        assert set(idx[r, :cnt[r]]) <= set(pool[r, :pc[r]])
