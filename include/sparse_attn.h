@@ -303,6 +303,20 @@ sa_status sparse_attn_gather_fwd(const sa_attn_desc* desc, void* ws, size_t ws_b
                                  void* stream);
 
 /*
+ * sparse_attn_gather_fwd_noalloc -- sparse_attn_gather_fwd for callers that
+ * cannot allocate or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same descriptor, same
+ * kernels, same results; the split partials that sparse_attn_gather_fwd keeps
+ * in `ws` live instead in one static device array of 64 MiB per GPU, which
+ * the library holds until the process ends.  A call needing more partials
+ * than that (sa_workspace_size(SA_OP_ATTN_GATHER_FWD, desc) > 64 MiB) returns
+ * SA_ERR_WORKSPACE and launches nothing.  The call allocates and frees
+ * nothing.  Every call on one GPU shares that GPU's array (nothing in it needs
+ * to start at any value): calls that overlap in time on one GPU race.
+ */
+sa_status sparse_attn_gather_fwd_noalloc(const sa_attn_desc* desc, void* stream);
+
+/*
  * sparse_attn_score -- the selection score of a full-attention layer
  * ["HySparse2", appendix A.1: the FA layer runs ordinary full attention and
  * picks the important history positions from its own attention scores, and

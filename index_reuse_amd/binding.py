@@ -58,8 +58,8 @@ class sa_attn_desc(ctypes.Structure):
 
 
 EXPORTS = ("sparse_index_score", "sparse_topk_select", "sparse_attn_gather_fwd",
-           "sparse_attn_score", "sparse_check_indices", "sa_workspace_size", "sa_last_error",
-           "sa_abi_version")
+           "sparse_attn_gather_fwd_noalloc", "sparse_attn_score", "sparse_check_indices",
+           "sa_workspace_size", "sa_last_error", "sa_abi_version")
 
 _lib = None
 
@@ -83,6 +83,8 @@ def load(path: str = LIB_PATH):
     L.sparse_index_score.argtypes = [ctypes.POINTER(sa_index_desc), _P, ctypes.c_size_t, _P]
     L.sparse_topk_select.argtypes = [ctypes.POINTER(sa_topk_desc), _P, ctypes.c_size_t, _P]
     L.sparse_attn_gather_fwd.argtypes = [ctypes.POINTER(sa_attn_desc), _P, ctypes.c_size_t, _P]
+    L.sparse_attn_gather_fwd_noalloc.restype = _i32
+    L.sparse_attn_gather_fwd_noalloc.argtypes = [ctypes.POINTER(sa_attn_desc), _P]
     L.sparse_attn_score.restype = _i32
     L.sparse_attn_score.argtypes = [ctypes.POINTER(sa_attn_desc), _P, _i64, _P]
     L.sparse_check_indices.restype = _i32

@@ -412,6 +412,18 @@ sa_status sparse_check_indices(const sa_topk_desc* desc, uint32_t* err, void* st
   return hip_status(sa::launch_check_indices(a, (hipStream_t)stream), op);
 }
 
+sa_status sparse_attn_gather_fwd_noalloc(const sa_attn_desc* desc, void* stream) {
+  const char* op = "sparse_attn_gather_fwd_noalloc";
+  sa::AttnArgs a;
+  sa_status st = validate_attn(desc, &a);
+  if (st || desc->rows.n_rows == 0) return st;
+  const size_t need = sa::attn_workspace_bytes(a);
+  CHECK(need <= sa::kNoAllocScratchBytes, SA_ERR_WORKSPACE,
+        "%s: the call needs %zu bytes of split partials, above the %zu-byte static scratch", op,
+        need, sa::kNoAllocScratchBytes);
+  return hip_status(sa::launch_attn_gather_noalloc(a, (hipStream_t)stream), op);
+}
+
 size_t sa_workspace_size(int32_t op, const void* desc) {
   switch (op) {
     case SA_OP_INDEX_SCORE:

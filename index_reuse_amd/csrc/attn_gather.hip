@@ -32,6 +32,9 @@
 //      statistics are reduced with the gfx950 lane-swap instructions.
 // Long entry lists are split across workgroups; a combine kernel merges the
 // (max, sum, unnormalised O) partials.  F32 inputs use a plain VALU kernel.
+#include <atomic>
+#include <mutex>
+
 #include "kernels.hpp"
 
 namespace sa {
@@ -1363,6 +1366,57 @@ hipError_t launch_attn_gather(const AttnArgs& a, hipStream_t s) {
     if (a.dqk == 512 && a.dv == 512) return launch_shaped<512, 512, KV_FP4, 4>(a, s);
   }
   return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------ allocation-free variant
+// Split partials of sparse_attn_gather_fwd_noalloc live in one static device
+// array per GPU, so the call needs no workspace argument and allocates
+// nothing.  The host never passes the array's name to a kernel (in host code
+// it is only a stand-in): its device address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// used.  Calls that overlap in time on one GPU share the array and race.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, looked up on first use.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_attn_gather_noalloc(AttnArgs a, hipStream_t s) {
+  if (a.rows.n_rows == 0) return hipSuccess;
+  if (attn_workspace_bytes(a) > kNoAllocScratchBytes) return hipErrorInvalidValue;
+  a.part = nullptr;
+  if (a.n_split > 1) {
+    void* p = nullptr;
+    const hipError_t e = scratch_address(&p);
+    if (e != hipSuccess) return e;
+    a.part = reinterpret_cast<float*>(p);
+  }
+  return launch_attn_gather(a, s);
 }
 
 }  // namespace sa

@@ -81,6 +81,10 @@ struct AttnArgs {
 size_t attn_workspace_bytes(const AttnArgs& a);
 void attn_plan(AttnArgs& a);  // fills n_split
 hipError_t launch_attn_gather(const AttnArgs& a, hipStream_t s);
+// The allocation-free variant: split partials in a static per-device array
+// of kNoAllocScratchBytes (hipErrorInvalidValue if a call needs more).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t launch_attn_gather_noalloc(AttnArgs a, hipStream_t s);
 
 // ------------------------------------------------- full-attention score
 struct ScoreArgs {
