@@ -352,12 +352,25 @@ def prefill_work_rows(wl, pos, seq_len: int):
     cand = np.maximum(n - wl.window, 0)
     sel = np.minimum(cand, wl.k)
     attn_pairs = int((np.minimum(n, wl.window) + sel).sum())
-    return {
+    out = {
         "index_score": 2.0 * pairs * wl.idx_heads * wl.idx_dim,
         "attn_gather_fwd": 2.0 * attn_pairs * wl.hq * (wl.dqk + wl.dv),
         "topk_select": 4.0 * int(cand.sum()) + 4.0 * len(pos) * (wl.k + 1),
         "pairs": pairs, "attn_pairs": attn_pairs,
     }
+    if wl.block:
+        # the pool of a row: every candidate while they fit max_blocks blocks,
+        # else max_blocks whole blocks (a kept partial last block trims it by
+        # fewer than `block` entries: ignored)
+        pool = np.minimum(cand, wl.max_blocks * wl.block)
+        sel_r = np.minimum(pool, wl.k)
+        sets_r = 1 + wl.n_reuse
+        out["pool_pairs"] = int(pool.sum())
+        out["topk_select"] += 4.0 * int(pool.sum())
+        out["index_score_reindex"] = 2.0 * int(pool.sum()) * wl.idx_heads * wl.idx_dim
+        out["topk_select_reindex"] = 8.0 * int(pool.sum()) + 4.0 * len(pos) * (wl.k + 1)
+        out["attn_gather_fwd_1"] = 2.0 * int(sel_r.sum()) * sets_r * wl.hq * (wl.dqk + wl.dv)
+    return out
 
 
 def prefill_cpu_baseline(prob, n_rows: int, min_seconds: float):
@@ -380,16 +393,25 @@ def prefill_cpu_baseline(prob, n_rows: int, min_seconds: float):
 
     kl = logical(prob.kidx)
     K = logical(prob.k)
-    q_idx, w = prob.idx_q[0][rows].cpu(), prob.idx_w[0][rows].cpu()
-    q = prob.q[0][:, rows].cpu()
+    q_idx = [x[rows].cpu() for x in prob.idx_q]
+    w = [x[rows].cpu() for x in prob.idx_w]
+    q = [x[:, rows].cpu() for x in prob.q]
     scale = float(np.float32(wl.dqk ** -0.5))
     geo = (so, po, sl, wl.stride)
     reps = 0
     t0 = time.perf_counter()
     while True:
-        sc = oracle.index_score(*geo, q_idx, w, kl)
-        idx, cnt = oracle.topk_select(*geo, wl.window, sc, wl.k)
-        oracle.attention(*geo, wl.window, q, K, None, idx, cnt, scale=scale, v_from_k=True,
+        sc = oracle.index_score(*geo, q_idx[0], w[0], kl)
+        if wl.block:  # Full: top-k + pool; Reindex over the pool
+            idx, cnt, pool, pc = oracle.topk_select(*geo, wl.window, sc, wl.k, block=wl.block,
+                                                    max_blocks=wl.max_blocks)
+            rs = oracle.index_score(*geo, q_idx[1], w[1], kl, cand=pool, cand_count=pc)
+            ridx, rcnt = oracle.topk_select(*geo, wl.window, rs, wl.k, cand=pool, cand_count=pc)
+            oracle.attention(*geo, wl.window, q[1], K, None, ridx, rcnt, scale=scale,
+                             v_from_k=True, dv=wl.dv)
+        else:
+            idx, cnt = oracle.topk_select(*geo, wl.window, sc, wl.k)
+        oracle.attention(*geo, wl.window, q[0], K, None, idx, cnt, scale=scale, v_from_k=True,
                          dv=wl.dv)
         reps += 1
         dt = time.perf_counter() - t0
@@ -437,14 +459,15 @@ def run_prefill(args, wl):
     work = prefill_work(wl, prob)
     kernels = {}
     for n, ms in fam_ms.items():
-        if n == "topk_select":
+        if n.startswith("topk_select"):
             kernels[n] = {"ms": round(ms, 4), "alg_bytes": int(work[n]),
                           "GB/s": round(work[n] / (ms * 1e-3) / 1e9, 1)}
         else:
             kernels[n] = {"ms": round(ms, 4), "alg_tflop": round(work[n] / 1e12, 3),
                           "TFLOP/s": round(work[n] / (ms * 1e-3) / 1e12, 1)}
-    dom = max(("index_score", "attn_gather_fwd"), key=lambda n: fam_ms[n])
-    dt = "fp8" if wl.idx_dtype == torch.float8_e4m3fn and dom == "index_score" else "bf16"
+    dom = max((n for n in fam_ms if not n.startswith("topk_select")), key=lambda n: fam_ms[n])
+    dt = ("fp8" if wl.idx_dtype == torch.float8_e4m3fn and dom.startswith("index_score")
+          else "bf16")
     achieved = work[dom] / (fam_ms[dom] * 1e-3) / 1e12
     R = prob.n_rows
     out = {
@@ -460,12 +483,14 @@ def run_prefill(args, wl):
         "vs_baseline": None,
         "dtype": "fp8 indexer, bf16 attention",
         "data": "synthetic",
-        "config": {"workload": "%s_prefill" % wl.name, "rows": R, "context": wl.seq_len,
+        "config": {"workload": wl.name if wl.name.endswith("_prefill") else "%s_prefill" % wl.name,
+                   "rows": R, "context": wl.seq_len,
                    "topk": wl.k, "indexer": "%dx%d %s" % (wl.idx_heads, wl.idx_dim,
                                                           str(wl.idx_dtype).replace("torch.", "")),
                    "q_heads": wl.hq, "latent": wl.dqk, "v_width": wl.dv,
                    "row_block": args.row_block, "causal_pairs": work["pairs"],
-                   "attention_pairs": work["attn_pairs"]},
+                   "attention_pairs": work["attn_pairs"], "stride": wl.stride,
+                   "pool": wl.max_blocks * wl.block if wl.block else None},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": MFMA_PEAK_TFLOPS[dt], "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_TFLOPS[dt], 4), "traffic": None,
@@ -473,6 +498,13 @@ def run_prefill(args, wl):
         "gpu_ms_per_step": round(gpu_ms, 3),
         "kernels": kernels,
     }
+    if wl.block:
+        # entries scored per query row by the group (Full + Reindex) against
+        # a full-domain indexer in both layers
+        flat, hier = layer_group_index_work(work["pairs"] / R, work["pool_pairs"] / R, 1, 1,
+                                            wl.n_reuse)
+        out["index_comparisons_per_query"] = {"hierarchical": round(hier, 1),
+                                              "flat": round(flat, 1)}
     if not args.no_cpu:
         out["cpu_baseline"] = prefill_cpu_baseline(prob, args.cpu_rows or 16, args.cpu_seconds)
     del step, prob, calls
@@ -627,7 +659,7 @@ def run_decode(args, wl, fa: bool = False):
 
 
 # Extra workloads measured by the default run, next to the headline decode.
-EXTRA = ("hysparse2_fa", "csa", "csa2", "hca", "dsa")
+EXTRA = ("hysparse2_fa", "csa", "csa2", "hca", "dsa", "csa2_prefill")
 
 
 def main():
@@ -636,8 +668,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
-                    help="hysparse2, hysparse2_fa, csa, csa2, hca, dsa, or all (the headline "
-                         "HySparse2 decode, with the other workloads as extra records)")
+                    help="hysparse2, hysparse2_fa, csa, csa2, hca, dsa, csa2_prefill, or all "
+                         "(the headline HySparse2 decode, with the other workloads as extra "
+                         "records)")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="decode rows for the oracle baseline (default: all rows of a step)")

@@ -182,28 +182,51 @@ class PrefillStep:
     ([row_block, n] f32) is the only materialised scores: per block, the
     indexer scores the causal history of each row, the selection keeps the
     top-k, and attention gathers it.  Indices, outputs and LSE cover all
-    rows; the score buffer is reused from block to block."""
+    rows; the score buffer is reused from block to block.
+
+    With a block pool (the hierarchical indexer, "CSA, HCA and CSA2",
+    sections 3.1-3.2), each row block runs the whole layer group: the Full
+    layer's scores give its own top-k and the block-max pool; the Reindex
+    layer rescores only the pool with its own query and selects its top-k
+    there; the Full query attends over the Full indices and the Reindex (and
+    any Reuse) queries over the Reindex indices.  The pool and the Reindex
+    scores exist for one row block at a time ([row_block, max_blocks*block]),
+    never for every prefill row (section 3.1: a pool materialised for all
+    131072 queries would take about 2 GiB)."""
 
     def __init__(self, prob, row_block: int = 8192, dense_route: bool = False):
         wl = prob.wl
-        assert wl.prefill and not wl.block, "prefill workloads without a block pool"
-        self.skip_k = wl.k if dense_route else 0
+        assert wl.prefill, "prefill workloads"
+        self.skip_k = wl.k if dense_route and not wl.block else 0
         self.prob = prob
         self.wl = wl
         dev = prob.seq_of_row.device
         R = prob.n_rows
         self.R = R
         self.row_block = row_block
+        rb = min(row_block, R)
+        i32, f32 = torch.int32, torch.float32
         self.kidx = _cache(prob.kidx, 1, wl.idx_dim)
         self.k = _cache(prob.k, wl.hkv, wl.dqk)
         self.v = _cache(prob.v, wl.hkv, wl.dv) if prob.v is not None else None
         self.S = wl.n_entries_cap
-        self.scores = torch.empty(min(row_block, R), self.S, dtype=torch.float32, device=dev)
-        self.idx = torch.empty(R, wl.k, dtype=torch.int32, device=dev)
-        self.count = torch.empty(R, dtype=torch.int32, device=dev)
+        self.scores = torch.empty(rb, self.S, dtype=f32, device=dev)
+        self.idx = torch.empty(R, wl.k, dtype=i32, device=dev)
+        self.count = torch.empty(R, dtype=i32, device=dev)
         q = prob.q[0]
         self.o = torch.empty(q.shape[0], R, wl.hq, wl.dv, dtype=q.dtype, device=dev)
-        self.lse = torch.empty(q.shape[0], R, wl.hq, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(q.shape[0], R, wl.hq, dtype=f32, device=dev)
+        self.pool = self.pool_count = None
+        if wl.block:
+            P = wl.max_blocks * wl.block
+            self.pool = torch.empty(rb, P, dtype=i32, device=dev)
+            self.pool_count = torch.empty(rb, dtype=i32, device=dev)
+            self.scores_r = torch.empty(rb, P, dtype=f32, device=dev)
+            self.idx_r = torch.empty(R, wl.k, dtype=i32, device=dev)
+            self.count_r = torch.empty(R, dtype=i32, device=dev)
+            q1 = prob.q[1]
+            self.o_r = torch.empty(q1.shape[0], R, wl.hq, wl.dv, dtype=q1.dtype, device=dev)
+            self.lse_r = torch.empty(q1.shape[0], R, wl.hq, dtype=f32, device=dev)
         self.scale = wl.dqk ** -0.5
         self._prepared = None
 
@@ -218,19 +241,40 @@ class PrefillStep:
         p, wl = self.prob, self.wl
         calls = []
         ws = None  # one selection workspace for every block (the calls never overlap)
+
+        def select(name, *a, **kw):
+            nonlocal ws
+            sel = prepare_topk_select(*a, workspace=ws, **kw)
+            ws = sel.ws if ws is None or (sel.ws is not None and sel.ws.numel() > ws.numel()) else ws
+            calls.append((name, sel))
+
         for lo, hi in self.blocks():
             rows = Rows(p.seq_of_row[lo:hi], p.pos_of_row[lo:hi], p.seq_len, wl.stride, wl.window)
-            sc = self.scores[: hi - lo]
+            n = hi - lo
+            sc = self.scores[:n]
             calls.append(("index_score", prepare_index_score(rows, p.idx_q[0][lo:hi],
                                                              p.idx_w[0][lo:hi], self.kidx, sc,
                                                              skip_k=self.skip_k)))
-            sel = prepare_topk_select(rows, sc, wl.k, self.idx[lo:hi], self.count[lo:hi],
-                                      workspace=ws)
-            ws = sel.ws if ws is None else ws
-            calls.append(("topk_select", sel))
+            if not wl.block:
+                select("topk_select", rows, sc, wl.k, self.idx[lo:hi], self.count[lo:hi])
+            else:
+                pool, pc = self.pool[:n], self.pool_count[:n]
+                select("topk_select", rows, sc, wl.k, self.idx[lo:hi], self.count[lo:hi],
+                       block=wl.block, max_blocks=wl.max_blocks, pool=pool, pool_count=pc)
+                scr = self.scores_r[:n]
+                calls.append(("index_score_reindex", prepare_index_score(
+                    rows, p.idx_q[1][lo:hi], p.idx_w[1][lo:hi], self.kidx, scr, cand=pool,
+                    cand_count=pc)))
+                select("topk_select_reindex", rows, scr, wl.k, self.idx_r[lo:hi],
+                       self.count_r[lo:hi], cand=pool, cand_count=pc)
             calls.append(("attn_gather_fwd", prepare_attn_gather_fwd(
                 rows, p.q[0][:, lo:hi], self.k, self.v, self.idx[lo:hi], self.count[lo:hi],
                 self.o[:, lo:hi], self.lse[:, lo:hi], self.scale, wl.dv)))
+            if wl.block:
+                calls.append(("attn_gather_fwd_1", prepare_attn_gather_fwd(
+                    rows, p.q[1][:, lo:hi], self.k, self.v, self.idx_r[lo:hi],
+                    self.count_r[lo:hi], self.o_r[:, lo:hi], self.lse_r[:, lo:hi], self.scale,
+                    wl.dv)))
         self._prepared = calls
         return calls
 

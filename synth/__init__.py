@@ -20,7 +20,9 @@ Workload shapes follow the five configurations the method is measured on:
 * ``csa``      -- CSA-style decode over entries compressed at stride 4;
 * ``csa2``     -- CSA2 hierarchical decode with an FP4 (E2M1 + E4M3/16) KV;
 * ``hca``      -- HCA decode: every entry compressed at stride 128, read
-  densely (no selector).
+  densely (no selector);
+* ``csa2_prefill`` -- the CSA2 layer group (Full + pool, Reindex) over every
+  token of a 131072-token prefill at stride 4.
 """
 from __future__ import annotations
 
@@ -198,7 +200,18 @@ HCA = Workload("hca", 5, n_seqs=16, seq_len=1048576, prefill=False, stride=128, 
                idx_heads=0, idx_dim=0, idx_dtype=torch.bfloat16, hq=64, hkv=1, dqk=512, dv=512,
                kv_mode="shared", attn_dtype=torch.bfloat16, n_qsets=1, page_size=0)
 
-WORKLOADS = {w.name: w for w in (TINY, HYSPARSE2, DSA, CSA, CSA2, HCA)}
+# CSA2's hierarchical indexer in prefill ("CSA, HCA and CSA2", section 3.1,
+# the layer-group cost breakdown: n = 131072 tokens at m = 4 give 32768
+# entries; the Full layer builds a 4096-entry pool, the Reindex layer keeps
+# 1024; section 2.2: prefill must not materialise an n x n_c score or pool).
+# Every token is a query row; the FP8 indexer runs as the row-block GEMM.
+CSA2_PREFILL = Workload("csa2_prefill", 6, n_seqs=1, seq_len=131072, prefill=True, stride=4,
+                        window=0, k=1024, idx_heads=32, idx_dim=128,
+                        idx_dtype=torch.float8_e4m3fn, hq=64, hkv=1, dqk=512, dv=512,
+                        kv_mode="shared", attn_dtype=torch.bfloat16, n_qsets=1, page_size=0,
+                        block=8, max_blocks=512, n_reuse=0)
+
+WORKLOADS = {w.name: w for w in (TINY, HYSPARSE2, DSA, CSA, CSA2, HCA, CSA2_PREFILL)}
 
 
 # ---------------------------------------------------------------------------
