@@ -26,8 +26,7 @@
 //   4. O^T += V^T . P^T with the contraction order permuted so that the
 //      lane's 8 probabilities are directly its B operand; the V^T operand
 //      comes straight from LDS through the gfx950 transpose read
-//      (ds_read_b64_tr_b16; the latent kernel below transposes 16-byte
-//      reads in registers with v_perm).  O^T keeps each lane on one query
+//      (ds_read_b64_tr_b16).  O^T keeps each lane on one query
 //      row, so the final normalisation needs no cross-lane traffic; row
 //      statistics are reduced with the gfx950 lane-swap instructions.
 // Long entry lists are split across workgroups; a combine kernel merges the
@@ -44,15 +43,6 @@ namespace {
 constexpr int kTile = 32;   // entries per tile
 
 enum { KV_SEPARATE = 0, KV_SHARED = 1, KV_FP4 = 2 };
-
-// Low (high) 16-bit halves of a and b packed as {a, b}: one v_perm_b32 each
-// (selector bytes 0-3 pick bytes of the second operand, 4-7 of the first).
-__device__ __forceinline__ uint32_t lo16x2(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
 
 // 2^x on the hardware exp unit (v_exp_f32): exact at 0, 0 at -inf; results
 // below 2^-126 flush to zero, which softmax weights can afford.
@@ -909,7 +899,7 @@ __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, in
   // second pass runs with m_run = m_top if some tile exceeds it by more than
   // kHeadroom.
   constexpr float kHeadroom = 64.0f;
-  f32x4 O[RT][8];  // [row tile][channel tile j]: channels 128 w + 8 (4 gq + i) + j
+  f32x4 O[RT][8];  // [row tile][M-tile t]: lane element i is channel 128 w + 32 gq + 4 t + i
   float m_run = -__builtin_huge_valf(), m_top = -__builtin_huge_valf();
   float l_run = 0.0f, l_lse = 0.0f;
 
@@ -985,25 +975,22 @@ __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, in
     bf16x8 pb[RT];
 #pragma unroll
     for (int q = 0; q < RT; ++q) pb[q] = __builtin_bit_cast(bf16x8, lds.p[q][lane]);
-    // V^T as the A operand for channels 128 w + 8 col + j of the 8 entries of
-    // each lane's k-slots (an 8x8 bf16 transpose in registers)
-    u32x4 R[8];
+    // V^T as the A operand straight from LDS through the gfx950 transpose
+    // read, with attn_mfma's lane layout: M-tile t row m is channel
+    // 128 w + 32 (m / 4) + 4 t + m % 4, so accumulator O[q][t][i] of lane
+    // (col, gq) holds channel 128 w + 32 gq + 4 t + i of query row col, and
+    // the k-slots of each lane are the entries P^T's packing gives them.
+    const uint16_t* vr0 = kb + (4 * gq + ((lane >> 2) & 3)) * L::KROW + 32 * (lane & 3) + wave * 128;
+    const uint16_t* vr1 = vr0 + 16 * L::KROW;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = i < 4 ? 4 * gq + i : 16 + 4 * gq + (i - 4);
-      R[i] = *reinterpret_cast<const u32x4*>(kb + e * L::KROW + wave * 128 + col * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x4 b;
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd)
-        b[qd] = (j & 1) ? hi16x2(R[2 * qd][j >> 1], R[2 * qd + 1][j >> 1])
-                        : lo16x2(R[2 * qd][j >> 1], R[2 * qd + 1][j >> 1]);
+    for (int t = 0; t < 8; ++t) {
+      const s16x4 lo = lds_read_tr16(vr0 + 4 * t);
+      const s16x4 hi = lds_read_tr16(vr1 + 4 * t);
+      const s16x8 b = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int q = 0; q < RT; ++q)
-        O[q][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), pb[q],
-                                                          O[q][j], 0, 0, 0);
+        O[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), pb[q],
+                                                          O[q][t], 0, 0, 0);
     }
   };
 
@@ -1060,11 +1047,10 @@ __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, in
       float lse;
       const float inv = finish_row(m_r, l_r, lx, sink_log2(a, set, h), lse);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c0 = wave * 128 + 32 * gq + 8 * i;
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = o[j][i] * inv;
+      for (int hh2 = 0; hh2 < 4; ++hh2) {
+        const int c0 = wave * 128 + 32 * gq + 8 * hh2;
+        const f32x4 v0 = o[2 * hh2] * inv, v1 = o[2 * hh2 + 1] * inv;
+        float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         apply_gate(a, orow * DV + c0, v);
         store8(a, orow * DV + c0, v);
       }
@@ -1073,10 +1059,10 @@ __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, in
       const int64_t nrows = (int64_t)a.n_qsets * R_ * a.hq;
       float* po = a.part + ((int64_t)sp * nrows + orow) * DV;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float* op = po + wave * 128 + 32 * gq + 8 * i;
-        reinterpret_cast<f32x4*>(op)[0] = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
-        reinterpret_cast<f32x4*>(op)[1] = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
+      for (int hh2 = 0; hh2 < 4; ++hh2) {
+        float* op = po + wave * 128 + 32 * gq + 8 * hh2;
+        reinterpret_cast<f32x4*>(op)[0] = o[2 * hh2];
+        reinterpret_cast<f32x4*>(op)[1] = o[2 * hh2 + 1];
       }
       if (wave == 0 && gq == 0) {
         float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 3;
