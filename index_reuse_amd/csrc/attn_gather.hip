@@ -799,7 +799,7 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
 // (Two row tiles per workgroup with one K buffer, two workgroups per CU, ran
 // 15% slower: each K fragment then feeds one MFMA, with four barriers per
 // tile.)
-constexpr int kMlaDqk = 576, kMlaDv = 512, kMlaRT = 4, kMlaD = 2;
+constexpr int kMlaDqk = 576, kMlaDv = 512, kMlaRT = 4, kMlaD = 1;
 
 struct MlaLds {
   static constexpr int RT = kMlaRT, D = kMlaD;
@@ -994,31 +994,25 @@ __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, in
     }
   };
 
-  T ring[D];
+  // One register stage: tile s + 1 loads while tile s is computed from LDS
+  // buffer s & 1 (its last readers, tile s - 2, all passed the barrier of
+  // tile s - 1).  One loop body keeps every O accumulator in a fixed register
+  // (an unrolled pair of bodies made the compiler rotate them between AGPRs).
+  static_assert(D == 1, "one register stage");
+  T ring;
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int q = 0; q < RT; ++q)
 #pragma unroll
       for (int j = 0; j < 8; ++j) O[q][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < D; ++u) load_step(u, ring[u]);
-    int s0 = 0;
-    for (; s0 + D <= nsteps_run; s0 += D) {
-#pragma unroll
-      for (int u = 0; u < D; ++u) {
-        store_step(ring[u], u);  // D = 2: buffer u
-        __syncthreads();
-        load_step(s0 + u + D, ring[u]);
-        compute(u, s0 + u);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-      if (s0 + u < nsteps_run) {
-        store_step(ring[u], u);
-        __syncthreads();
-        compute(u, s0 + u);
-      }
+    load_step(0, ring);
+#pragma unroll 1
+    for (int s = 0; s < nsteps_run; ++s) {
+      const int sb = s & 1;
+      store_step(ring, sb);
+      __syncthreads();
+      load_step(s + 1, ring);  // past the last tile: the table's padding step
+      compute(sb, s);
     }
     if (!__syncthreads_or(m_top > m_run + kHeadroom)) break;
     m_run = m_top;
