@@ -635,26 +635,23 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
 #pragma unroll
     for (int u = 0; u < D; ++u)
       if (u > 0 || pass > 0 || !early) load_step(u, ring[u]);
-    int s0 = 0;
-    for (; s0 + D <= nsteps_run; s0 += D) {
+    // One unrolled group of D steps per iteration, the last group guarded
+    // step by step (a uniform branch): the tile code appears D times, not 2D
+    // (a workgroup with few tiles runs each instruction about once, so code
+    // size is instruction-fetch time).  Loads past the last step read the
+    // table's D padding steps.
+    for (int s0 = 0; s0 < nsteps_run; s0 += D) {
 #pragma unroll
       for (int u = 0; u < D; ++u) {
-        const int sb = D % 2 == 0 ? (u & 1) : ((s0 + u) & 1);
-        store_step(ring[u], sb);
-        // the next loads go out before the barrier: the stores above have
-        // read these registers, and the slot table does not change
-        load_step(s0 + u + D, ring[u]);
-        __syncthreads();
-        if (active) compute(sb * NG + grp, (s0 + u) * NG + grp);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-      if (s0 + u < nsteps_run) {
-        const int sb = (s0 + u) & 1;
-        store_step(ring[u], sb);
-        __syncthreads();
-        if (active) compute(sb * NG + grp, (s0 + u) * NG + grp);
+        if (s0 + u < nsteps_run) {
+          const int sb = D % 2 == 0 ? (u & 1) : ((s0 + u) & 1);
+          store_step(ring[u], sb);
+          // the next loads go out before the barrier: the stores above have
+          // read these registers, and the slot table does not change
+          load_step(s0 + u + D, ring[u]);
+          __syncthreads();
+          if (active) compute(sb * NG + grp, (s0 + u) * NG + grp);
+        }
       }
     }
     // Every wave of the workgroup takes the same decision (the loop holds
@@ -799,11 +796,12 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
 // (Two row tiles per workgroup with one K buffer, two workgroups per CU, ran
 // 15% slower: each K fragment then feeds one MFMA, with four barriers per
 // tile.)
-constexpr int kMlaDqk = 576, kMlaDv = 512, kMlaRT = 4, kMlaD = 1;
+constexpr int kMlaDv = 512, kMlaRT = 4, kMlaD = 1;
 
+template <int DQK>
 struct MlaLds {
   static constexpr int RT = kMlaRT, D = kMlaD;
-  static constexpr int KROW = kMlaDqk + 8;  // bf16 per LDS row (padded)
+  static constexpr int KROW = DQK + 8;  // bf16 per LDS row (padded)
   static constexpr int SLOTS = kMaxEntries + (D + 1) * kTile;
   uint16_t k[2][kTile * KROW];
   float sx[4][8][64];      // S partials handed to the other dim half
@@ -825,12 +823,16 @@ __device__ __forceinline__ void mla_unit(int n_units, int Z, int& unit, int& z) 
   if (unit >= n_units) unit = -1;
 }
 
+// DQK = 576 (latent rows, V = the first 512 channels) or 512 (one row as K
+// and V); KV = KV_SHARED (bf16 rows) or KV_FP4 (E2M1 codes with E4M3 scales,
+// decoded exactly to bf16 on the way into LDS).
+template <int DQK, int KV>
 __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, int n_units, int Z) {
-  constexpr int NTH = 256, DQK = kMlaDqk, DV = kMlaDv, RT = kMlaRT, D = kMlaD;
+  constexpr int NTH = 256, DV = kMlaDv, RT = kMlaRT, D = kMlaD;
   constexpr int KH = DQK / 64;      // k-steps per dim half
   constexpr int HT = 2;             // row tiles in this wave's S
-  using L = MlaLds;
-  using T = TileRegs<DQK, DV, KV_SHARED, NTH, 1>;
+  using L = MlaLds<DQK>;
+  using T = TileRegs<DQK, DV, KV, NTH, 1>;
   static_assert(sizeof(L) <= 160 * 1024, "LDS budget");
   __shared__ __align__(16) L lds;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -881,8 +883,15 @@ __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, in
       const int e = c / T::CPR_K, part = c % T::CPR_K;
       const int sv = lds.slot[s * kTile + e];
       const uint32_t slot = sv >= 0 ? (uint32_t)sv : dummy;
-      regs.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-          a.k.data + (uint64_t)slot * (uint32_t)a.k.row_stride + g * (DQK * 2) + part * 16));
+      if constexpr (T::FP4) {
+        regs.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            a.k.data + (uint64_t)slot * (uint32_t)a.k.row_stride + g * (DQK / 2) + part * 16));
+        regs.sc[u] = *reinterpret_cast<const uint16_t*>(
+            a.k.scale + (uint64_t)slot * (uint32_t)a.k.scale_stride + g * (DQK / 16) + part * 2);
+      } else {
+        regs.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            a.k.data + (uint64_t)slot * (uint32_t)a.k.row_stride + g * (DQK * 2) + part * 16));
+      }
     }
   };
   auto store_step = [&](const T& regs, int sb) {
@@ -890,7 +899,17 @@ __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, in
     for (int u = 0; u < T::U; ++u) {
       const int c = tid + NTH * u;
       const int e = c / T::CPR_K, part = c % T::CPR_K;
-      *reinterpret_cast<u32x4*>(&lds.k[sb][e * L::KROW + part * 8]) = regs.v[u];
+      if constexpr (T::FP4) {
+        // 16 code bytes = 32 channels, decoded exactly to bf16
+        uint32_t vals[16];
+        fp4_dequant32(regs.v[u], regs.sc[u] & 0xFFu, regs.sc[u] >> 8, vals);
+        u32x4* dst = reinterpret_cast<u32x4*>(&lds.k[sb][e * L::KROW + part * 32]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[i] = u32x4{vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]};
+      } else {
+        *reinterpret_cast<u32x4*>(&lds.k[sb][e * L::KROW + part * 8]) = regs.v[u];
+      }
     }
   };
 
@@ -1266,13 +1285,15 @@ hipError_t launch_mfma_attn(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DQK, int KV>
 hipError_t launch_mla(const AttnArgs& a, hipStream_t s) {
   const int G = a.hq / a.hkv;
   const int groups = (a.n_qsets * G + 16 * kMlaRT - 1) / (16 * kMlaRT);
   const int per = ((a.max_entries + a.n_split - 1) / a.n_split + kTile - 1) / kTile * kTile;
   const int n_units = a.n_split * a.rows.n_rows * a.hkv;
   const int64_t nwg = (int64_t)(n_units + 7) / 8 * 8 * groups;
-  hipLaunchKernelGGL(attn_mla, dim3((unsigned)nwg), dim3(256), 0, s, a, per, n_units, groups);
+  hipLaunchKernelGGL((attn_mla<DQK, KV>), dim3((unsigned)nwg), dim3(256), 0, s, a, per, n_units,
+                     groups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const int64_t nrows = (int64_t)a.n_qsets * a.rows.n_rows * a.hq;
@@ -1331,19 +1352,28 @@ hipError_t launch_attn_gather(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(attn_f32, grid, dim3(256), 0, s, a);
     return hipGetLastError();
   }
+  // Rows of 512 or more channels with at least 64 query rows per KV head:
+  // the kernel that splits S by channel halves and O by channel quarters
+  // across its waves, so each K fragment read from LDS feeds two MFMAs.
+  const bool many_rows = a.n_qsets * (a.hq / a.hkv) >= 16 * kMlaRT;
   if (a.kv_kind == KV_SEPARATE) {
     if (a.dqk == 128 && a.dv == 128) return launch_shaped<128, 128, KV_SEPARATE, 2>(a, s);
     if (a.dqk == 256 && a.dv == 256) return launch_shaped<256, 256, KV_SEPARATE, 2>(a, s);
   } else if (a.kv_kind == KV_SHARED) {
     if (a.dqk == 576 && a.dv == 512) {
-      // latent rows with at least 64 query rows per KV head: split S / O
-      if (a.n_qsets * (a.hq / a.hkv) >= 16 * kMlaRT) return launch_mla(a, s);
+      if (many_rows) return launch_mla<576, KV_SHARED>(a, s);
       return launch_shaped<576, 512, KV_SHARED, 2>(a, s);
     }
-    if (a.dqk == 512 && a.dv == 512) return launch_shaped<512, 512, KV_SHARED, 2>(a, s);
+    if (a.dqk == 512 && a.dv == 512) {
+      if (many_rows) return launch_mla<512, KV_SHARED>(a, s);
+      return launch_shaped<512, 512, KV_SHARED, 2>(a, s);
+    }
     if (a.dqk == 128 && a.dv == 128) return launch_shaped<128, 128, KV_SHARED, 2>(a, s);
   } else if (a.kv_kind == KV_FP4) {
-    if (a.dqk == 512 && a.dv == 512) return launch_shaped<512, 512, KV_FP4, 4>(a, s);
+    if (a.dqk == 512 && a.dv == 512) {
+      if (many_rows) return launch_mla<512, KV_FP4>(a, s);
+      return launch_shaped<512, 512, KV_FP4, 4>(a, s);
+    }
   }
   return hipErrorInvalidValue;
 }
