@@ -319,26 +319,63 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_mfma(IndexArgs a, int
 
 // ----------------------------------------------------------------- prefill
 // Many query rows of one sequence (prefill) make the score a GEMM: M = (query
-// row, head), N = cache entries, K = dim.  A workgroup holds kPRowsW rows per
-// wave (their FP8 query rows as the A operand of v_mfma_scale 16x16x128,
-// heads on M, the whole 128-wide contraction in one instruction) and streams
-// 64-entry chunks of the sequence's keys through LDS, shared by every row of
-// the workgroup.  Blocks run heaviest (latest rows) first; a block whose rows
-// span several sequences makes one pass per sequence.
+// row, head), N = cache entries, K = dim.  A workgroup holds one row per wave
+// (its FP8 query as the A operand of v_mfma_scale 16x16x128, heads on M, the
+// whole 128-wide contraction in one instruction) and streams 64-entry chunks
+// of the sequence's keys through LDS, shared by every row of the workgroup.
+// Blocks run heaviest (latest rows) first; a block whose rows span several
+// sequences makes one pass per sequence.
+//
+// The epilogue is where the time goes: every (head, entry) product needs a
+// ReLU and a weighted add on the VALU while the matrix pipe does 128 MACs.
+// With ReLU(x) = (x + |x|) / 2,
+//   sum_h w_h ReLU(s_h) = 1/2 sum_h w_h |s_h| + 1/2 (sum_h w_h q_h) . k,
+// and the first half is one fma per product (|x| is a free source
+// modifier).  The second half is linear in the key, so the MFMA takes it:
+// q' = sum_h w_h q_h (fp32, per row) is split into kLimbs FP8 rows
+// q' = sum_j 2^e(j,b) c_j (each limb takes the next ~4 significant bits of
+// what the previous ones left, with one E8M0 scale per limb and 32-channel
+// block b), which fill rows 4i and 4i+1 of one more 16-row A tile.  Its
+// accumulator rows sum to q'.k / 2 (the 1/2 rides in the scales), so each
+// lane starts its fma chain with its two limb rows and the transposed
+// reduction does the rest.  On integer
+// inputs q' is an exact integer, every limb decodes to integers and every
+// partial sum stays below 2^24, so the scores are exact.
 constexpr int kPWaves = 8;
-constexpr int kPRowsW = 1;                  // rows per wave
-constexpr int kPRows = kPWaves * kPRowsW;   // rows per workgroup
+constexpr int kPRows = kPWaves;             // rows per workgroup, one per wave
 constexpr int kPChunk = 64;                 // entries per LDS chunk
+constexpr int kPPT = kPChunk * 8 / (64 * kPWaves);  // 16-byte pieces per thread per chunk
 constexpr int kPTiles = kPChunk / 16;       // 16-entry MFMA tiles per chunk
-constexpr int kPRowB = 128 + 16;            // LDS bytes per entry (padded)
+constexpr int kPRowB = 128;                 // LDS bytes per entry
+// LDS swizzle: 16-byte piece j of entry e sits in slot j ^ ((e >> 1) & 7) of
+// its row, so 16 lanes reading one piece of 16 consecutive entries, or
+// writing two whole entries, touch 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int kslot(int e, int j) { return 16 * (j ^ ((e >> 1) & 7)); }
+constexpr int kLimbs = 8;                   // FP8 limbs of q' (about 32 bits), two per lane group
+constexpr int kPMaxSub = 1024;              // 64-entry pieces per pass with a block table
+// Word 3 of a raw buffer resource on CDNA (32-bit dword accesses,
+// range-checked against the resource's byte size: stores past it are
+// dropped).
+constexpr int kOutWord3 = 0x00020000;
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+struct Pre {
+  u32x4 v[kPPT];
+};
 
-template <int NMT>
+__device__ __forceinline__ i32x8 cat8(u32x4 x0, u32x4 x1) {
+  return i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+               (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+}
+
+template <int NMT, bool TABLE>
 __global__ __launch_bounds__(64 * kPWaves) void index_score_prefill(IndexArgs a, int n_blocks) {
   __shared__ __align__(16) char kb[2][kPChunk * kPRowB];
+  __shared__ __align__(16) uint8_t limb[kPWaves][16 * 128];  // [wave][limb row][channel]
+  __shared__ uint8_t limb_scale[kPWaves][16 * 4];            // [wave][limb row][block]
   __shared__ int sb[kPRows], sn[kPRows], sz[kPRows];
-  __shared__ int wred[kPWaves][2];
+  __shared__ int cpage[TABLE ? kPMaxSub : 1];  // page of each 64-entry piece of the pass
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
   const int r0 = (n_blocks - 1 - (int)blockIdx.x) * kPRows;
@@ -364,35 +401,87 @@ __global__ __launch_bounds__(64 * kPWaves) void index_score_prefill(IndexArgs a,
     for (int i = tid; i < sz[j]; i += 64 * kPWaves)
       a.scores[(int64_t)(r0 + j) * a.score_stride + i] = 0.0f;
 
-  // this wave's rows: A operands (head mt*16 + col, bytes [32g, 32g+32)) and
-  // head weights in the accumulator layout (head mt*16 + 4g + i)
-  i32x8 qa[kPRowsW][NMT];
-  float wv[kPRowsW][NMT][4];
-  int rb[kPRowsW], rn[kPRowsW];
+  // This wave's row: A operands (head mt*16 + col, bytes [32g, 32g+32)) and
+  // half the head weights in the accumulator layout (head mt*16 + 4g + i).
+  const int r = __builtin_amdgcn_readfirstlane(r0 + wave);
+  const int rb = __builtin_amdgcn_readfirstlane(sb[wave]);
+  const int rn = __builtin_amdgcn_readfirstlane(sn[wave]);
+  i32x8 qa[NMT];
+  float wh[NMT][4];
 #pragma unroll
-  for (int j = 0; j < kPRowsW; ++j) {
-    const int lr = wave * kPRowsW + j, r = r0 + lr;
-    rb[j] = sb[lr];
-    rn[j] = sn[lr];
+  for (int mt = 0; mt < NMT; ++mt) {
+    const int h = mt * 16 + col;
+    if (rb >= 0 && h < a.n_heads) {
+      const u32x4* qp = reinterpret_cast<const u32x4*>(
+          reinterpret_cast<const char*>(a.q) + ((int64_t)r * a.n_heads + h) * 128 + 32 * g);
+      qa[mt] = cat8(qp[0], qp[1]);
+    } else {
+      qa[mt] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-      const int h = mt * 16 + col;
-      if (rb[j] >= 0 && h < a.n_heads) {
-        const u32x4* qp = reinterpret_cast<const u32x4*>(
-            reinterpret_cast<const char*>(a.q) + ((int64_t)r * a.n_heads + h) * 128 + 32 * g);
-        const u32x4 x0 = qp[0], x1 = qp[1];
-        qa[j][mt] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                          (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-      } else {
-        qa[j][mt] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hw = mt * 16 + 4 * g + i;
-        wv[j][mt][i] = (rb[j] >= 0 && hw < a.n_heads) ? a.w[(int64_t)r * a.n_heads + hw] : 0.0f;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int hw = mt * 16 + 4 * g + i;
+      wh[mt][i] = (rb >= 0 && hw < a.n_heads) ? 0.5f * a.w[(int64_t)r * a.n_heads + hw] : 0.0f;
     }
   }
+
+  // q' = sum_h w_h q_h; lane l owns channels 2l and 2l + 1.
+  float x0 = 0.f, x1 = 0.f;
+  if (rb >= 0) {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(
+                             reinterpret_cast<const char*>(a.q) + (int64_t)r * a.n_heads * 128) + lane;
+    const float* wr = a.w + (int64_t)r * a.n_heads;
+#pragma unroll 8
+    for (int h = 0; h < a.n_heads; ++h) {
+      const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)qp[64 * h], false);
+      const float w = wr[h];
+      x0 = fmaf(w, f.x, x0);
+      x1 = fmaf(w, f.y, x1);
+    }
+  }
+  // Limbs: each takes what the previous ones left, rounded to FP8 under a
+  // power-of-two scale set by the largest remainder of its scale block.  A
+  // limb that decodes to d leaves x - d exactly, so the limbs sum to q' up
+  // to the last remainder.
+  //
+  // Scale blocks follow the matrix unit's K order, not the channel order: in
+  // a 16x16x128 operand, bytes [0, 16) of lane group g are K [16g, 16g+16)
+  // and bytes [16, 32) are K [64+16g, +16), and lane group b's scales cover
+  // K [32b, 32b+32).  With lane group g holding channels [32g, 32g+32),
+  // block 2h+p is channels {c : (c >> 4) & 1 == h, c >> 6 == p}: for
+  // channels 2l and 2l+1, h is bit 3 of l and p is bit 5, and the 16 lanes
+  // of a block differ in bits 0, 1, 2 and 4.
+  const int blk = 2 * ((lane >> 3) & 1) + (lane >> 5);
+  static_assert(kLimbs == 8, "rows 4i and 4i+1 of the tile");
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {  // tile row j: limb 2 (j / 4) + j % 4 if j % 4 < 2
+    uint32_t two = 0;
+    int sc = 127;
+    if (j % 4 < 2) {
+      float m = fmaxf(fabsf(x0), fabsf(x1));
+      m = fmaxf(m, __shfl_xor(m, 1));
+      m = fmaxf(m, __shfl_xor(m, 2));
+      m = fmaxf(m, __shfl_xor(m, 4));
+      m = fmaxf(m, __shfl_xor(m, 16));
+      if (m > 0.f) {
+        // m < 2^E, so |x| * 2^-(E-8) < 256, inside FP8's range
+        const int e = min(max(__builtin_amdgcn_frexp_expf(m) - 8, -126), 127);
+        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(x0, -e),
+                                                       __builtin_amdgcn_ldexpf(x1, -e), 0, false);
+        const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false);
+        x0 -= __builtin_amdgcn_ldexpf(d.x, e);
+        x1 -= __builtin_amdgcn_ldexpf(d.y, e);
+        two = (uint32_t)pk & 0xFFFFu;
+        sc = 126 + e;  // 2^(e-1): the 1/2 of the linear half
+      }
+    }
+    *reinterpret_cast<uint16_t*>(&limb[wave][j * 128 + 2 * lane]) = (uint16_t)two;
+    if ((lane & 0x17) == 0) limb_scale[wave][j * 4 + blk] = (uint8_t)sc;
+  }
+  __syncthreads();
+  const i32x8 la = cat8(*reinterpret_cast<const u32x4*>(&limb[wave][col * 128 + 32 * g]),
+                        *reinterpret_cast<const u32x4*>(&limb[wave][col * 128 + 32 * g + 16]));
+  const int lsc = limb_scale[wave][col * 4 + g];  // lane (col, g): limb col, block g
 
   // one pass per distinct sequence of the block, in increasing order
   int bprev = -1;
@@ -403,72 +492,91 @@ __global__ __launch_bounds__(64 * kPWaves) void index_score_prefill(IndexArgs a,
     if (bs == 0x7FFFFFFF) break;
     for (int i = 0; i < kPRows; ++i)
       if (sb[i] == bs) nmax = max(nmax, sn[i]);
+    bs = __builtin_amdgcn_readfirstlane(bs);
+    nmax = __builtin_amdgcn_readfirstlane(nmax);
     bprev = bs;
     if (nmax == 0) continue;
+    // every wave is done with the previous pass's LDS (chunks, pages)
+    __syncthreads();
+    // With a block table, each chunk's page is read here once per pass and
+    // kept in LDS: a table read inside the loop would be a vector load whose
+    // wait also waits for the chunk loads in flight before it.
+    const int nsub = (nmax + 63) / 64;  // 64-entry pieces: <= kPMaxSub (host check)
+    if (TABLE) {
+      for (int ci = tid; ci < min(nsub, kPMaxSub); ci += 64 * kPWaves)
+        cpage[ci] = a.k.block_table[(int64_t)bs * a.k.max_pages + ((ci * 64) >> a.k.page_shift)];
+      __syncthreads();
+    }
 
-    // chunk loads: piece p = tid + i*blockDim is entry p/8 of the chunk,
-    // 16 bytes at 16 (p%8)
-    constexpr int PPT = kPChunk * 8 / (64 * kPWaves);
-    static_assert(PPT * 64 * kPWaves == kPChunk * 8, "whole 16-byte pieces per thread");
-    u32x4 pre[PPT];
-    auto load_chunk = [&](int c0) {
+    // chunk loads: thread tid fetches 16 bytes at 16 (tid % 8) of entries
+    // tid / 8 + 64 i of the chunk (clamped to the last visible entry).  Each
+    // 64-entry piece starts at a multiple of 64 and lies in one page (the
+    // host sends a block table here only with pages of at least 64 entries),
+    // so its first row comes from scalar arithmetic and each thread adds its
+    // own offset.
+    const int pe = tid >> 3, pb = 16 * (tid & 7);
+    const int rs = (int)a.k.row_stride;  // at most 2^24 (host check)
+    // Every chunk issues the same loads and stores, so the compiler's wait
+    // counts stay exact across iterations: loads past the last chunk re-read
+    // it, and the score stores are range-checked buffer stores (lanes past
+    // the row, or every lane when the row is not in this pass, are dropped
+    // by the hardware).
+    const int last = (nmax - 1) & ~63;  // first entry of the last 64-entry piece
+    auto load_chunk = [&](int c, Pre& pre) {
 #pragma unroll
-      for (int i = 0; i < PPT; ++i) {
-        const int pc = tid + i * 64 * kPWaves;
-        const int e = min(c0 + (pc >> 3), nmax - 1);
-        pre[i] = *reinterpret_cast<const u32x4*>(cache_row(a.k, bs, e) + 16 * (pc & 7));
+      for (int i = 0; i < kPPT; ++i) {
+        // piece i: 64 entries from sub (in one page), clamped to the row
+        const int sub = min(c + 64 * i, last);
+        int64_t slot;
+        if (TABLE) {
+          const int pg = __builtin_amdgcn_readfirstlane(cpage[min(sub / 64, kPMaxSub - 1)]);
+          slot = ((int64_t)pg << a.k.page_shift) + (sub & (a.k.page_size - 1));
+        } else {
+          slot = (int64_t)bs * a.k.max_pages * a.k.page_size + sub;
+        }
+        const uint32_t off = (uint32_t)(__mul24(min(pe, nmax - 1 - sub), rs) + pb);
+        pre.v[i] = *reinterpret_cast<const u32x4*>(a.k.data + slot * a.k.row_stride + off);
       }
     };
-    load_chunk(0);
-    int buf = 0;
-    for (int c0 = 0; c0 < nmax; c0 += kPChunk) {
+    const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+        a.scores + (int64_t)r * a.score_stride, (short)0, rb == bs ? 4 * rn : 0, kOutWord3);
+    // One chunk: store its prefetched pieces, then (after the barrier) start
+    // the loads of the chunk two ahead into the same registers, and score.
+    auto chunk = [&](int c0, int buf, Pre& pre) {
 #pragma unroll
-      for (int i = 0; i < PPT; ++i) {
-        const int pc = tid + i * 64 * kPWaves;
-        *reinterpret_cast<u32x4*>(&kb[buf][(pc >> 3) * kPRowB + 16 * (pc & 7)]) = pre[i];
-      }
+      for (int i = 0; i < kPPT; ++i)
+        *reinterpret_cast<u32x4*>(&kb[buf][(pe + 64 * i) * kPRowB + kslot(pe, tid & 7)]) = pre.v[i];
       __syncthreads();
-      if (c0 + kPChunk < nmax) load_chunk(c0 + kPChunk);
+      load_chunk(c0 + 2 * kPChunk, pre);
       // Tile t+1's MFMAs are issued before tile t's epilogue, so the matrix
-      // pipe works while the VALU applies ReLU and the head weights.
-      float res[kPRowsW][4];  // lane partial of each of the last 4 tiles
-      f32x4 acc[2][kPRowsW][NMT];
-      auto issue = [&](int t, f32x4 (&A)[kPRowsW][NMT]) {
-        const char* kr = &kb[buf][(16 * t + col) * kPRowB + 32 * g];
-        const u32x4 y0 = *reinterpret_cast<const u32x4*>(kr);
-        const u32x4 y1 = *reinterpret_cast<const u32x4*>(kr + 16);
-        const i32x8 kbv = {(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3],
-                           (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
+      // pipe works while the VALU finishes the scores.
+      float res[4];  // lane partial of each of the last 4 tiles
+      f32x4 acc[2][NMT + 1];
+      auto issue = [&](int t, f32x4 (&A)[NMT + 1]) {
+        const char* kr = &kb[buf][(16 * t + col) * kPRowB];
+        const i32x8 kbv = cat8(*reinterpret_cast<const u32x4*>(kr + kslot(col, 2 * g)),
+                               *reinterpret_cast<const u32x4*>(kr + kslot(col, 2 * g + 1)));
 #pragma unroll
-        for (int j = 0; j < kPRowsW; ++j)
-#pragma unroll
-          for (int mt = 0; mt < NMT; ++mt)
-            A[j][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                qa[j][mt], kbv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+        for (int mt = 0; mt < NMT; ++mt)
+          A[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              qa[mt], kbv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+        A[NMT] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(la, kbv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                 lsc, 0, 0x7F7F7F7F);
       };
-      auto epilogue = [&](int t, const f32x4 (&A)[kPRowsW][NMT]) {
+      auto epilogue = [&](int t, const f32x4 (&A)[NMT + 1]) {
+        // the lane's two limb rows start one fma chain; the tiles in flight
+        // and the waves sharing the SIMD cover its latency
+        float part = A[NMT][0] + A[NMT][1];
 #pragma unroll
-        for (int j = 0; j < kPRowsW; ++j) {
-          // one fma chain: the tiles in flight and the waves sharing the
-          // SIMD cover its latency, and no adds are needed to join chains
-          float part = 0.f;
+        for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-          for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) part = fmaf(wv[j][mt][i], relu(A[j][mt][i]), part);
-          res[j][t & 3] = part;
-        }
-        // After every 4 tiles, one transposed reduction over the four lane
-        // groups leaves lane l with entry l of those 64 (tile l/16, column
-        // l%16).
+          for (int i = 0; i < 4; ++i) part = fmaf(wh[mt][i], fabsf(A[mt][i]), part);
+        res[t & 3] = part;
         if ((t & 3) == 3) {
-#pragma unroll
-          for (int j = 0; j < kPRowsW; ++j) {
-            const float mine = sum4_transposed(res[j][0], res[j][1], res[j][2], res[j][3]);
-            const int e = c0 + 16 * (t - 3) + lane;
-            if (rb[j] == bs && e < rn[j])
-              a.scores[(int64_t)(r0 + wave * kPRowsW + j) * a.score_stride + e] = mine;
-          }
+          // one transposed reduction over the four lane groups leaves lane
+          // l with entry 16 (t - 3) + l of the chunk (tile l/16, column l%16)
+          const float mine = sum4_transposed(res[0], res[1], res[2], res[3]);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mine), out, 4 * (c0 + 16 * (t - 3) + lane), 0, 0);
         }
       };
       static_assert(kPTiles % 4 == 0, "whole 64-entry store groups per chunk");
@@ -480,11 +588,27 @@ __global__ __launch_bounds__(64 * kPWaves) void index_score_prefill(IndexArgs a,
         if (t + 2 < kPTiles) issue(t + 2, acc[0]);
         epilogue(t + 1, acc[1]);
       }
-      // No barrier here: the next chunk is stored into the other buffer,
-      // whose last readers (the previous chunk) all passed this chunk's
-      // barrier.
-      buf ^= 1;
+    };
+    // Two chunks per iteration keep the prefetch registers static.  Chunk c
+    // uses LDS buffer c % 2; it is stored again (chunk c + 2) only after the
+    // barrier of chunk c + 1, which every wave reaches after scoring chunk c.
+    // Stores that the hardware drops (a zero-size range) give the first
+    // iteration the loop's own order of loads and stores, so the waits
+    // before each LDS store can leave the other chunk's loads in flight.
+    const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(a.scores, (short)0, 0, kOutWord3);
+    Pre pre0, pre1;
+    load_chunk(0, pre0);
+#pragma unroll
+    for (int i = 0; i < kPTiles / 4; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 4 * i, 0, 0);
+    load_chunk(kPChunk, pre1);
+#pragma unroll
+    for (int i = 0; i < kPTiles / 4; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 64 + 4 * i, 0, 0);
+    int c0 = 0;
+    for (; c0 + kPChunk < nmax; c0 += 2 * kPChunk) {
+      chunk(c0, 0, pre0);
+      chunk(c0 + kPChunk, 1, pre1);
     }
+    if (c0 < nmax) chunk(c0, 0, pre0);
   }
 }
 
@@ -517,6 +641,20 @@ __global__ __launch_bounds__(256) void index_score_f32(IndexArgs a) {
     }
   }
   a.scores[(int64_t)r * a.score_stride + slot] = s;
+}
+
+template <bool TABLE>
+hipError_t launch_prefill(const IndexArgs& a, int nmt, int n_blocks, hipStream_t s) {
+  const dim3 grid(n_blocks), block(64 * kPWaves);
+  if (nmt == 4)
+    hipLaunchKernelGGL((index_score_prefill<4, TABLE>), grid, block, 0, s, a, n_blocks);
+  else if (nmt == 3)
+    hipLaunchKernelGGL((index_score_prefill<3, TABLE>), grid, block, 0, s, a, n_blocks);
+  else if (nmt == 2)
+    hipLaunchKernelGGL((index_score_prefill<2, TABLE>), grid, block, 0, s, a, n_blocks);
+  else
+    hipLaunchKernelGGL((index_score_prefill<1, TABLE>), grid, block, 0, s, a, n_blocks);
+  return hipGetLastError();
 }
 
 template <int NMT, int DIM, bool FP8>
@@ -559,18 +697,13 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t s) {
   }
   const bool fp8 = a.dtype == 2;
   // Many rows of FP8 128-wide keys (prefill): the GEMM-shaped kernel.
-  if (fp8 && a.dim == 128 && a.cand == nullptr && a.rows.n_rows >= kPRows && a.n_heads <= 64) {
+  const bool chunkable =
+      (a.k.block_table == nullptr || (a.k.page_shift >= 6 && a.n_slots <= kPMaxSub * 64)) &&
+      a.k.row_stride <= (1 << 24);
+  if (fp8 && a.dim == 128 && a.cand == nullptr && a.rows.n_rows >= kPRows && a.n_heads <= 64 && chunkable) {
     const int n_blocks = (a.rows.n_rows + kPRows - 1) / kPRows;
     const int nmt = (a.n_heads + 15) / 16;
-    if (nmt == 4)
-      hipLaunchKernelGGL(index_score_prefill<4>, dim3(n_blocks), dim3(64 * kPWaves), 0, s, a, n_blocks);
-    else if (nmt == 2)
-      hipLaunchKernelGGL(index_score_prefill<2>, dim3(n_blocks), dim3(64 * kPWaves), 0, s, a, n_blocks);
-    else if (nmt == 3)
-      hipLaunchKernelGGL(index_score_prefill<3>, dim3(n_blocks), dim3(64 * kPWaves), 0, s, a, n_blocks);
-    else
-      hipLaunchKernelGGL(index_score_prefill<1>, dim3(n_blocks), dim3(64 * kPWaves), 0, s, a, n_blocks);
-    return hipGetLastError();
+    return a.k.block_table ? launch_prefill<true>(a, nmt, n_blocks, s) : launch_prefill<false>(a, nmt, n_blocks, s);
   }
   if (a.dim == 64) return fp8 ? dispatch_heads<64, true>(a, s) : dispatch_heads<64, false>(a, s);
   return fp8 ? dispatch_heads<128, true>(a, s) : dispatch_heads<128, false>(a, s);
