@@ -7,16 +7,20 @@ Headline workload (the one the metric is quoted on): HySparse2-style decode,
 128 + top-1024, 6 query sets (1 FA + 5 SA) reusing one index tensor.  A step
 = index score -> window + top-k -> gather attention for all 6 query sets; 192
 queries per step.  The default run (--workload all) also measures, as extra
-records in the same JSON line: CSA compressed decode (queries/s), the CSA2
-FP4 layer group (queries/s) and the 64K-row DSA prefill (rows/s).
+records in the same JSON line: HySparse2 with its FA layer, CSA compressed
+decode, the CSA2 FP4 layer group, HCA (queries/s), the 64K-row DSA prefill and
+the CSA2 prefill group (rows/s).
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 Decode steps rotate over several independent input replicas so that a step's
-working set is not already resident in the 256 MB last-level cache.  Each
-entry-point call is bracketed by HIP events on the launch stream for the
-per-kernel breakdown and the roofline of the dominant kernel.
+working set is not already resident in the 256 MB last-level cache.  Decode
+throughput comes from one HIP graph of the K steps with --inflight (default
+2) independent steps in flight on as many streams, as a serving loop overlaps
+micro-batches; the strictly serial rate is reported beside it.  Each
+entry-point call is also timed alone (a graph of K calls between HIP events)
+for the per-kernel breakdown and the roofline of the dominant kernel.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload all]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload all] [--inflight 2]
 """
 from __future__ import annotations
 
@@ -540,6 +544,8 @@ def run_decode(args, wl, fa: bool = False):
     # on the launch stream (gpu_ms_per_step; with --eager also the per-call
     # times and the throughput).
     K = args.steps
+    inflight = max(1, min(args.inflight, len(calls)))
+    serial_elapsed = None
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -580,20 +586,37 @@ def run_decode(args, wl, fa: bool = False):
         # Throughput: the same K steps captured once as a HIP graph (no host
         # launches between calls, as a serving loop would run them); one
         # untimed replay uploads it, the timed replay runs the K steps.
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            cs = torch.cuda.current_stream().cuda_stream
-            for i in range(K):
-                for _, c in calls[i % len(calls)]:
-                    c(cs)
-        g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        g.replay()
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-        mode = "graph"
-        del g
+        # With --inflight n, step i goes to stream i % n of the graph: n
+        # independent batches in flight (each on its own replicas, so no
+        # buffer is shared), as a serving loop overlaps micro-batches; the
+        # serial figure (one stream) is reported next to it.
+        def timed_graph(n):
+            g = torch.cuda.CUDAGraph()
+            sides = [torch.cuda.Stream() for _ in range(n - 1)]
+            with torch.cuda.graph(g):
+                main = torch.cuda.current_stream()
+                for sd in sides:
+                    sd.wait_stream(main)
+                sts = [main] + sides
+                for i in range(K):
+                    with torch.cuda.stream(sts[i % n]):
+                        cs = sts[i % n].cuda_stream
+                        for _, c in calls[i % len(calls)]:
+                            c(cs)
+                for sd in sides:
+                    main.wait_stream(sd)
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            del g
+            return dt
+
+        serial_elapsed = timed_graph(1)
+        elapsed = timed_graph(inflight) if inflight > 1 else serial_elapsed
+        mode = "graph" if inflight == 1 else "graph, %d steps in flight" % inflight
     ms_step = elapsed * 1e3 / K
     gpu_ms_step = sum(evs[i][0].elapsed_time(evs[i][-1]) for i in range(K)) / K
 
@@ -640,6 +663,9 @@ def run_decode(args, wl, fa: bool = False):
         "gpu_ms_per_step": round(gpu_ms_step, 5),
         "kernels": kernels,
     }
+    if serial_elapsed is not None and inflight > 1:
+        out["serial"] = {"value": round(queries * K / serial_elapsed, 1),
+                         "ms_per_step": round(serial_elapsed * 1e3 / K, 5)}
     if wl.block:
         # entries scored per query by the layer group (Full + Reindex; the
         # Reuse layers score none), against one full-domain indexer per layer
@@ -681,6 +707,9 @@ def main():
                     help="prefill: query rows per block (the score buffer holds one block)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run a plain copy of this size first (counter calibration)")
+    ap.add_argument("--inflight", type=int, default=2,
+                    help="decode: independent steps in flight on that many streams of the timed "
+                         "graph (1 = strictly one step after another; at most --replicas)")
     ap.add_argument("--eager", action="store_true",
                     help="decode: launch every call from the host in the timed region instead of "
                          "replaying one captured graph of the K steps")

@@ -534,6 +534,49 @@ def test_graph_replay_matches_eager(name, dev):
             assert torch.equal(a, b), (name, rep)
 
 
+@pytest.mark.parametrize("name", ["hysparse2", "csa2"])
+def test_steps_in_flight_match_serial(name, dev):
+    """Independent steps issued on two streams of one HIP graph (the
+    benchmark's steps in flight) give the outputs each step gives alone: no
+    workspace or other state is shared between the steps."""
+    wl, _ = CASES[name]
+    _flush("case in flight %s" % name)
+    steps = [_step(synth.make_problem(wl, device="cpu", seed_base=900 + 50 * i), dev)[1]
+             for i in range(2)]
+    outs = lambda st: [t for t in (st.scores + st.idx + st.count + st.o + st.lse
+                                   + [st.pool, st.pool_count]) if t is not None]
+    stream = torch.cuda.current_stream().cuda_stream
+    refs = []
+    for st in steps:
+        for t in outs(st):
+            t.zero_()
+        for _, c in st.prepare():
+            c(stream)
+        torch.cuda.synchronize()
+        refs.append([t.clone() for t in outs(st)])
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g):
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        for i in range(4):  # A B A B, alternating streams
+            st_ = main if i % 2 == 0 else side
+            with torch.cuda.stream(st_):
+                for _, c in steps[i % 2].prepare():
+                    c(st_.cuda_stream)
+        main.wait_stream(side)
+    for rep in range(2):
+        for st in steps:
+            for t in outs(st):
+                t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, st in enumerate(steps):
+            for a, b in zip(outs(st), refs[k]):
+                assert torch.equal(a, b), (name, rep, k)
+
+
 def test_deterministic_and_reuse(dev):
     """Two runs are bitwise identical; one fused call over all query sets
     equals one call per set (index reuse changes nothing numerically)."""
