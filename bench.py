@@ -688,6 +688,34 @@ def run_decode(args, wl, fa: bool = False):
 EXTRA = ("hysparse2_fa", "csa", "csa2", "hca", "dsa", "csa2_prefill")
 
 
+def achievable_peaks():
+    """What plain kernels of this library reach on this GPU (include/sa_peak.h):
+    a streaming 16-byte-load HBM read over 4 GiB, and dense MFMA loops in bf16
+    (16x16x32) and fp8 (16x16x128).  Context for the roofline fractions, which
+    stay against the published peaks."""
+    from index_reuse_amd import binding as B
+
+    t = time.perf_counter()
+    out = {"hbm_read_GBs": round(B.peak_read_gbs(4 << 30), 1),
+           "bf16_mfma_TFLOPs": round(B.peak_mfma_tflops("bf16"), 1),
+           "fp8_mfma_TFLOPs": round(B.peak_mfma_tflops("fp8"), 1)}
+    print("# achievable peaks in %.1f s: %s" % (time.perf_counter() - t, out), file=sys.stderr,
+          flush=True)
+    return out
+
+
+def add_achievable(rec, ach):
+    """The dominant call's rate as a fraction of the matching achievable peak."""
+    rf = rec.get("roofline")
+    if not rf:
+        return
+    if rf["unit"] == "GB/s":
+        ref = ach["hbm_read_GBs"]
+    else:
+        ref = ach["fp8_mfma_TFLOPs"] if rf["peak"] == MFMA_PEAK_TFLOPS["fp8"] else ach["bf16_mfma_TFLOPs"]
+    rf["frac_of_achievable"] = round(rf["achieved"] / ref, 4) if ref else None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -739,13 +767,20 @@ def main():
         print("# %s done in %.1f s" % (name, time.perf_counter() - t), file=sys.stderr, flush=True)
         return rec
 
+    ach = achievable_peaks()
     if args.workload != "all":
-        print(json.dumps(run(args.workload)), flush=True)
+        rec = run(args.workload)
+        add_achievable(rec, ach)
+        rec["achievable"] = ach
+        print(json.dumps(rec), flush=True)
         return
     out = run("hysparse2")
+    add_achievable(out, ach)
+    out["achievable"] = ach
     extra = {}
     for name in EXTRA:
         rec = run(name)
+        add_achievable(rec, ach)
         for k in ("metric", "n_gpus", "steps", "warmup", "higher_is_better", "scaling",
                   "vs_baseline", "data"):
             rec.pop(k, None)

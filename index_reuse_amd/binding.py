@@ -60,6 +60,8 @@ class sa_attn_desc(ctypes.Structure):
 EXPORTS = ("sparse_index_score", "sparse_topk_select", "sparse_attn_gather_fwd",
            "sparse_attn_gather_fwd_noalloc", "sparse_attn_score", "sparse_check_indices",
            "sa_workspace_size", "sa_last_error", "sa_abi_version")
+# include/sa_peak.h: achievable-peak probes (measurement only)
+PEAK_EXPORTS = ("sa_peak_read", "sa_peak_mfma")
 
 _lib = None
 
@@ -93,6 +95,10 @@ def load(path: str = LIB_PATH):
     L.sa_workspace_size.argtypes = [_i32, _P]
     L.sa_last_error.restype = ctypes.c_char_p
     L.sa_abi_version.restype = _i32
+    L.sa_peak_read.restype = _i32
+    L.sa_peak_read.argtypes = [_P, ctypes.c_size_t, _P, _i32, _P]
+    L.sa_peak_mfma.restype = _i32
+    L.sa_peak_mfma.argtypes = [_i32, _i32, _P, _i32, _P]
     _lib = L
     return L
 
@@ -441,3 +447,54 @@ def prepare_attn_gather_fwd(rows: Rows, q, k: Cache, v: Optional[Cache], idx, co
     d = attn_desc(rows, q, k, v, idx, count, o, lse, scale, d_v, sink, gate)
     return Prepared("sparse_attn_gather_fwd", d, SA_OP_ATTN_GATHER_FWD, q.device,
                     keep=(rows, q, k, v, idx, count, o, lse, sink, gate))
+
+
+# --------------------------------------------------------------------------
+# Achievable peaks (include/sa_peak.h): what plain kernels reach on this GPU,
+# for context next to the published peaks.
+
+
+def _timed(launch, reps: int = 5) -> float:
+    """Best of `reps` event-timed launches on the current stream, seconds."""
+    best = float("inf")
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        launch()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    return best
+
+
+def peak_read_gbs(nbytes: int = 4 << 30, device="cuda") -> float:
+    """HBM read rate (GB/s) of a streaming 16-byte-load kernel over `nbytes`
+    (one contiguous slab per workgroup)."""
+    L = load()
+    src = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    src.fill_(1)
+    grid = 1024  # four workgroups per CU, one contiguous slab each
+    sink = torch.empty(grid * 256, dtype=torch.int32, device=device)
+    launch = lambda: _check(L.sa_peak_read(_ptr(src), nbytes, _ptr(sink), grid, _stream()))
+    launch()
+    torch.cuda.synchronize()
+    dt = _timed(launch)
+    del src, sink
+    return nbytes / dt / 1e9
+
+
+def peak_mfma_tflops(dtype: str = "bf16", iters: int = 4096, device="cuda") -> float:
+    """Dense MFMA rate (TFLOP/s) of a loop of independent 16x16 MFMA chains
+    (bf16 16x16x32 or fp8 16x16x128) on every SIMD."""
+    L = load()
+    dt_code = {"bf16": 1, "fp8": 2}[dtype]
+    grid = 256 * 4  # 4 workgroups of 4 waves per CU: 4 waves per SIMD
+    sink = torch.empty(grid * 256, dtype=torch.float32, device=device)
+    launch = lambda: _check(L.sa_peak_mfma(dt_code, iters, _ptr(sink), grid, _stream()))
+    launch()
+    torch.cuda.synchronize()
+    dt = _timed(launch)
+    flops = grid * 4 * iters * 8 * (16384 if dt_code == 1 else 65536)
+    del sink
+    return flops / dt / 1e12

@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
 
 SOURCES = ["abi.cpp", "index_score.hip", "topk_select.hip", "attn_gather.hip", "attn_score.hip",
-           "check_idx.hip"]
+           "check_idx.hip", "peak_probe.hip"]
 HEADERS = ["common.hpp", "kernels.hpp"]
 
 ARCH = "gfx950"

@@ -24,8 +24,8 @@ def lib():
     return ira.load()
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, re.M))
 
@@ -35,6 +35,20 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
+
+
+def test_exports_peak_probes(lib):
+    """include/sa_peak.h (measurement probes) is exported by the same library."""
+    declared = _declared_functions(os.path.join(ROOT, "include", "sa_peak.h"))
+    assert declared == set(B.PEAK_EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_peak_probes_reject_bad_arguments(lib):
+    """Invalid probe arguments are rejected on the host (no launch)."""
+    assert lib.sa_peak_mfma(3, 1, None, 1, None) < 0
+    assert lib.sa_peak_read(None, 16, None, 1, None) < 0
 
 
 def test_abi_version(lib):

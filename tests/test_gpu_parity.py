@@ -883,3 +883,18 @@ def test_check_indices_device(dev):
         with pytest.raises(SAError, match="row %d: .*%s" % (row, what)):
             check_indices(rows, torch.from_numpy(np.ascontiguousarray(bad_idx)).to(dev),
                           torch.from_numpy(np.ascontiguousarray(bad_cnt)).to(dev))
+
+
+def test_peak_probes_run(dev):
+    """The achievable-peak probes run and report plausible MI355X rates (a
+    streaming read between 1 and 8 TB/s; dense MFMA loops above 100 TFLOP/s
+    and below the 2.5 / 5.0 PF dense peaks)."""
+    from index_reuse_amd import binding as B
+
+    _flush("case peak probes")
+    gbs = B.peak_read_gbs(1 << 30)
+    bf16 = B.peak_mfma_tflops("bf16", iters=512)
+    fp8 = B.peak_mfma_tflops("fp8", iters=256)
+    assert 1000 < gbs < 8000, gbs
+    assert 100 < bf16 < 2500 * 1.02, bf16
+    assert 100 < fp8 < 5000 * 1.02, fp8
