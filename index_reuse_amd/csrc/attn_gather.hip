@@ -1087,6 +1087,341 @@ __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, in
   }
 }
 
+// ------------------------------------------- latent prefill, eight waves
+// The same work as attn_mla (64 query rows of one KV head per workgroup, one
+// 576- or 512-wide bf16 row per entry, V its first 512 channels), on eight
+// waves, two per SIMD, so that one wave's LDS and MFMA latency hides behind
+// the other's work.  Wave w = (hp, dh, mh) = (w & 1, (w >> 1) & 1, w >> 2):
+//   - S: partial logits of row tiles {2 hp, 2 hp + 1} over the entries of
+//     half mh of the 32-entry tile (16 entries) and the k-steps of dim half
+//     dh; each K fragment read from LDS feeds two MFMAs;
+//   - the dim halves swap one row tile's partials through LDS; wave w then
+//     finishes row tile 2 hp + dh over entry half mh (mask, softmax) and
+//     writes its probabilities into its half of the tile's P^T operand;
+//   - O: channels [64 w, 64 w + 64) of all four row tiles.
+// The two entry halves of a row tile share one reference max, taken once
+// (the first tile with an entry) through LDS, and add their probability
+// sums at the end.
+// Tiles come from HBM straight into LDS with gfx950's 16-byte load-to-LDS
+// (no register staging), two tiles ahead, into three buffers that are
+// separate LDS arrays, so the compiler can tell a tile's reads from the
+// loads into the other buffers and count the loads still in flight.  Each
+// load instruction fills 1 KB of consecutive LDS; rows are laid out as in
+// attn_mla, 16 bytes longer than the data (the lanes that land on a row's
+// pad load the row's first piece again), which keeps the MFMA-layout reads
+// of K free of bank conflicts.
+template <int DQK>
+struct Mla8Lds {
+  static constexpr int SLOTS = kMaxEntries + 3 * kTile;
+  float sx[8][4][64];           // S partials handed to the other dim half
+  u32x4 p[kMlaRT][64];          // P^T operand of each row tile: 8 bytes per entry half
+  float mx[8][16];              // row max of a wave's entry half
+  float ml[kMlaRT][2][16][3];   // per row tile and entry half: m, rounded and unrounded sums
+  int32_t wfirst[8];
+  int32_t slot[SLOTS];
+};
+
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// s_waitcnt with only the vector-memory count set (expcnt, lgkmcnt at max).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+// Barrier for LDS data only: waits for this wave's LDS operations, not for
+// its loads to LDS still in flight (a __syncthreads would wait for those
+// too).  The empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int DQK>
+__global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, int n_units, int Z) {
+  constexpr int NTH = 512, DV = kMlaDv, RT = kMlaRT;
+  constexpr int P = DQK / 8;               // 16-byte pieces per row
+  constexpr int PP = P + 1;                // with the pad
+  constexpr int KH = DQK / 64;             // k-steps per dim half
+  // 1 KB loads per tile, the same number for every wave (the loads past the
+  // tile's last row fill slack that nothing reads), so that one wait count
+  // leaves exactly the newest tile's loads in flight in every wave
+  constexpr int JW = (kTile * PP + 511) / 512;
+  constexpr int NJ = 8 * JW;
+  using L = Mla8Lds<DQK>;
+  static_assert(sizeof(L) + 3 * NJ * 1024 <= 160 * 1024, "LDS budget");
+  __shared__ __align__(16) L lds;
+  __shared__ __align__(16) u32x4 kb0[NJ * 64];
+  __shared__ __align__(16) u32x4 kb1[NJ * 64];
+  __shared__ __align__(16) u32x4 kb2[NJ * 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar
+  const int col = lane & 15, gq = lane >> 4;
+  const int hp = wave & 1, dh = (wave >> 1) & 1, mh = wave >> 2;
+  const int own = 2 * hp + dh;   // row tile whose entry half mh this wave finishes
+  const int partner = wave ^ 2;  // same row tiles and entry half, other dim half
+  const int twin = wave ^ 4;     // same row tile, other entry half
+  int unit, zg;
+  mla_unit(n_units, Z, unit, zg);
+  if (unit < 0) return;
+  const int sp = unit % a.n_split;
+  const int ry = unit / a.n_split;
+  const int r = ry / a.hkv, g = ry % a.hkv;
+  const int G = a.hq / a.hkv;
+  const int Mq = a.n_qsets * G;
+  const int qrow0 = zg * 16 * RT;
+
+  // this wave's S row tiles, k-steps [KH dh, KH dh + KH), as B operands:
+  // [0] the tile it finishes (own), [1] the one its partner finishes
+  u32x4 qv[2][KH];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const int qr = qrow0 + 16 * (ht == 0 ? own : own ^ 1) + col;
+    if (qr < Mq) {
+      const int set = qr / G, h = g * G + qr % G;
+      const u32x4* qp = reinterpret_cast<const u32x4*>(
+          reinterpret_cast<const uint16_t*>(a.q) +
+          (((int64_t)set * a.rows.n_rows + r) * a.hq + h) * DQK + gq * (DQK / 4));
+#pragma unroll
+      for (int i = 0; i < KH; ++i) qv[ht][i] = qp[KH * dh + i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < KH; ++i) qv[ht][i] = u32x4{0, 0, 0, 0};
+    }
+  }
+  int sel_pre[kPT];
+  issue_index_loads<NTH>(a, r, sp * per_split, sel_pre);
+  const RowInfo ri = row_info(a.rows, r);
+  // two tiles read ahead: the table covers tiles up to nsteps + 1
+  const RangeTable rt = build_range_table<NTH, 1, 2>(a, r, sp * per_split, per_split, ri, sel_pre,
+                                                     lds.slot, lds.wfirst);
+  const int nsteps_run = rt.nsteps_run;
+  const uint32_t dummy = rt.dummy;
+  const char* kbase = reinterpret_cast<const char*>(a.k.data) + (size_t)g * (DQK * 2);
+  const uint32_t rstride = (uint32_t)a.k.row_stride;
+
+  // Tile s into buf: load J = wave + 8 j fills LDS pieces f = 64 J + lane,
+  // piece f % PP of row f / PP (the pad and the lanes past the last row load
+  // a valid piece that nothing reads).  The addresses are worked out ahead
+  // of the issue (tile_addr), so that the table reads and the arithmetic
+  // overlap other work.
+  int drow[JW], doff[JW];
+#pragma unroll
+  for (int j = 0; j < JW; ++j) {
+    const int f = 64 * (wave + 8 * j) + lane;
+    const int ps = f % PP;
+    drow[j] = min(f / PP, kTile - 1);
+    doff[j] = (ps < P ? ps : 0) * 16;
+  }
+  struct TileAddr {
+    const char* p[JW];
+  };
+  auto tile_addr = [&](int s) __attribute__((always_inline)) {
+    TileAddr ta;
+    int sv[JW];
+#pragma unroll
+    for (int j = 0; j < JW; ++j) sv[j] = lds.slot[s * kTile + drow[j]];
+#pragma unroll
+    for (int j = 0; j < JW; ++j) {
+      const uint32_t slot = sv[j] >= 0 ? (uint32_t)sv[j] : dummy;
+      ta.p[j] = kbase + (uint64_t)slot * rstride + doff[j];
+    }
+    return ta;
+  };
+  auto issue_tile = [&](const TileAddr& ta, u32x4* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < JW; ++j)
+      __builtin_amdgcn_global_load_lds((gptr_t)ta.p[j], (lptr_t)(buf + 64 * (wave + 8 * j)), 16, 0, 0);
+  };
+  // Wait until only the loads of the last tile issued are in flight.
+  auto wait_all_but_last = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(JW));
+  };
+
+  // Softmax state of row tile `own` over entry half mh (lane col): the
+  // reference m_run is fixed by the first tile with an entry; a second pass
+  // runs with the true max if some logit exceeds it by more than kHeadroom.
+  constexpr float kHeadroom = 64.0f;
+  f32x4 O[RT][4];  // [row tile][t]: lane element i is channel 64 w + 16 gq + 4 (t ^ (gq & 1)) + i
+  float m_run = -__builtin_huge_valf(), m_top = -__builtin_huge_valf();
+  float l_run = 0.0f, l_lse = 0.0f;
+  bool m_set = false;
+
+  // Transpose-read addressing of V (see attn_mfma): lane 4 jj + q of k-group
+  // gq fetches channels [64 w + 16 q + 4 (t ^ (q & 1)), +4) of entry
+  // 4 gq + jj (then 16 + 4 gq + jj).  With the padded rows, alternating t
+  // between the q groups puts the 16 lanes of a block on distinct banks.
+  const int vq = lane & 3;
+  const int voff = (4 * gq + ((lane >> 2) & 3)) * (PP * 8) + 64 * wave + 16 * vq + 4 * (vq & 1);
+
+  auto body = [&](int s, const u32x4* cur, u32x4* nx2) __attribute__((always_inline)) {
+    const TileAddr ta = tile_addr(s + 2);
+    // S^T partials [ht]: entries 16 mh + (M), query rows of tile own (ht 0)
+    // and own ^ 1 (ht 1) (N)
+    f32x4 acc[2];
+    acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      const u32x4* krow = cur + (16 * mh + col) * PP + gq * (P / 4) + KH * dh;
+#pragma unroll
+      for (int i = 0; i < KH; ++i) {
+        const u32x4 av = krow[i];
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+          acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, qv[ht][i]), acc[ht], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds.sx[wave][i][lane] = acc[1][i];
+    lds_barrier();
+    // every wave is past tile s - 1's O phase: its buffer takes tile s + 2
+    issue_tile(ta, nx2);
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = acc[0][i] + lds.sx[partner][i][lane];
+    // mask and scale: lane holds entries 16 mh + 4 gq + i for query row col
+    const i32x4 sl = *reinterpret_cast<const i32x4*>(&lds.slot[s * kTile + 16 * mh + 4 * gq]);
+    float tmax = -__builtin_huge_valf();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = sl[i] >= 0 ? x[i] * a.scale_log2 : -__builtin_huge_valf();
+      tmax = fmaxf(tmax, x[i]);
+    }
+    tmax = xor16_32_max(tmax);
+    if (!m_set) {
+      // whether the tile has an entry is read from the slot table, so every
+      // wave takes the same branch
+      const i32x4 so = *reinterpret_cast<const i32x4*>(&lds.slot[s * kTile + 16 * (1 - mh) + 4 * gq]);
+      const bool any = (sl[0] >= 0) | (sl[1] >= 0) | (sl[2] >= 0) | (sl[3] >= 0) | (so[0] >= 0) |
+                       (so[1] >= 0) | (so[2] >= 0) | (so[3] >= 0);
+      if (__builtin_amdgcn_ballot_w64(any) != 0) {
+        if (gq == 0) lds.mx[wave][col] = tmax;
+        lds_barrier();
+        m_run = fmaxf(tmax, lds.mx[twin][col]);
+        m_set = true;
+      }
+    }
+    m_top = fmaxf(m_top, tmax);
+    const float m_use = m_run == -__builtin_huge_valf() ? 0.0f : m_run;
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(x[i] - m_use);
+    const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
+    const float psum = (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u)) +
+                       (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xFFFF0000u));
+    const float xsum = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    l_run += xor16_32_sum(psum);
+    l_lse += xor16_32_sum(xsum);
+    // P^T k-slots 8 gq + j: entry 4 gq + j (half 0) in the low 8 bytes,
+    // 16 + 4 gq + j (half 1) in the high 8 bytes
+    reinterpret_cast<uint2*>(&lds.p[own][lane])[mh] = uint2{p01, p23};
+    // tile s + 1 has landed (tile s + 2 may still be in flight)
+    wait_all_but_last();
+    lds_barrier();
+    bf16x8 pb[RT];
+#pragma unroll
+    for (int q = 0; q < RT; ++q) pb[q] = __builtin_bit_cast(bf16x8, lds.p[q][lane]);
+    const uint16_t* kb = reinterpret_cast<const uint16_t*>(cur);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // 4 (t ^ (q & 1)) = 4 t + 4 (q & 1) - 8 (t & 1) (q & 1)
+      const int off = voff + 4 * t - (t & 1) * 8 * (vq & 1);
+      const s16x4 lo = lds_read_tr16(kb + off);
+      const s16x4 hi = lds_read_tr16(kb + off + 16 * PP * 8);
+      const s16x8 b = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int q = 0; q < RT; ++q)
+        O[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), pb[q],
+                                                          O[q][t], 0, 0, 0);
+    }
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int q = 0; q < RT; ++q)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) O[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    issue_tile(tile_addr(0), kb0);
+    issue_tile(tile_addr(1), kb1);
+    wait_all_but_last();
+    lds_barrier();
+    int s = 0;
+#pragma unroll 1
+    for (; s + 3 <= nsteps_run; s += 3) {
+      body(s, kb0, kb2);
+      body(s + 1, kb1, kb0);
+      body(s + 2, kb2, kb1);
+    }
+    if (s < nsteps_run) body(s, kb0, kb2);
+    if (s + 1 < nsteps_run) body(s + 1, kb1, kb0);
+    if (gq == 0) lds.mx[wave][col] = m_top;
+    if (!__syncthreads_or(m_top > m_run + kHeadroom)) break;
+    m_run = fmaxf(m_top, lds.mx[twin][col]);
+    m_set = true;
+    l_run = 0.0f;
+    l_lse = 0.0f;
+  }
+  // no load to LDS may still be in flight when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+  // publish this wave's half of its row tile, then write channels 64 w.. of
+  // all RT row tiles
+  if (gq == 0) {
+    lds.ml[own][mh][col][0] = m_run;
+    lds.ml[own][mh][col][1] = l_run;
+    lds.ml[own][mh][col][2] = l_lse;
+  }
+  __syncthreads();
+  const int R_ = a.rows.n_rows;
+  const bool swp = gq & 1;
+#pragma unroll
+  for (int q = 0; q < RT; ++q) {
+    const int qr = qrow0 + 16 * q + col;
+    if (qr >= Mq) continue;
+    const int set = qr / G, h = g * G + qr % G;
+    const int64_t orow = ((int64_t)set * R_ + r) * a.hq + h;
+    const float m_r = lds.ml[q][0][col][0];
+    const float l_r = lds.ml[q][0][col][1] + lds.ml[q][1][col][1];
+    const float lx = lds.ml[q][0][col][2] + lds.ml[q][1][col][2];
+    const int c0 = wave * 64 + 16 * gq;
+    // channels c0 + 8 c2 + [0, 8): t = 2 c2 and 2 c2 + 1, swapped on odd gq
+    f32x4 o8[2][2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      o8[c2][0] = swp ? O[q][2 * c2 + 1] : O[q][2 * c2];
+      o8[c2][1] = swp ? O[q][2 * c2] : O[q][2 * c2 + 1];
+    }
+    if (a.n_split == 1) {
+      float lse;
+      const float inv = finish_row(m_r, l_r, lx, sink_log2(a, set, h), lse);
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const f32x4 v0 = o8[c2][0] * inv, v1 = o8[c2][1] * inv;
+        float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        apply_gate(a, orow * DV + c0 + 8 * c2, v);
+        store8(a, orow * DV + c0 + 8 * c2, v);
+      }
+      if (a.lse && wave == 0 && gq == 0) a.lse[orow] = lse;
+    } else {
+      const int64_t nrows = (int64_t)a.n_qsets * R_ * a.hq;
+      float* po = a.part + ((int64_t)sp * nrows + orow) * DV + c0;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        reinterpret_cast<f32x4*>(po + 8 * c2)[0] = o8[c2][0];
+        reinterpret_cast<f32x4*>(po + 8 * c2)[1] = o8[c2][1];
+      }
+      if (wave == 0 && gq == 0) {
+        float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 3;
+        ml[0] = m_r;
+        ml[1] = l_r;
+        ml[2] = lx;
+      }
+    }
+  }
+}
+
 // Merge split partials: o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i,
 // lse from the unrounded sums lx_i the same way.  One wave per output row:
 // lane i < n_split holds split i's (m, l, lx) and its weight; every lane then
@@ -1301,6 +1636,21 @@ hipError_t launch_mla(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DQK>
+hipError_t launch_mla8(const AttnArgs& a, hipStream_t s) {
+  const int G = a.hq / a.hkv;
+  const int groups = (a.n_qsets * G + 16 * kMlaRT - 1) / (16 * kMlaRT);
+  const int per = ((a.max_entries + a.n_split - 1) / a.n_split + kTile - 1) / kTile * kTile;
+  const int n_units = a.n_split * a.rows.n_rows * a.hkv;
+  const int64_t nwg = (int64_t)(n_units + 7) / 8 * 8 * groups;
+  hipLaunchKernelGGL((attn_mla8<DQK>), dim3((unsigned)nwg), dim3(512), 0, s, a, per, n_units, groups);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split == 1) return e;
+  const int64_t nrows = (int64_t)a.n_qsets * a.rows.n_rows * a.hq;
+  hipLaunchKernelGGL(attn_combine, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int DQK, int DV, int KV, int D>
 hipError_t launch_shaped(const AttnArgs& a, hipStream_t s) {
   const AttnShape sh = attn_shape(a);
@@ -1361,11 +1711,11 @@ hipError_t launch_attn_gather(const AttnArgs& a, hipStream_t s) {
     if (a.dqk == 256 && a.dv == 256) return launch_shaped<256, 256, KV_SEPARATE, 2>(a, s);
   } else if (a.kv_kind == KV_SHARED) {
     if (a.dqk == 576 && a.dv == 512) {
-      if (many_rows) return launch_mla<576, KV_SHARED>(a, s);
+      if (many_rows) return launch_mla8<576>(a, s);
       return launch_shaped<576, 512, KV_SHARED, 2>(a, s);
     }
     if (a.dqk == 512 && a.dv == 512) {
-      if (many_rows) return launch_mla<512, KV_SHARED>(a, s);
+      if (many_rows) return launch_mla8<512>(a, s);
       return launch_shaped<512, 512, KV_SHARED, 2>(a, s);
     }
     if (a.dqk == 128 && a.dv == 128) return launch_shaped<128, 128, KV_SHARED, 2>(a, s);
