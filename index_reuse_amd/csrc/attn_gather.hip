@@ -1242,6 +1242,8 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
   // Softmax state of row tile `own` over entry half mh (lane col): the
   // reference m_run is fixed by the first tile with an entry; a second pass
   // runs with the true max if some logit exceeds it by more than kHeadroom.
+  // m_top and the two sums are kept per lane (over the lane's entries) and
+  // reduced over the row's four lanes once, at the end of a pass.
   constexpr float kHeadroom = 64.0f;
   f32x4 O[RT][4];  // [row tile][t]: lane element i is channel 64 w + 16 gq + 4 (t ^ (gq & 1)) + i
   float m_run = -__builtin_huge_valf(), m_top = -__builtin_huge_valf();
@@ -1289,7 +1291,7 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
       x[i] = sl[i] >= 0 ? x[i] * a.scale_log2 : -__builtin_huge_valf();
       tmax = fmaxf(tmax, x[i]);
     }
-    tmax = xor16_32_max(tmax);
+    m_top = fmaxf(m_top, tmax);
     if (!m_set) {
       // whether the tile has an entry is read from the slot table, so every
       // wave takes the same branch
@@ -1297,13 +1299,13 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
       const bool any = (sl[0] >= 0) | (sl[1] >= 0) | (sl[2] >= 0) | (sl[3] >= 0) | (so[0] >= 0) |
                        (so[1] >= 0) | (so[2] >= 0) | (so[3] >= 0);
       if (__builtin_amdgcn_ballot_w64(any) != 0) {
+        tmax = xor16_32_max(tmax);
         if (gq == 0) lds.mx[wave][col] = tmax;
         lds_barrier();
         m_run = fmaxf(tmax, lds.mx[twin][col]);
         m_set = true;
       }
     }
-    m_top = fmaxf(m_top, tmax);
     const float m_use = m_run == -__builtin_huge_valf() ? 0.0f : m_run;
     float pr[4];
 #pragma unroll
@@ -1312,8 +1314,8 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
     const float psum = (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u)) +
                        (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xFFFF0000u));
     const float xsum = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    l_run += xor16_32_sum(psum);
-    l_lse += xor16_32_sum(xsum);
+    l_run += psum;
+    l_lse += xsum;
     // P^T k-slots 8 gq + j: entry 4 gq + j (half 0) in the low 8 bytes,
     // 16 + 4 gq + j (half 1) in the high 8 bytes
     reinterpret_cast<uint2*>(&lds.p[own][lane])[mh] = uint2{p01, p23};
@@ -1356,9 +1358,10 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
     }
     if (s < nsteps_run) body(s, kb0, kb2);
     if (s + 1 < nsteps_run) body(s + 1, kb1, kb0);
-    if (gq == 0) lds.mx[wave][col] = m_top;
+    const float m_row = xor16_32_max(m_top);
+    if (gq == 0) lds.mx[wave][col] = m_row;
     if (!__syncthreads_or(m_top > m_run + kHeadroom)) break;
-    m_run = fmaxf(m_top, lds.mx[twin][col]);
+    m_run = fmaxf(m_row, lds.mx[twin][col]);
     m_set = true;
     l_run = 0.0f;
     l_lse = 0.0f;
@@ -1368,6 +1371,8 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
 
   // publish this wave's half of its row tile, then write channels 64 w.. of
   // all RT row tiles
+  l_run = xor16_32_sum(l_run);
+  l_lse = xor16_32_sum(l_lse);
   if (gq == 0) {
     lds.ml[own][mh][col][0] = m_run;
     lds.ml[own][mh][col][1] = l_run;
