@@ -1257,6 +1257,20 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
   const int vq = lane & 3;
   const int voff = (4 * gq + ((lane >> 2) & 3)) * (PP * 8) + 64 * wave + 16 * vq + 4 * (vq & 1);
 
+  // The O update of channel blocks t = 2, 3 of a tile waits in registers
+  // (its P^T operands and V fragments) and runs in the next tile's softmax
+  // phase, where the matrix pipe has nothing else to do.
+  bf16x8 pd[RT];
+  s16x8 vd[2];
+  auto deferred_o = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 2; t < 4; ++t)
+#pragma unroll
+      for (int q = 0; q < RT; ++q)
+        O[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vd[t - 2]), pd[q],
+                                                          O[q][t], 0, 0, 0);
+  };
+
   auto body = [&](int s, const u32x4* cur, u32x4* nx2) __attribute__((always_inline)) {
     const TileAddr ta = tile_addr(s + 2);
     // S^T partials [ht]: entries 16 mh + (M), query rows of tile own (ht 0)
@@ -1280,6 +1294,7 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
     lds_barrier();
     // every wave is past tile s - 1's O phase: its buffer takes tile s + 2
     issue_tile(ta, nx2);
+    deferred_o();
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = acc[0][i] + lds.sx[partner][i][lane];
@@ -1322,9 +1337,8 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
     // tile s + 1 has landed (tile s + 2 may still be in flight)
     wait_all_but_last();
     lds_barrier();
-    bf16x8 pb[RT];
 #pragma unroll
-    for (int q = 0; q < RT; ++q) pb[q] = __builtin_bit_cast(bf16x8, lds.p[q][lane]);
+    for (int q = 0; q < RT; ++q) pd[q] = __builtin_bit_cast(bf16x8, lds.p[q][lane]);
     const uint16_t* kb = reinterpret_cast<const uint16_t*>(cur);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -1333,18 +1347,26 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
       const s16x4 lo = lds_read_tr16(kb + off);
       const s16x4 hi = lds_read_tr16(kb + off + 16 * PP * 8);
       const s16x8 b = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      if (t >= 2) {
+        vd[t - 2] = b;
+        continue;
+      }
 #pragma unroll
       for (int q = 0; q < RT; ++q)
-        O[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), pb[q],
+        O[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), pd[q],
                                                           O[q][t], 0, 0, 0);
     }
   };
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int q = 0; q < RT; ++q)
+    for (int q = 0; q < RT; ++q) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) O[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pd[q] = bf16x8{};
+    }
+    vd[0] = s16x8{};
+    vd[1] = s16x8{};
     issue_tile(tile_addr(0), kb0);
     issue_tile(tile_addr(1), kb1);
     wait_all_but_last();
@@ -1358,6 +1380,7 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
     }
     if (s < nsteps_run) body(s, kb0, kb2);
     if (s + 1 < nsteps_run) body(s + 1, kb1, kb0);
+    deferred_o();
     const float m_row = xor16_32_max(m_top);
     if (gq == 0) lds.mx[wave][col] = m_row;
     if (!__syncthreads_or(m_top > m_run + kHeadroom)) break;
