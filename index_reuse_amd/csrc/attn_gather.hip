@@ -1257,17 +1257,19 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
   const int vq = lane & 3;
   const int voff = (4 * gq + ((lane >> 2) & 3)) * (PP * 8) + 64 * wave + 16 * vq + 4 * (vq & 1);
 
-  // The O update of channel blocks t = 2, 3 of a tile waits in registers
-  // (its P^T operands and V fragments) and runs in the next tile's softmax
-  // phase, where the matrix pipe has nothing else to do.
+  // The O update of channel blocks t >= TD of a tile waits in registers (its
+  // P^T operands and V fragments) and runs in the next tile's softmax phase,
+  // where the matrix pipe has nothing else to do.  (Deferring all four
+  // blocks made the loop spill.)
   bf16x8 pd[RT];
-  s16x8 vd[2];
+  constexpr int TD = 1;  // first deferred channel block
+  s16x8 vd[4 - TD];
   auto deferred_o = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 2; t < 4; ++t)
+    for (int t = TD; t < 4; ++t)
 #pragma unroll
       for (int q = 0; q < RT; ++q)
-        O[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vd[t - 2]), pd[q],
+        O[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vd[t - TD]), pd[q],
                                                           O[q][t], 0, 0, 0);
   };
 
@@ -1347,8 +1349,8 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
       const s16x4 lo = lds_read_tr16(kb + off);
       const s16x4 hi = lds_read_tr16(kb + off + 16 * PP * 8);
       const s16x8 b = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      if (t >= 2) {
-        vd[t - 2] = b;
+      if (t >= TD) {
+        vd[t - TD] = b;
         continue;
       }
 #pragma unroll
@@ -1365,8 +1367,8 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
       for (int t = 0; t < 4; ++t) O[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
       pd[q] = bf16x8{};
     }
-    vd[0] = s16x8{};
-    vd[1] = s16x8{};
+#pragma unroll
+    for (int t = TD; t < 4; ++t) vd[t - TD] = s16x8{};
     issue_tile(tile_addr(0), kb0);
     issue_tile(tile_addr(1), kb1);
     wait_all_but_last();
