@@ -15,12 +15,12 @@ Inputs are seeded synthetic tensors resident in HBM before timing starts.
 Decode steps rotate over several independent input replicas so that a step's
 working set is not already resident in the 256 MB last-level cache.  Decode
 throughput comes from one HIP graph of the K steps with --inflight (default
-2) independent steps in flight on as many streams, as a serving loop overlaps
+4) independent steps in flight on as many streams, as a serving loop overlaps
 micro-batches; the strictly serial rate is reported beside it.  Each
 entry-point call is also timed alone (a graph of K calls between HIP events)
 for the per-kernel breakdown and the roofline of the dominant kernel.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload all] [--inflight 2]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload all] [--inflight 4]
 """
 from __future__ import annotations
 
@@ -586,9 +586,10 @@ def run_decode(args, wl, fa: bool = False):
         # Throughput: the same K steps captured once as a HIP graph (no host
         # launches between calls, as a serving loop would run them); one
         # untimed replay uploads it, the timed replay runs the K steps.
-        # With --inflight n, step i goes to stream i % n of the graph: n
-        # independent batches in flight (each on its own replicas, so no
-        # buffer is shared), as a serving loop overlaps micro-batches; the
+        # With --inflight n, step i (replica i % R) goes to stream
+        # (i % R) % n of the graph: n independent batches in flight, each
+        # replica always on the same stream (so no buffer is used by two
+        # streams at once), as a serving loop overlaps micro-batches; the
         # serial figure (one stream) is reported next to it.
         def timed_graph(n):
             g = torch.cuda.CUDAGraph()
@@ -599,8 +600,9 @@ def run_decode(args, wl, fa: bool = False):
                     sd.wait_stream(main)
                 sts = [main] + sides
                 for i in range(K):
-                    with torch.cuda.stream(sts[i % n]):
-                        cs = sts[i % n].cuda_stream
+                    st = sts[(i % len(calls)) % n]
+                    with torch.cuda.stream(st):
+                        cs = st.cuda_stream
                         for _, c in calls[i % len(calls)]:
                             c(cs)
                 for sd in sides:
@@ -735,7 +737,7 @@ def main():
                     help="prefill: query rows per block (the score buffer holds one block)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run a plain copy of this size first (counter calibration)")
-    ap.add_argument("--inflight", type=int, default=2,
+    ap.add_argument("--inflight", type=int, default=4,
                     help="decode: independent steps in flight on that many streams of the timed "
                          "graph (1 = strictly one step after another; at most --replicas)")
     ap.add_argument("--eager", action="store_true",

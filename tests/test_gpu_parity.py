@@ -536,13 +536,14 @@ def test_graph_replay_matches_eager(name, dev):
 
 @pytest.mark.parametrize("name", ["hysparse2", "csa2"])
 def test_steps_in_flight_match_serial(name, dev):
-    """Independent steps issued on two streams of one HIP graph (the
+    """Independent steps issued on four streams of one HIP graph (the
     benchmark's steps in flight) give the outputs each step gives alone: no
     workspace or other state is shared between the steps."""
     wl, _ = CASES[name]
     _flush("case in flight %s" % name)
+    n = 4
     steps = [_step(synth.make_problem(wl, device="cpu", seed_base=900 + 50 * i), dev)[1]
-             for i in range(2)]
+             for i in range(n)]
     outs = lambda st: [t for t in (st.scores + st.idx + st.count + st.o + st.lse
                                    + [st.pool, st.pool_count]) if t is not None]
     stream = torch.cuda.current_stream().cuda_stream
@@ -555,16 +556,19 @@ def test_steps_in_flight_match_serial(name, dev):
         torch.cuda.synchronize()
         refs.append([t.clone() for t in outs(st)])
     g = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
+    sides = [torch.cuda.Stream() for _ in range(n - 1)]
     with torch.cuda.graph(g):
         main = torch.cuda.current_stream()
-        side.wait_stream(main)
-        for i in range(4):  # A B A B, alternating streams
-            st_ = main if i % 2 == 0 else side
+        for sd in sides:
+            sd.wait_stream(main)
+        sts = [main] + sides
+        for i in range(2 * n):  # each step twice, step j always on stream j
+            st_ = sts[i % n]
             with torch.cuda.stream(st_):
-                for _, c in steps[i % 2].prepare():
+                for _, c in steps[i % n].prepare():
                     c(st_.cuda_stream)
-        main.wait_stream(side)
+        for sd in sides:
+            main.wait_stream(sd)
     for rep in range(2):
         for st in steps:
             for t in outs(st):
