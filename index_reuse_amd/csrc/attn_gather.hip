@@ -339,6 +339,15 @@ __device__ __forceinline__ void fill_range_table(const AttnArgs& a, int r, int e
     }
     chunk(0, sel, mid, bt);
     for (int i0 = kPT * NTH; i0 < rt.n_tab; i0 += kPT * NTH) {
+      if (i0 >= rt.ne) {
+        // only padding from here on: no index or block-table reads to wait for
+#pragma unroll
+        for (int j = 0; j < kPT; ++j) {
+          const int i = i0 + j * NTH + tid;
+          if (i >= from && i < rt.n_tab) slot_tab[i] = -1;
+        }
+        continue;
+      }
       sel_of(i0, sel);
       chunk(i0, sel, NoMid(), bt);
     }
