@@ -1243,8 +1243,10 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
     for (int j = 0; j < JW; ++j)
       __builtin_amdgcn_global_load_lds((gptr_t)ta.p[j], (lptr_t)(buf + 64 * (wave + 8 * j)), 16, 0, 0);
   };
-  // Wait until only the loads of the last tile issued are in flight.
+  // Wait until only the loads of the last tile issued are in flight (the
+  // empty asm keeps the compiler from sinking those loads below the wait).
   auto wait_all_but_last = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(JW));
   };
 
@@ -1401,6 +1403,7 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
     l_lse = 0.0f;
   }
   // no load to LDS may still be in flight when the workgroup ends
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
   // publish this wave's half of its row tile, then write channels 64 w.. of
