@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 2       /* bumped on any descriptor layout change   */
+#define SA_ABI_VERSION 3       /* bumped on any descriptor layout change   */
 #define SA_INDEX_FORMAT 1      /* int32 asc, -1 pad, lowest-index tie-break */
 
 typedef int32_t sa_status;
@@ -164,7 +164,28 @@ typedef struct {
  *
  * Accumulation is fp32 (MFMA for BF16/FP8, FMA for F32); the ReLU and the
  * weighted head sum are fp32.
+ *
+ * Fused selection (sel != NULL): the scores feed the window + top-k selection
+ * (and/or the block-max pool) directly, and the call writes the selection's
+ * outputs instead of a score tensor ("CSA, HCA and CSA2", section 2.2: a
+ * prefill must not hold the n x n_c score matrix; "Lecture 10", section 5.1:
+ * the indexer's scores exist only to be ranked).  The rows are processed in
+ * passes of row_block rows (0 = all rows in one pass): each pass scores its
+ * rows into the workspace, then runs on them exactly the selection
+ * sparse_topk_select would run with *sel.  So the outputs are identical to
+ * the two calls made separately, and the workspace holds the scores of one
+ * pass only (row_block * score_stride floats) plus the selection's own
+ * workspace for row_block rows (sa_workspace_size(SA_OP_INDEX_SCORE, desc)).
+ *   - From *sel the call reads k, idx, count, idx_stride, block, max_blocks,
+ *     pool_stride, pool and pool_count (outputs for all R rows, as for
+ *     sparse_topk_select); its rows, scores, score_stride, cand, cand_count
+ *     and cand_stride are ignored: the rows and candidates are this
+ *     descriptor's, and score_stride here gives the capacity of a pass's
+ *     score rows (>= max n_avail, or >= cand_stride in candidate mode).
+ *   - `scores` may be NULL and is not written.
  */
+struct sa_topk_desc;
+
 typedef struct {
   sa_rows rows;
   const void* q;
@@ -178,6 +199,9 @@ typedef struct {
   int32_t skip_k;            /* dense route threshold (0 = off), see above     */
   float* scores;
   int64_t score_stride;
+  const struct sa_topk_desc* sel;  /* optional fused selection, see above      */
+  int32_t row_block;         /* fused selection: rows per pass (0 = all)      */
+  int32_t reserved;          /* 0                                             */
 } sa_index_desc;
 
 /*
@@ -215,7 +239,7 @@ typedef struct {
  * workspace may serve any sequence of calls, of any entry point and any row
  * count, as long as no two of them overlap in time.
  */
-typedef struct {
+typedef struct sa_topk_desc {
   sa_rows rows;
   const float* scores;
   int64_t score_stride;

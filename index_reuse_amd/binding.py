@@ -39,7 +39,8 @@ class sa_rows(ctypes.Structure):
 class sa_index_desc(ctypes.Structure):
     _fields_ = [("rows", sa_rows), ("q", _P), ("w", _P), ("k", sa_cache), ("n_heads", _i32),
                 ("dim", _i32), ("cand", _P), ("cand_count", _P), ("cand_stride", _i32),
-                ("skip_k", _i32), ("scores", _P), ("score_stride", _i64)]
+                ("skip_k", _i32), ("scores", _P), ("score_stride", _i64), ("sel", _P),
+                ("row_block", _i32), ("reserved", _i32)]
 
 
 class sa_topk_desc(ctypes.Structure):
@@ -218,15 +219,21 @@ def workspace(nbytes: int, device, op: int) -> Optional[torch.Tensor]:
 
 
 def index_desc(rows: Rows, q, w, k: Cache, scores, cand=None, cand_count=None,
-               skip_k: int = 0) -> sa_index_desc:
+               skip_k: int = 0, sel: Optional["sa_topk_desc"] = None, row_block: int = 0,
+               n_slots: Optional[int] = None) -> sa_index_desc:
+    """``sel`` (a topk descriptor, kept alive by the caller) asks for the
+    fused selection; ``scores`` may then be None with ``n_slots`` giving the
+    score capacity per row."""
     _dense(q, "q")
     _dense(w, "w")
     _dense(scores, "scores", rows=True)
     _dense(cand, "cand", rows=True)
     _dense(cand_count, "cand_count")
+    stride = int(scores.stride(0)) if scores is not None else int(n_slots)
+    sel_ptr = None if sel is None else ctypes.addressof(sel)
     return sa_index_desc(rows.c(), _ptr(q), _ptr(w), k.c(), int(q.shape[1]), int(q.shape[2]),
                          _ptr(cand), _ptr(cand_count), 0 if cand is None else int(cand.stride(0)),
-                         int(skip_k), _ptr(scores), int(scores.stride(0)))
+                         int(skip_k), _ptr(scores), stride, sel_ptr, int(row_block), 0)
 
 
 def index_score(rows: Rows, q: torch.Tensor, w: torch.Tensor, k: Cache,
@@ -246,12 +253,14 @@ def index_score(rows: Rows, q: torch.Tensor, w: torch.Tensor, k: Cache,
 
 def topk_desc(rows: Rows, scores, k: int, idx, count, cand=None, cand_count=None, block=0,
               max_blocks=0, pool=None, pool_count=None) -> sa_topk_desc:
+    """``scores`` may be None for the ``sel`` of a fused index call."""
     _dense(scores, "scores", rows=True)
     for t, n in ((idx, "idx"), (cand, "cand"), (pool, "pool")):
         _dense(t, n, rows=True)
     for t, n in ((count, "count"), (cand_count, "cand_count"), (pool_count, "pool_count")):
         _dense(t, n)
-    return sa_topk_desc(rows.c(), _ptr(scores), int(scores.stride(0)), _ptr(cand), _ptr(cand_count),
+    return sa_topk_desc(rows.c(), _ptr(scores), 0 if scores is None else int(scores.stride(0)),
+                        _ptr(cand), _ptr(cand_count),
                         0 if cand is None else int(cand.stride(0)), int(k), _ptr(idx), _ptr(count),
                         0 if idx is None else int(idx.stride(0)), int(block), int(max_blocks),
                         0 if pool is None else int(pool.stride(0)), _ptr(pool), _ptr(pool_count))
@@ -413,6 +422,22 @@ def prepare_index_score(rows: Rows, q, w, k: Cache, scores, cand=None, cand_coun
     d = index_desc(rows, q, w, k, scores, cand, cand_count, skip_k)
     return Prepared("sparse_index_score", d, SA_OP_INDEX_SCORE, q.device,
                     keep=(rows, q, w, k, scores, cand, cand_count))
+
+
+def prepare_index_select(rows: Rows, q, w, kc: Cache, n_slots: int, k: int, idx, count,
+                         cand=None, cand_count=None, block=0, max_blocks=0, pool=None,
+                         pool_count=None, skip_k: int = 0, row_block: int = 0, workspace=None):
+    """sparse_index_score with the fused selection: idx/count (and the pool)
+    straight from the indexer, with n_slots score slots per row held in the
+    workspace for row_block rows at a time (0 = all rows).  ``workspace``: a
+    buffer to share with calls that never overlap in time, if large enough."""
+    sel = topk_desc(rows, None, k, idx, count, cand, cand_count, block, max_blocks, pool,
+                    pool_count)
+    d = index_desc(rows, q, w, kc, None, cand, cand_count, skip_k, sel=sel, row_block=row_block,
+                   n_slots=n_slots)
+    return Prepared("sparse_index_score", d, SA_OP_INDEX_SCORE, q.device,
+                    keep=(rows, q, w, kc, sel, idx, count, cand, cand_count, pool, pool_count),
+                    workspace=workspace)
 
 
 def prepare_topk_select(rows: Rows, scores, k, idx, count, cand=None, cand_count=None, block=0,

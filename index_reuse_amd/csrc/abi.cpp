@@ -118,8 +118,11 @@ sa_status validate_index(const sa_index_desc* d, sa::IndexArgs* out) {
   }
   CHECK(d->k.heads == 1 && d->k.width == d->dim, SA_ERR_SHAPE,
         "%s: k must have heads == 1 and width == dim", op);
+  CHECK(d->row_block >= 0, SA_ERR_SHAPE, "%s: row_block must be >= 0", op);
+  CHECK(d->reserved == 0, SA_ERR_SHAPE, "%s: reserved must be 0", op);
   if (d->rows.n_rows == 0) return SA_OK;
-  CHECK(d->q && d->w && d->scores, SA_ERR_NULL, "%s: q, w and scores are required", op);
+  CHECK(d->q && d->w && (d->scores || d->sel), SA_ERR_NULL,
+        "%s: q, w and scores (or sel) are required", op);
   CHECK(aligned16(d->q), SA_ERR_SHAPE, "%s: q must be 16-byte aligned", op);
   st = check_cache(d->k, op, "k", (int64_t)d->dim * eb);
   if (st) return st;
@@ -203,6 +206,41 @@ sa_status validate_topk(const sa_topk_desc* d, sa::SelectArgs* out) {
     out->beta = nullptr;
     out->beta_stride = pool ? ((d->score_stride + d->block - 1) / d->block + 63) / 64 * 64 : 0;
   }
+  return SA_OK;
+}
+
+// ------------------------------------------------------- fused selection
+// sparse_index_score with sel: the rows per pass, the selection's arguments
+// for a pass of that many rows, and the workspace (one pass's scores, then
+// the selection's own workspace).
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+struct FusedPlan {
+  int rb;              // rows per pass
+  sa::SelectArgs sel;  // for a pass of rb rows (pointers of the first pass)
+  size_t score_bytes;  // one pass's scores, rounded up to 256 bytes
+  size_t sel_bytes;    // the selection's workspace for rb rows
+};
+
+sa_status validate_fused(const sa_index_desc* d, FusedPlan* plan) {
+  const char* op = "sparse_index_score";
+  CHECK(d->sel, SA_ERR_NULL, "%s: sel is NULL", op);
+  const int R = d->rows.n_rows;
+  const int rb = (d->row_block > 0 && d->row_block < R) ? d->row_block : R;
+  sa_topk_desc t = *d->sel;
+  t.rows = d->rows;
+  t.rows.n_rows = rb;
+  // stands in for the pass's score buffer (replaced at launch)
+  t.scores = reinterpret_cast<const float*>(uintptr_t(256));
+  t.score_stride = d->score_stride;
+  t.cand = d->cand;
+  t.cand_count = d->cand_count;
+  t.cand_stride = d->cand_stride;
+  sa_status st = validate_topk(&t, &plan->sel);
+  if (st) return st;
+  plan->rb = rb;
+  plan->score_bytes = align256((size_t)rb * (size_t)d->score_stride * sizeof(float));
+  plan->sel_bytes = rb > 0 ? sa::topk_workspace_bytes(plan->sel) : 0;
   return SA_OK;
 }
 
@@ -306,12 +344,59 @@ sa_status validate_attn(const sa_attn_desc* d, sa::AttnArgs* out) {
 extern "C" {
 
 sa_status sparse_index_score(const sa_index_desc* desc, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
+  const char* op = "sparse_index_score";
   sa::IndexArgs a;
   sa_status st = validate_index(desc, &a);
   if (st || desc->rows.n_rows == 0) return st;
-  return hip_status(sa::launch_index_score(a, (hipStream_t)stream), "sparse_index_score");
+  const hipStream_t s = (hipStream_t)stream;
+  if (!desc->sel) return hip_status(sa::launch_index_score(a, s), op);
+
+  // Fused selection: score a pass of rows into the workspace, select on it.
+  FusedPlan plan;
+  st = validate_fused(desc, &plan);
+  if (st) return st;
+  const size_t need = plan.score_bytes + plan.sel_bytes;
+  CHECK(ws && ws_bytes >= need, SA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given",
+        op, need, ws_bytes);
+  CHECK(((uintptr_t)ws & 255u) == 0, SA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned",
+        op);
+  float* pass_scores = reinterpret_cast<float*>(ws);
+  const int R = desc->rows.n_rows, rb = plan.rb;
+  const size_t q_row = (size_t)desc->n_heads * desc->dim * elem_bytes(desc->k.dtype);
+  for (int lo = 0; lo < R; lo += rb) {
+    const int n = R - lo < rb ? R - lo : rb;
+    sa::IndexArgs ia = a;
+    ia.rows.n_rows = n;
+    ia.rows.seq_of_row = a.rows.seq_of_row + lo;
+    ia.rows.pos_of_row = a.rows.pos_of_row + lo;
+    ia.q = reinterpret_cast<const char*>(a.q) + (size_t)lo * q_row;
+    ia.w = a.w + (size_t)lo * desc->n_heads;
+    if (a.cand) {
+      ia.cand = a.cand + (size_t)lo * a.cand_stride;
+      ia.cand_count = a.cand_count + lo;
+    }
+    ia.scores = pass_scores;
+    st = hip_status(sa::launch_index_score(ia, s), op);
+    if (st) return st;
+    sa::SelectArgs sl = plan.sel;
+    sl.rows = ia.rows;
+    sl.scores = pass_scores;
+    sl.cand = ia.cand;
+    sl.cand_count = ia.cand_count;
+    if (sl.k > 0) {
+      sl.idx = plan.sel.idx + (size_t)lo * sl.idx_stride;
+      sl.count = plan.sel.count + lo;
+    }
+    if (sl.pool) {
+      sl.pool = plan.sel.pool + (size_t)lo * sl.pool_stride;
+      sl.pool_count = plan.sel.pool_count + lo;
+    }
+    sl.beta = plan.sel_bytes ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + plan.score_bytes)
+                             : nullptr;
+    st = hip_status(sa::launch_topk_select(sl, s), op);
+    if (st) return st;
+  }
+  return SA_OK;
 }
 
 sa_status sparse_topk_select(const sa_topk_desc* desc, void* ws, size_t ws_bytes, void* stream) {
@@ -426,8 +511,14 @@ sa_status sparse_attn_gather_fwd_noalloc(const sa_attn_desc* desc, void* stream)
 
 size_t sa_workspace_size(int32_t op, const void* desc) {
   switch (op) {
-    case SA_OP_INDEX_SCORE:
-      return validate_index(reinterpret_cast<const sa_index_desc*>(desc), nullptr) ? (size_t)-1 : 0;
+    case SA_OP_INDEX_SCORE: {
+      const sa_index_desc* d = reinterpret_cast<const sa_index_desc*>(desc);
+      if (validate_index(d, nullptr)) return (size_t)-1;
+      if (!d->sel || d->rows.n_rows == 0) return 0;
+      FusedPlan plan;
+      if (validate_fused(d, &plan)) return (size_t)-1;
+      return plan.score_bytes + plan.sel_bytes;
+    }
     case SA_OP_TOPK_SELECT: {
       const sa_topk_desc* d = reinterpret_cast<const sa_topk_desc*>(desc);
       sa::SelectArgs a;

@@ -20,8 +20,8 @@ from typing import List, Optional
 import torch
 
 from .binding import (Cache, PreparedScore, Rows, attn_gather_fwd, index_score,
-                      prepare_attn_gather_fwd, prepare_index_score, prepare_topk_select,
-                      topk_select)
+                      prepare_attn_gather_fwd, prepare_index_score, prepare_index_select,
+                      prepare_topk_select, topk_select)
 
 
 def _cache(c, heads, width, fp4=False) -> Cache:
@@ -49,11 +49,16 @@ class Step:
     with the Reindex indices (Reindex query + Reuse queries, fused)."""
 
     def __init__(self, prob, scores_slots: Optional[int] = None, dense_route: bool = False,
-                 block_select=None):
+                 block_select=None, fused_select: bool = False, fused_row_block: int = 0):
         """``block_select`` = (block, n_blocks): select whole aligned blocks of
         candidates by their best score instead of single entries (HySparse's
         first generation: 16 blocks of 64 tokens next to the window); the
-        pool of kept blocks is the index tensor."""
+        pool of kept blocks is the index tensor.  ``fused_select``: each
+        index call selects in the same call (sparse_index_score with a
+        selection, ``fused_row_block`` rows per pass) and writes no score
+        tensor."""
+        self.fused_select = fused_select
+        self.fused_row_block = fused_row_block
         wl = prob.wl
         assert block_select is None or not wl.block, "block selection replaces the token top-k"
         self.block_select = block_select
@@ -105,6 +110,18 @@ class Step:
                 self.rows, p.q[0], self.k, self.v, None, None, self.o[0], self.lse[0], self.scale,
                 wl.dv))]
             return self._prepared
+        calls = self._fused_index_calls() if self.fused_select else self._index_calls()
+        for c, q in enumerate(p.q):
+            calls.append(("attn_gather_fwd" + ("" if c == 0 else "_%d" % c),
+                          prepare_attn_gather_fwd(self.rows, q, self.k, self.v, self.idx[c],
+                                                  self.count[c], self.o[c], self.lse[c],
+                                                  self.scale, wl.dv)))
+        self._prepared = calls
+        return calls
+
+    def _index_calls(self):
+        """Index calls writing scores, each followed by its selection."""
+        p, wl = self.prob, self.wl
         calls = [("index_score", prepare_index_score(self.rows, p.idx_q[0], p.idx_w[0], self.kidx,
                                                      self.scores[0], skip_k=self.skip_k))]
         if self.block_select is not None:
@@ -125,13 +142,29 @@ class Step:
             calls.append(("topk_select_reindex", prepare_topk_select(
                 self.rows, self.scores[1], wl.k, self.idx[1], self.count[1], cand=self.pool,
                 cand_count=self.pool_count)))
-        for c, q in enumerate(p.q):
-            calls.append(("attn_gather_fwd" + ("" if c == 0 else "_%d" % c),
-                          prepare_attn_gather_fwd(self.rows, q, self.k, self.v, self.idx[c],
-                                                  self.count[c], self.o[c], self.lse[c],
-                                                  self.scale, wl.dv)))
-        self._prepared = calls
         return calls
+
+    def _fused_index_calls(self):
+        """Index and selection in one call per layer (no score tensor)."""
+        p, wl, rb = self.prob, self.wl, self.fused_row_block
+        if self.block_select is not None:
+            bs, nb = self.block_select
+            return [("index_select", prepare_index_select(
+                self.rows, p.idx_q[0], p.idx_w[0], self.kidx, self.S, 0, None, None, block=bs,
+                max_blocks=nb, pool=self.idx[0], pool_count=self.count[0], skip_k=self.skip_k,
+                row_block=rb))]
+        if not wl.block:
+            return [("index_select", prepare_index_select(
+                self.rows, p.idx_q[0], p.idx_w[0], self.kidx, self.S, wl.k, self.idx[0],
+                self.count[0], skip_k=self.skip_k, row_block=rb))]
+        P = wl.max_blocks * wl.block
+        return [("index_select", prepare_index_select(
+                    self.rows, p.idx_q[0], p.idx_w[0], self.kidx, self.S, wl.k, self.idx[0],
+                    self.count[0], block=wl.block, max_blocks=wl.max_blocks, pool=self.pool,
+                    pool_count=self.pool_count, skip_k=self.skip_k, row_block=rb)),
+                ("index_select_reindex", prepare_index_select(
+                    self.rows, p.idx_q[1], p.idx_w[1], self.kidx, P, wl.k, self.idx[1],
+                    self.count[1], cand=self.pool, cand_count=self.pool_count, row_block=rb))]
 
     def run_index(self):
         p, wl = self.prob, self.wl
@@ -194,9 +227,15 @@ class PrefillStep:
     never for every prefill row (section 3.1: a pool materialised for all
     131072 queries would take about 2 GiB)."""
 
-    def __init__(self, prob, row_block: int = 8192, dense_route: bool = False):
+    def __init__(self, prob, row_block: int = 8192, dense_route: bool = False,
+                 fused_select: bool = False, fused_row_block: int = 0):
+        """``fused_select``: each block's index calls select in the same call
+        (sparse_index_score with a selection, ``fused_row_block`` rows per
+        pass inside the call) and write no score tensor."""
         wl = prob.wl
         assert wl.prefill, "prefill workloads"
+        self.fused_select = fused_select
+        self.fused_row_block = fused_row_block
         self.skip_k = wl.k if dense_route and not wl.block else 0
         self.prob = prob
         self.wl = wl
@@ -210,7 +249,8 @@ class PrefillStep:
         self.k = _cache(prob.k, wl.hkv, wl.dqk)
         self.v = _cache(prob.v, wl.hkv, wl.dv) if prob.v is not None else None
         self.S = wl.n_entries_cap
-        self.scores = torch.empty(rb, self.S, dtype=f32, device=dev)
+        # score buffers only without the fused selection
+        self.scores = None if fused_select else torch.empty(rb, self.S, dtype=f32, device=dev)
         self.idx = torch.empty(R, wl.k, dtype=i32, device=dev)
         self.count = torch.empty(R, dtype=i32, device=dev)
         q = prob.q[0]
@@ -221,7 +261,7 @@ class PrefillStep:
             P = wl.max_blocks * wl.block
             self.pool = torch.empty(rb, P, dtype=i32, device=dev)
             self.pool_count = torch.empty(rb, dtype=i32, device=dev)
-            self.scores_r = torch.empty(rb, P, dtype=f32, device=dev)
+            self.scores_r = None if fused_select else torch.empty(rb, P, dtype=f32, device=dev)
             self.idx_r = torch.empty(R, wl.k, dtype=i32, device=dev)
             self.count_r = torch.empty(R, dtype=i32, device=dev)
             q1 = prob.q[1]
@@ -248,9 +288,31 @@ class PrefillStep:
             ws = sel.ws if ws is None or (sel.ws is not None and sel.ws.numel() > ws.numel()) else ws
             calls.append((name, sel))
 
+        def fused(name, *a, **kw):
+            nonlocal ws
+            c = prepare_index_select(*a, workspace=ws, **kw)
+            ws = c.ws if ws is None or (c.ws is not None and c.ws.numel() > ws.numel()) else ws
+            calls.append((name, c))
+
         for lo, hi in self.blocks():
             rows = Rows(p.seq_of_row[lo:hi], p.pos_of_row[lo:hi], p.seq_len, wl.stride, wl.window)
             n = hi - lo
+            if self.fused_select:
+                frb = self.fused_row_block
+                if not wl.block:
+                    fused("index_select", rows, p.idx_q[0][lo:hi], p.idx_w[0][lo:hi], self.kidx,
+                          self.S, wl.k, self.idx[lo:hi], self.count[lo:hi], skip_k=self.skip_k,
+                          row_block=frb)
+                else:
+                    pool, pc = self.pool[:n], self.pool_count[:n]
+                    fused("index_select", rows, p.idx_q[0][lo:hi], p.idx_w[0][lo:hi], self.kidx,
+                          self.S, wl.k, self.idx[lo:hi], self.count[lo:hi], block=wl.block,
+                          max_blocks=wl.max_blocks, pool=pool, pool_count=pc, row_block=frb)
+                    fused("index_select_reindex", rows, p.idx_q[1][lo:hi], p.idx_w[1][lo:hi],
+                          self.kidx, wl.max_blocks * wl.block, wl.k, self.idx_r[lo:hi],
+                          self.count_r[lo:hi], cand=pool, cand_count=pc, row_block=frb)
+                self._attention_calls(calls, rows, lo, hi)
+                continue
             sc = self.scores[:n]
             calls.append(("index_score", prepare_index_score(rows, p.idx_q[0][lo:hi],
                                                              p.idx_w[0][lo:hi], self.kidx, sc,
@@ -267,16 +329,19 @@ class PrefillStep:
                     cand_count=pc)))
                 select("topk_select_reindex", rows, scr, wl.k, self.idx_r[lo:hi],
                        self.count_r[lo:hi], cand=pool, cand_count=pc)
-            calls.append(("attn_gather_fwd", prepare_attn_gather_fwd(
-                rows, p.q[0][:, lo:hi], self.k, self.v, self.idx[lo:hi], self.count[lo:hi],
-                self.o[:, lo:hi], self.lse[:, lo:hi], self.scale, wl.dv)))
-            if wl.block:
-                calls.append(("attn_gather_fwd_1", prepare_attn_gather_fwd(
-                    rows, p.q[1][:, lo:hi], self.k, self.v, self.idx_r[lo:hi],
-                    self.count_r[lo:hi], self.o_r[:, lo:hi], self.lse_r[:, lo:hi], self.scale,
-                    wl.dv)))
+            self._attention_calls(calls, rows, lo, hi)
         self._prepared = calls
         return calls
+
+    def _attention_calls(self, calls, rows, lo, hi):
+        p, wl = self.prob, self.wl
+        calls.append(("attn_gather_fwd", prepare_attn_gather_fwd(
+            rows, p.q[0][:, lo:hi], self.k, self.v, self.idx[lo:hi], self.count[lo:hi],
+            self.o[:, lo:hi], self.lse[:, lo:hi], self.scale, wl.dv)))
+        if wl.block:
+            calls.append(("attn_gather_fwd_1", prepare_attn_gather_fwd(
+                rows, p.q[1][:, lo:hi], self.k, self.v, self.idx_r[lo:hi], self.count_r[lo:hi],
+                self.o_r[:, lo:hi], self.lse_r[:, lo:hi], self.scale, wl.dv)))
 
     def run(self):
         for _, c in self.prepare():

@@ -53,7 +53,7 @@ def test_peak_probes_reject_bad_arguments(lib):
 
 def test_abi_version(lib):
     v = ira.abi_version()
-    assert v >> 16 == 2 and v & 0xFFFF == 1
+    assert v >> 16 == 3 and v & 0xFFFF == 1
 
 
 def test_struct_layout_matches_c_compiler(tmp_path):
@@ -91,7 +91,8 @@ def _status(fn, desc):
 
 def test_index_score_validation(lib):
     k = B.sa_cache(0x10000, None, None, 64, 8, 1, 64, 128, 0, B.SA_BF16, 0)
-    d = B.sa_index_desc(_rows(), 0x20000, 0x30000, k, 16, 64, None, None, 0, 0, 0x40000, 4096)
+    d = B.sa_index_desc(_rows(), 0x20000, 0x30000, k, 16, 64, None, None, 0, 0, 0x40000, 4096,
+                        None, 0, 0)
     bad = B.sa_index_desc.from_buffer_copy(d)
     bad.scores = None
     assert _status(lib.sparse_index_score, bad) == -1
@@ -112,6 +113,35 @@ def test_index_score_validation(lib):
     bad.rows.stride = 0
     assert _status(lib.sparse_index_score, bad) == -2
     assert lib.sa_workspace_size(B.SA_OP_INDEX_SCORE, ctypes.byref(d)) == 0
+
+
+def test_index_score_fused_selection_validation(lib):
+    """The fused selection: scores may be NULL, the workspace holds one pass
+    of rows' scores plus the selection's workspace, and the selection's
+    descriptor is validated like sparse_topk_select's."""
+    k = B.sa_cache(0x10000, None, None, 64, 8, 1, 64, 128, 0, B.SA_BF16, 0)
+    d = B.sa_index_desc(_rows(), 0x20000, 0x30000, k, 16, 64, None, None, 0, 0, None, 4096,
+                        None, 0, 0)
+    assert _status(lib.sparse_index_score, d) == -1  # neither scores nor sel
+    sel = B.sa_topk_desc(_rows(), None, 0, None, None, 0, 8, 0x50000, 0x60000, 8, 0, 0, 0, None,
+                         None)
+    d.sel = ctypes.addressof(sel)
+    size = lambda: lib.sa_workspace_size(B.SA_OP_INDEX_SCORE, ctypes.byref(d))
+    whole = size()
+    assert whole >= 4 * 4096 * 4 and whole != ctypes.c_size_t(-1).value
+    d.row_block = 2
+    half = size()
+    assert 2 * 4096 * 4 <= half < whole
+    assert _status(lib.sparse_index_score, d) == -5  # no workspace given
+    d.row_block = -1
+    assert _status(lib.sparse_index_score, d) == -2
+    d.row_block = 0
+    d.reserved = 1
+    assert _status(lib.sparse_index_score, d) == -2
+    d.reserved = 0
+    sel.idx_stride = 4  # below k
+    assert size() == ctypes.c_size_t(-1).value
+    assert b"idx_stride < k" in lib.sa_last_error()
 
 
 def test_topk_validation(lib):
