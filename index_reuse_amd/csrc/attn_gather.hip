@@ -787,21 +787,22 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
   }
 }
 
-// ---------------------------------------------------------- latent prefill
-// The latent shape of prefill: one 576-wide row per entry serves as K, its
-// first 512 channels as V, with 64 query rows per workgroup (4 waves, one
-// per SIMD; RT = 4 row tiles of 16).  Wave w = (hh, dh), hh = w & 1,
-// dh = w >> 1:
+// ------------------------------------------------------- FP4 rows, 4 waves
+// FP4 rows (one 512-channel row per entry as K and V, E2M1 codes with E4M3
+// scales) with 64 query rows per workgroup (4 waves, one per SIMD; RT = 4
+// row tiles of 16).  The rows are decoded to bf16 in registers on their way
+// into LDS, so they cannot be loaded straight to LDS as attn_mla8 does for
+// bf16 rows.  Wave w = (hh, dh), hh = w & 1, dh = w >> 1:
 //   - S: partial logits of row tiles {2 hh, 2 hh + 1} over k-steps
-//     [9 dh, 9 dh + 9) of the 18; every K fragment read from LDS feeds both
-//     row tiles;
+//     [KH dh, KH dh + KH); every K fragment read from LDS feeds both row
+//     tiles;
 //   - the two dim halves hand each other the partials of one row tile
 //     through LDS; wave w then finishes row tile 2 hh + dh: mask, softmax,
 //     and its probabilities (bf16) into LDS;
 //   - O: channels [128 w, 128 w + 128) of all four row tiles, so each V
 //     channel block is read from LDS by one wave.
-// Per 32-entry tile a wave reads 18 KB of K, 8 KB of V and 4 KB of P from
-// LDS, against 68 KB of K and V when a wave owns one row tile outright.
+// Per 32-entry tile a wave reads 16 KB of K, 8 KB of V and 4 KB of P from
+// LDS, against 64 KB of K and V when a wave owns one row tile outright.
 // (Two row tiles per workgroup with one K buffer, two workgroups per CU, ran
 // 15% slower: each K fragment then feeds one MFMA, with four barriers per
 // tile.)
@@ -832,11 +833,11 @@ __device__ __forceinline__ void mla_unit(int n_units, int Z, int& unit, int& z) 
   if (unit >= n_units) unit = -1;
 }
 
-// DQK = 576 (latent rows, V = the first 512 channels) or 512 (one row as K
-// and V); KV = KV_SHARED (bf16 rows) or KV_FP4 (E2M1 codes with E4M3 scales,
-// decoded exactly to bf16 on the way into LDS).
+// DQK = 512; KV = KV_FP4 (E2M1 codes with E4M3 scales, decoded exactly to
+// bf16 on the way into LDS).
 template <int DQK, int KV>
 __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, int n_units, int Z) {
+  static_assert(KV == KV_FP4, "bf16 rows take attn_mla8");
   constexpr int NTH = 256, DV = kMlaDv, RT = kMlaRT, D = kMlaD;
   constexpr int KH = DQK / 64;      // k-steps per dim half
   constexpr int HT = 2;             // row tiles in this wave's S
@@ -892,15 +893,10 @@ __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, in
       const int e = c / T::CPR_K, part = c % T::CPR_K;
       const int sv = lds.slot[s * kTile + e];
       const uint32_t slot = sv >= 0 ? (uint32_t)sv : dummy;
-      if constexpr (T::FP4) {
-        regs.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            a.k.data + (uint64_t)slot * (uint32_t)a.k.row_stride + g * (DQK / 2) + part * 16));
-        regs.sc[u] = *reinterpret_cast<const uint16_t*>(
-            a.k.scale + (uint64_t)slot * (uint32_t)a.k.scale_stride + g * (DQK / 16) + part * 2);
-      } else {
-        regs.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            a.k.data + (uint64_t)slot * (uint32_t)a.k.row_stride + g * (DQK * 2) + part * 16));
-      }
+      regs.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          a.k.data + (uint64_t)slot * (uint32_t)a.k.row_stride + g * (DQK / 2) + part * 16));
+      regs.sc[u] = *reinterpret_cast<const uint16_t*>(
+          a.k.scale + (uint64_t)slot * (uint32_t)a.k.scale_stride + g * (DQK / 16) + part * 2);
     }
   };
   auto store_step = [&](const T& regs, int sb) {
@@ -908,17 +904,13 @@ __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, in
     for (int u = 0; u < T::U; ++u) {
       const int c = tid + NTH * u;
       const int e = c / T::CPR_K, part = c % T::CPR_K;
-      if constexpr (T::FP4) {
-        // 16 code bytes = 32 channels, decoded exactly to bf16
-        uint32_t vals[16];
-        fp4_dequant32(regs.v[u], regs.sc[u] & 0xFFu, regs.sc[u] >> 8, vals);
-        u32x4* dst = reinterpret_cast<u32x4*>(&lds.k[sb][e * L::KROW + part * 32]);
+      // 16 code bytes = 32 channels, decoded exactly to bf16
+      uint32_t vals[16];
+      fp4_dequant32(regs.v[u], regs.sc[u] & 0xFFu, regs.sc[u] >> 8, vals);
+      u32x4* dst = reinterpret_cast<u32x4*>(&lds.k[sb][e * L::KROW + part * 32]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dst[i] = u32x4{vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]};
-      } else {
-        *reinterpret_cast<u32x4*>(&lds.k[sb][e * L::KROW + part * 8]) = regs.v[u];
-      }
+      for (int i = 0; i < 4; ++i)
+        dst[i] = u32x4{vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]};
     }
   };
 
@@ -1745,8 +1737,9 @@ hipError_t launch_attn_gather(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   // Rows of 512 or more channels with at least 64 query rows per KV head:
-  // the kernel that splits S by channel halves and O by channel quarters
-  // across its waves, so each K fragment read from LDS feeds two MFMAs.
+  // the kernels that split S by channel halves across their waves, so each
+  // K fragment read from LDS feeds two MFMAs (attn_mla8 for bf16 rows,
+  // attn_mla for FP4 rows).
   const bool many_rows = a.n_qsets * (a.hq / a.hkv) >= 16 * kMlaRT;
   if (a.kv_kind == KV_SEPARATE) {
     if (a.dqk == 128 && a.dv == 128) return launch_shaped<128, 128, KV_SEPARATE, 2>(a, s);
