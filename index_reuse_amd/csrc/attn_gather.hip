@@ -1461,6 +1461,7 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
 // lane i < n_split holds split i's (m, l, lx) and its weight; every lane then
 // sums 4 consecutive channels per 256-channel block over the splits with
 // 16-byte loads.
+template <int KS>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -1468,11 +1469,12 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   if (row >= nrows) return;
   const int DV = a.dv, ns = a.n_split;
   const float* ml = a.part + (int64_t)ns * nrows * DV;
-  // Up to 8 splits of 512 channels: every partial load is issued before the
-  // split weights are known (one memory round trip instead of two).  Splits
-  // past ns re-read split 0 and get weight 0.
-  constexpr int kS = 8;
-  const bool pre = ns <= kS && DV == 512;
+  // KS > 0 (at most KS splits of 512 channels): every partial load is issued
+  // before the split weights are known (one memory round trip instead of
+  // several).  Splits past ns re-read split 0 and get weight 0.  KS = 0: a
+  // loop over the splits for any count and width.
+  constexpr int kS = KS > 0 ? KS : 1;
+  constexpr bool pre = KS > 0;
   f32x4 v[kS][2];
   if (pre) {
 #pragma unroll
@@ -1639,6 +1641,18 @@ AttnShape attn_shape(const AttnArgs& a) {
   return {4, 2};
 }
 
+// The merge of split partials: all of a row's partial loads at once when the
+// splits of 512 channels fit the registers (up to 16), else a loop.
+void launch_combine(const AttnArgs& a, int64_t nrows, hipStream_t s) {
+  const dim3 grid((unsigned)((nrows + 3) / 4)), block(256);
+  if (a.dv == 512 && a.n_split <= 8)
+    hipLaunchKernelGGL(attn_combine<8>, grid, block, 0, s, a);
+  else if (a.dv == 512 && a.n_split <= 16)
+    hipLaunchKernelGGL(attn_combine<16>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_combine<0>, grid, block, 0, s, a);
+}
+
 template <int DQK, int DV, int KV, int W, int NG, int D>
 hipError_t launch_mfma_attn(const AttnArgs& a, hipStream_t s) {
   const int G = a.hq / a.hkv;
@@ -1650,7 +1664,7 @@ hipError_t launch_mfma_attn(const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const int64_t nrows = (int64_t)a.n_qsets * a.rows.n_rows * a.hq;
-  hipLaunchKernelGGL(attn_combine, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, a);
+  launch_combine(a, nrows, s);
   return hipGetLastError();
 }
 
@@ -1666,7 +1680,7 @@ hipError_t launch_mla(const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const int64_t nrows = (int64_t)a.n_qsets * a.rows.n_rows * a.hq;
-  hipLaunchKernelGGL(attn_combine, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, a);
+  launch_combine(a, nrows, s);
   return hipGetLastError();
 }
 
@@ -1681,7 +1695,7 @@ hipError_t launch_mla8(const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const int64_t nrows = (int64_t)a.n_qsets * a.rows.n_rows * a.hq;
-  hipLaunchKernelGGL(attn_combine, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, a);
+  launch_combine(a, nrows, s);
   return hipGetLastError();
 }
 
