@@ -654,7 +654,7 @@ def _same_rows(gi, gc, oi, oc):
             if gc[r] == oc[r] and np.array_equal(gi[r, :gc[r]], oi[r, :oc[r]])]
 
 
-def _spread(rows, n=4):
+def _spread(rows, n=16):
     if len(rows) <= n:
         return list(rows)
     return [rows[int(round(i * (len(rows) - 1) / (n - 1)))] for i in range(n)]
