@@ -791,7 +791,7 @@ __global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_
 // FP4 rows (one 512-channel row per entry as K and V, E2M1 codes with E4M3
 // scales) with 64 query rows per workgroup (4 waves, one per SIMD; RT = 4
 // row tiles of 16).  The rows are decoded to bf16 in registers on their way
-// into LDS, so they cannot be loaded straight to LDS as attn_mla8 does for
+// into LDS, so they cannot be loaded straight to LDS as attn_mla_ws does for
 // bf16 rows.  Wave w = (hh, dh), hh = w & 1, dh = w >> 1:
 //   - S: partial logits of row tiles {2 hh, 2 hh + 1} over k-steps
 //     [KH dh, KH dh + KH); every K fragment read from LDS feeds both row
@@ -837,7 +837,7 @@ __device__ __forceinline__ void mla_unit(int n_units, int Z, int& unit, int& z) 
 // bf16 on the way into LDS).
 template <int DQK, int KV>
 __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, int n_units, int Z) {
-  static_assert(KV == KV_FP4, "bf16 rows take attn_mla8");
+  static_assert(KV == KV_FP4, "bf16 rows take attn_mla_ws");
   constexpr int NTH = 256, DV = kMlaDv, RT = kMlaRT, D = kMlaD;
   constexpr int KH = DQK / 64;      // k-steps per dim half
   constexpr int HT = 2;             // row tiles in this wave's S
@@ -1088,40 +1088,7 @@ __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, in
   }
 }
 
-// ------------------------------------------- latent prefill, eight waves
-// The same work as attn_mla (64 query rows of one KV head per workgroup, one
-// 576- or 512-wide bf16 row per entry, V its first 512 channels), on eight
-// waves, two per SIMD, so that one wave's LDS and MFMA latency hides behind
-// the other's work.  Wave w = (hp, dh, mh) = (w & 1, (w >> 1) & 1, w >> 2):
-//   - S: partial logits of row tiles {2 hp, 2 hp + 1} over the entries of
-//     half mh of the 32-entry tile (16 entries) and the k-steps of dim half
-//     dh; each K fragment read from LDS feeds two MFMAs;
-//   - the dim halves swap one row tile's partials through LDS; wave w then
-//     finishes row tile 2 hp + dh over entry half mh (mask, softmax) and
-//     writes its probabilities into its half of the tile's P^T operand;
-//   - O: channels [64 w, 64 w + 64) of all four row tiles.
-// The two entry halves of a row tile share one reference max, taken once
-// (the first tile with an entry) through LDS, and add their probability
-// sums at the end.
-// Tiles come from HBM straight into LDS with gfx950's 16-byte load-to-LDS
-// (no register staging), two tiles ahead, into three buffers that are
-// separate LDS arrays, so the compiler can tell a tile's reads from the
-// loads into the other buffers and count the loads still in flight.  Each
-// load instruction fills 1 KB of consecutive LDS; rows are laid out as in
-// attn_mla, 16 bytes longer than the data (the lanes that land on a row's
-// pad load the row's first piece again), which keeps the MFMA-layout reads
-// of K free of bank conflicts.
-template <int DQK>
-struct Mla8Lds {
-  static constexpr int SLOTS = kMaxEntries + 3 * kTile;
-  float sx[8][4][64];           // S partials handed to the other dim half
-  u32x4 p[kMlaRT][64];          // P^T operand of each row tile: 8 bytes per entry half
-  float mx[8][16];              // row max of a wave's entry half
-  float ml[kMlaRT][2][16][3];   // per row tile and entry half: m, rounded and unrounded sums
-  int32_t wfirst[8];
-  int32_t slot[SLOTS];
-};
-
+// ---------------------------------------- load-to-LDS helpers (gfx950)
 typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
@@ -1139,18 +1106,52 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// ------------------------------- latent prefill, waves specialised by phase
+// The tiling of attn_mla (64 query rows of one KV head per workgroup) for
+// bf16 rows: one 576- or 512-wide row per entry, V its first 512 channels,
+// on eight waves, two per SIMD, split by role so that the two waves of a
+// SIMD are in different phases and one's VALU and LDS work overlaps the
+// other's MFMAs:
+//   - S waves a = 0..3, (hp, dh) = (a & 1, a >> 1): partial logits of row
+//     tiles {2 hp, 2 hp + 1} over all 32 entries and the k-steps of channel
+//     half dh (every K fragment read from LDS feeds two MFMAs); the halves
+//     swap one row tile's partials through LDS, and wave a finishes row tile
+//     2 hp + dh: mask, softmax, its P^T operand.  A wave owns whole rows of
+//     the tile, so the reference max needs no exchange between waves.
+//   - O waves b = 0..3: channels [128 b, 128 b + 128) of all four row tiles,
+//     and every load of the tiles.
+// Two barriers per tile.  Before the first, tile s's logits (S waves)
+// overlap the reads of tile s - 1's P^T and V (O waves); after it, tile s's
+// softmax (S waves) overlaps tile s - 1's O MFMAs, which run from
+// registers, and the loads of tile s + 2 into the buffer tile s - 1 has just
+// left, which go out among those MFMAs.
+// Tiles come from HBM straight into LDS with gfx950's 16-byte load-to-LDS
+// (no register staging), two tiles ahead, into three buffers that are
+// separate LDS arrays, so the compiler can tell a tile's reads from the
+// loads into the other buffers and count the loads still in flight.  Each
+// load instruction fills 1 KB of consecutive LDS; rows are laid out 16 bytes
+// longer than the data (the lanes that land on a row's pad load the row's
+// first piece again), which keeps the MFMA-layout reads of K and the
+// transposed reads of V free of bank conflicts.
 template <int DQK>
-__global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, int n_units, int Z) {
+struct MlaWsLds {
+  static constexpr int SLOTS = kMaxEntries + 3 * kTile;
+  float sx[4][8][64];         // S partials handed to the other channel half
+  u32x4 p[kMlaRT][64];        // P^T operand of each row tile
+  float ml[kMlaRT][16][3];    // per row tile: m, rounded and unrounded sums
+  int32_t wfirst[8];
+  int32_t slot[SLOTS];
+};
+
+template <int DQK>
+__global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split, int n_units, int Z) {
   constexpr int NTH = 512, DV = kMlaDv, RT = kMlaRT;
-  constexpr int P = DQK / 8;               // 16-byte pieces per row
-  constexpr int PP = P + 1;                // with the pad
-  constexpr int KH = DQK / 64;             // k-steps per dim half
-  // 1 KB loads per tile, the same number for every wave (the loads past the
-  // tile's last row fill slack that nothing reads), so that one wait count
-  // leaves exactly the newest tile's loads in flight in every wave
-  constexpr int JW = (kTile * PP + 511) / 512;
-  constexpr int NJ = 8 * JW;
-  using L = Mla8Lds<DQK>;
+  constexpr int P = DQK / 8;                  // 16-byte pieces per row
+  constexpr int PP = P + 1;                   // with the pad
+  constexpr int KH = DQK / 64;                // k-steps per channel half
+  constexpr int JA = (kTile * PP + 255) / 256;  // 1 KB loads per O wave per tile
+  constexpr int NJ = 4 * JA;
+  using L = MlaWsLds<DQK>;
   static_assert(sizeof(L) + 3 * NJ * 1024 <= 160 * 1024, "LDS budget");
   __shared__ __align__(16) L lds;
   __shared__ __align__(16) u32x4 kb0[NJ * 64];
@@ -1159,10 +1160,6 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar
   const int col = lane & 15, gq = lane >> 4;
-  const int hp = wave & 1, dh = (wave >> 1) & 1, mh = wave >> 2;
-  const int own = 2 * hp + dh;   // row tile whose entry half mh this wave finishes
-  const int partner = wave ^ 2;  // same row tiles and entry half, other dim half
-  const int twin = wave ^ 4;     // same row tile, other entry half
   int unit, zg;
   mla_unit(n_units, Z, unit, zg);
   if (unit < 0) return;
@@ -1173,280 +1170,316 @@ __global__ __launch_bounds__(512, 1) void attn_mla8(AttnArgs a, int per_split, i
   const int Mq = a.n_qsets * G;
   const int qrow0 = zg * 16 * RT;
 
-  // this wave's S row tiles, k-steps [KH dh, KH dh + KH), as B operands:
-  // [0] the tile it finishes (own), [1] the one its partner finishes
-  u32x4 qv[2][KH];
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const int qr = qrow0 + 16 * (ht == 0 ? own : own ^ 1) + col;
-    if (qr < Mq) {
-      const int set = qr / G, h = g * G + qr % G;
-      const u32x4* qp = reinterpret_cast<const u32x4*>(
-          reinterpret_cast<const uint16_t*>(a.q) +
-          (((int64_t)set * a.rows.n_rows + r) * a.hq + h) * DQK + gq * (DQK / 4));
-#pragma unroll
-      for (int i = 0; i < KH; ++i) qv[ht][i] = qp[KH * dh + i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < KH; ++i) qv[ht][i] = u32x4{0, 0, 0, 0};
-    }
-  }
   int sel_pre[kPT];
   issue_index_loads<NTH>(a, r, sp * per_split, sel_pre);
   const RowInfo ri = row_info(a.rows, r);
   // two tiles read ahead: the table covers tiles up to nsteps + 1
   const RangeTable rt = build_range_table<NTH, 1, 2>(a, r, sp * per_split, per_split, ri, sel_pre,
                                                      lds.slot, lds.wfirst);
-  const int nsteps_run = rt.nsteps_run;
+  const int n = rt.nsteps_run;
+  constexpr float kHeadroom = 64.0f;
+
+  if (wave < 4) {
+    // ------------------------------------------------------------ S waves
+    const int hp = wave & 1, dh = wave >> 1;
+    const int own = 2 * hp + dh;   // row tile this wave finishes
+    const int partner = wave ^ 2;  // same row tiles, other channel half
+    u32x4 qv[2][KH];  // [0] row tile own, [1] own ^ 1; k-steps [KH dh, KH dh + KH)
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const int qr = qrow0 + 16 * (ht == 0 ? own : own ^ 1) + col;
+      if (qr < Mq) {
+        const int set = qr / G, h = g * G + qr % G;
+        const u32x4* qp = reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const uint16_t*>(a.q) +
+            (((int64_t)set * a.rows.n_rows + r) * a.hq + h) * DQK + gq * (DQK / 4));
+#pragma unroll
+        for (int i = 0; i < KH; ++i) qv[ht][i] = qp[KH * dh + i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < KH; ++i) qv[ht][i] = u32x4{0, 0, 0, 0};
+      }
+    }
+
+    // softmax state of row tile `own` (lane col), per lane over its entries;
+    // m_run is fixed by the first tile with an entry (see attn_mfma)
+    float m_run = -__builtin_huge_valf(), m_top = -__builtin_huge_valf();
+    float l_run = 0.0f, l_lse = 0.0f;
+    bool m_set = false;
+
+    auto body = [&](int s, const u32x4* cur) __attribute__((always_inline)) {
+      // S^T partials [ht][mt]: entries 16 mt + (M), query rows of tile ht (N)
+      f32x4 acc[2][2];
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) acc[ht][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const u32x4* krow = cur + (16 * mt + col) * PP + gq * (P / 4) + KH * dh;
+#pragma unroll
+        for (int i = 0; i < KH; ++i) {
+          const u32x4 av = krow[i];
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht)
+            acc[ht][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, qv[ht][i]), acc[ht][mt], 0,
+                0, 0);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds.sx[wave][4 * mt + i][lane] = acc[1][mt][i];
+      // every logit MFMA before the barrier: after it the O waves' MFMAs run
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();  // (1) the partials
+      float x[2][4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[mt][i] = acc[0][mt][i] + lds.sx[partner][4 * mt + i][lane];
+      // keeps the reads out of a branch on the mask
+      asm volatile("" : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[1][0]),
+                   "+v"(x[1][1]), "+v"(x[1][2]), "+v"(x[1][3]));
+      // which of the tile's 32 entries are real: bit e (and e + 32) of the
+      // ballot over lanes e = lane & 31
+      const uint64_t valid = __builtin_amdgcn_ballot_w64(lds.slot[s * kTile + (lane & 31)] >= 0);
+      // mask and scale: lane holds entries 16 mt + 4 gq + i for query row col
+      float tmax = -__builtin_huge_valf();
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = (valid >> (16 * mt + 4 * gq + i)) & 1;
+          x[mt][i] = ok ? x[mt][i] * a.scale_log2 : -__builtin_huge_valf();
+          tmax = fmaxf(tmax, x[mt][i]);
+        }
+      }
+      m_top = fmaxf(m_top, tmax);
+      // the first tile with an entry (the same in every lane) fixes the
+      // reference
+      if (!m_set && valid != 0) {
+        m_run = xor16_32_max(tmax);
+        m_set = true;
+      }
+      const float m_use = m_run == -__builtin_huge_valf() ? 0.0f : m_run;
+      float pr[2][4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[mt][i] = fast_exp2(x[mt][i] - m_use);
+      // P^T as the B operand: k-slot 8 gq + i <-> entry (i < 4 ? 4 gq + i : 16 + 4 gq + i - 4)
+      u32x4 pa;
+      pa[0] = pack_bf16x2(pr[0][0], pr[0][1]);
+      pa[1] = pack_bf16x2(pr[0][2], pr[0][3]);
+      pa[2] = pack_bf16x2(pr[1][0], pr[1][1]);
+      pa[3] = pack_bf16x2(pr[1][2], pr[1][3]);
+      float psum = 0.0f, xsum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        psum += __uint_as_float(pa[i] << 16) + __uint_as_float(pa[i] & 0xFFFF0000u);
+        xsum += pr[i >> 1][2 * (i & 1)] + pr[i >> 1][2 * (i & 1) + 1];
+      }
+      l_run += psum;
+      l_lse += xsum;
+      lds.p[own][lane] = pa;
+      lds_barrier();  // (2) P^T of tile s; tile s + 1 has landed
+    };
+
+    for (int pass = 0; pass < 2; ++pass) {
+      lds_barrier();  // tiles 0 and 1 have landed
+      int s = 0;
+#pragma unroll 1
+      for (; s + 3 <= n; s += 3) {
+        body(s, kb0);
+        body(s + 1, kb1);
+        body(s + 2, kb2);
+      }
+      if (s < n) body(s, kb0);
+      if (s + 1 < n) body(s + 1, kb1);
+      if (n > 0) {
+        // the O waves' last tile
+        lds_barrier();
+        lds_barrier();
+      }
+      const float m_row = xor16_32_max(m_top);
+      if (!__syncthreads_or(m_top > m_run + kHeadroom)) break;
+      m_run = m_row;
+      m_set = true;
+      l_run = 0.0f;
+      l_lse = 0.0f;
+    }
+    l_run = xor16_32_sum(l_run);
+    l_lse = xor16_32_sum(l_lse);
+    if (gq == 0) {
+      lds.ml[own][col][0] = m_run;
+      lds.ml[own][col][1] = l_run;
+      lds.ml[own][col][2] = l_lse;
+    }
+    __syncthreads();
+    return;
+  }
+
+  // -------------------------------------------------------------- O waves
+  const int b = wave - 4;
   const uint32_t dummy = rt.dummy;
   const char* kbase = reinterpret_cast<const char*>(a.k.data) + (size_t)g * (DQK * 2);
   const uint32_t rstride = (uint32_t)a.k.row_stride;
-
-  // Tile s into buf: load J = wave + 8 j fills LDS pieces f = 64 J + lane,
+  // Tile s into buf: load J = b + 4 j fills LDS pieces f = 64 J + lane,
   // piece f % PP of row f / PP (the pad and the lanes past the last row load
-  // a valid piece that nothing reads).  The addresses are worked out ahead
-  // of the issue (tile_addr), so that the table reads and the arithmetic
-  // overlap other work.
-  int drow[JW], doff[JW];
+  // a valid piece that nothing reads); every O wave issues JA loads a tile,
+  // so one wait count leaves exactly the newest tile in flight.
+  int dlin[JA];  // row f / PP in the low 8 bits, byte offset in the row above
 #pragma unroll
-  for (int j = 0; j < JW; ++j) {
-    const int f = 64 * (wave + 8 * j) + lane;
+  for (int j = 0; j < JA; ++j) {
+    const int f = 64 * (b + 4 * j) + lane;
     const int ps = f % PP;
-    drow[j] = min(f / PP, kTile - 1);
-    doff[j] = (ps < P ? ps : 0) * 16;
+    dlin[j] = min(f / PP, kTile - 1) | ((ps < P ? ps : 0) * 16) << 8;
   }
+  // The slots of a tile's rows are read ahead (tile_addr); the 64-bit
+  // addresses are formed at the issue.
   struct TileAddr {
-    const char* p[JW];
+    uint32_t slot[JA];
   };
   auto tile_addr = [&](int s) __attribute__((always_inline)) {
     TileAddr ta;
-    int sv[JW];
+    int sv[JA];
 #pragma unroll
-    for (int j = 0; j < JW; ++j) sv[j] = lds.slot[s * kTile + drow[j]];
+    for (int j = 0; j < JA; ++j) sv[j] = lds.slot[s * kTile + (dlin[j] & 0xFF)];
 #pragma unroll
-    for (int j = 0; j < JW; ++j) {
-      const uint32_t slot = sv[j] >= 0 ? (uint32_t)sv[j] : dummy;
-      ta.p[j] = kbase + (uint64_t)slot * rstride + doff[j];
-    }
+    for (int j = 0; j < JA; ++j) ta.slot[j] = sv[j] >= 0 ? (uint32_t)sv[j] : dummy;
     return ta;
   };
-  auto issue_tile = [&](const TileAddr& ta, u32x4* buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < JW; ++j)
-      __builtin_amdgcn_global_load_lds((gptr_t)ta.p[j], (lptr_t)(buf + 64 * (wave + 8 * j)), 16, 0, 0);
+  auto issue_load = [&](const TileAddr& ta, u32x4* buf, int j) __attribute__((always_inline)) {
+    const char* src = kbase + (uint64_t)ta.slot[j] * rstride + (uint32_t)(dlin[j] >> 8);
+    __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(buf + 64 * (b + 4 * j)), 16, 0, 0);
   };
-  // Wait until only the loads of the last tile issued are in flight (the
-  // empty asm keeps the compiler from sinking those loads below the wait).
+  // wait until only the loads of the last tile issued are in flight (the
+  // empty asm keeps the compiler from sinking those loads below the wait)
   auto wait_all_but_last = [&]() __attribute__((always_inline)) {
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(JW));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(JA));
   };
 
-  // Softmax state of row tile `own` over entry half mh (lane col): the
-  // reference m_run is fixed by the first tile with an entry; a second pass
-  // runs with the true max if some logit exceeds it by more than kHeadroom.
-  // m_top and the two sums are kept per lane (over the lane's entries) and
-  // reduced over the row's four lanes once, at the end of a pass.
-  constexpr float kHeadroom = 64.0f;
-  f32x4 O[RT][4];  // [row tile][t]: lane element i is channel 64 w + 16 gq + 4 (t ^ (gq & 1)) + i
-  float m_run = -__builtin_huge_valf(), m_top = -__builtin_huge_valf();
-  float l_run = 0.0f, l_lse = 0.0f;
-  bool m_set = false;
-
+  f32x4 O[RT][8];  // [row tile][t]: lane element i is channel 128 b + 32 gq + 4 t + i
   // Transpose-read addressing of V (see attn_mfma): lane 4 jj + q of k-group
-  // gq fetches channels [64 w + 16 q + 4 (t ^ (q & 1)), +4) of entry
-  // 4 gq + jj (then 16 + 4 gq + jj).  With the padded rows, alternating t
-  // between the q groups puts the 16 lanes of a block on distinct banks.
+  // gq fetches channels [128 b + 32 q + 4 t, +4) of entry 4 gq + jj (then
+  // 16 + 4 gq + jj).  With rows PP pieces apart, the 16 lanes of a k-group
+  // fall on distinct banks, and the eight t differ by an immediate offset.
   const int vq = lane & 3;
-  const int voff = (4 * gq + ((lane >> 2) & 3)) * (PP * 8) + 64 * wave + 16 * vq + 4 * (vq & 1);
-
-  // The O update of channel blocks t >= TD of a tile waits in registers (its
-  // P^T operands and V fragments) and runs in the next tile's softmax phase,
-  // where the matrix pipe has nothing else to do.  (Deferring all four
-  // blocks made the loop spill.)
-  bf16x8 pd[RT];
-  constexpr int TD = 1;  // first deferred channel block
-  s16x8 vd[4 - TD];
-  auto deferred_o = [&]() __attribute__((always_inline)) {
+  const int voff = (4 * gq + ((lane >> 2) & 3)) * (PP * 8) + 128 * b + 32 * vq;
+  // Tile s: O update of tile s - 1 from buf, which then takes tile s + 2
+  // (the table ends at tile n + 1: the last pass reloads that one).
+  auto obody = [&](int s, u32x4* buf) __attribute__((always_inline)) {
+    const TileAddr ta = tile_addr(min(s + 2, n + 1));
+    bf16x8 pb[RT];
 #pragma unroll
-    for (int t = TD; t < 4; ++t)
+    for (int q = 0; q < RT; ++q) pb[q] = __builtin_bit_cast(bf16x8, lds.p[q][lane]);
+    const uint16_t* kb = reinterpret_cast<const uint16_t*>(buf);
+    s16x8 vf[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const s16x4 lo = lds_read_tr16(kb + voff + 4 * t);
+      const s16x4 hi = lds_read_tr16(kb + voff + 4 * t + 16 * PP * 8);
+      vf[t] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    lds_barrier();  // (1) every wave is past its reads of buf
+    // the MFMAs run between the two barriers, while the S waves do their
+    // softmax (the scheduling barriers keep the compiler from moving them
+    // across either barrier); the loads go out among them
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
 #pragma unroll
       for (int q = 0; q < RT; ++q)
-        O[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vd[t - TD]), pd[q],
+        O[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[t]), pb[q],
                                                           O[q][t], 0, 0, 0);
-  };
-
-  auto body = [&](int s, const u32x4* cur, u32x4* nx2) __attribute__((always_inline)) {
-    const TileAddr ta = tile_addr(s + 2);
-    // S^T partials [ht]: entries 16 mh + (M), query rows of tile own (ht 0)
-    // and own ^ 1 (ht 1) (N)
-    f32x4 acc[2];
-    acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      const u32x4* krow = cur + (16 * mh + col) * PP + gq * (P / 4) + KH * dh;
-#pragma unroll
-      for (int i = 0; i < KH; ++i) {
-        const u32x4 av = krow[i];
-#pragma unroll
-        for (int ht = 0; ht < 2; ++ht)
-          acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, qv[ht][i]), acc[ht], 0, 0, 0);
-      }
+      if (t < JA) issue_load(ta, buf, t);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds.sx[wave][i][lane] = acc[1][i];
-    lds_barrier();
-    // every wave is past tile s - 1's O phase: its buffer takes tile s + 2
-    issue_tile(ta, nx2);
-    deferred_o();
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = acc[0][i] + lds.sx[partner][i][lane];
-    // mask and scale: lane holds entries 16 mh + 4 gq + i for query row col
-    const i32x4 sl = *reinterpret_cast<const i32x4*>(&lds.slot[s * kTile + 16 * mh + 4 * gq]);
-    float tmax = -__builtin_huge_valf();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = sl[i] >= 0 ? x[i] * a.scale_log2 : -__builtin_huge_valf();
-      tmax = fmaxf(tmax, x[i]);
-    }
-    m_top = fmaxf(m_top, tmax);
-    if (!m_set) {
-      // whether the tile has an entry is read from the slot table, so every
-      // wave takes the same branch
-      const i32x4 so = *reinterpret_cast<const i32x4*>(&lds.slot[s * kTile + 16 * (1 - mh) + 4 * gq]);
-      const bool any = (sl[0] >= 0) | (sl[1] >= 0) | (sl[2] >= 0) | (sl[3] >= 0) | (so[0] >= 0) |
-                       (so[1] >= 0) | (so[2] >= 0) | (so[3] >= 0);
-      if (__builtin_amdgcn_ballot_w64(any) != 0) {
-        tmax = xor16_32_max(tmax);
-        if (gq == 0) lds.mx[wave][col] = tmax;
-        lds_barrier();
-        m_run = fmaxf(tmax, lds.mx[twin][col]);
-        m_set = true;
-      }
-    }
-    const float m_use = m_run == -__builtin_huge_valf() ? 0.0f : m_run;
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(x[i] - m_use);
-    const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
-    const float psum = (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u)) +
-                       (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xFFFF0000u));
-    const float xsum = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    l_run += psum;
-    l_lse += xsum;
-    // P^T k-slots 8 gq + j: entry 4 gq + j (half 0) in the low 8 bytes,
-    // 16 + 4 gq + j (half 1) in the high 8 bytes
-    reinterpret_cast<uint2*>(&lds.p[own][lane])[mh] = uint2{p01, p23};
+    for (int j = 8; j < JA; ++j) issue_load(ta, buf, j);
+    __builtin_amdgcn_sched_barrier(0);
     // tile s + 1 has landed (tile s + 2 may still be in flight)
     wait_all_but_last();
-    lds_barrier();
-#pragma unroll
-    for (int q = 0; q < RT; ++q) pd[q] = __builtin_bit_cast(bf16x8, lds.p[q][lane]);
-    const uint16_t* kb = reinterpret_cast<const uint16_t*>(cur);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      // 4 (t ^ (q & 1)) = 4 t + 4 (q & 1) - 8 (t & 1) (q & 1)
-      const int off = voff + 4 * t - (t & 1) * 8 * (vq & 1);
-      const s16x4 lo = lds_read_tr16(kb + off);
-      const s16x4 hi = lds_read_tr16(kb + off + 16 * PP * 8);
-      const s16x8 b = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      if (t >= TD) {
-        vd[t - TD] = b;
-        continue;
-      }
-#pragma unroll
-      for (int q = 0; q < RT; ++q)
-        O[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), pd[q],
-                                                          O[q][t], 0, 0, 0);
-    }
+    lds_barrier();  // (2)
   };
-
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int q = 0; q < RT; ++q) {
+    for (int q = 0; q < RT; ++q)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) O[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      pd[q] = bf16x8{};
+      for (int t = 0; t < 8; ++t) O[q][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      const TileAddr t0 = tile_addr(0);
+#pragma unroll
+      for (int j = 0; j < JA; ++j) issue_load(t0, kb0, j);
+      const TileAddr t1 = tile_addr(1);
+#pragma unroll
+      for (int j = 0; j < JA; ++j) issue_load(t1, kb1, j);
     }
-#pragma unroll
-    for (int t = TD; t < 4; ++t) vd[t - TD] = s16x8{};
-    issue_tile(tile_addr(0), kb0);
-    issue_tile(tile_addr(1), kb1);
     wait_all_but_last();
     lds_barrier();
-    int s = 0;
-#pragma unroll 1
-    for (; s + 3 <= nsteps_run; s += 3) {
-      body(s, kb0, kb2);
-      body(s + 1, kb1, kb0);
-      body(s + 2, kb2, kb1);
+    if (n > 0) {
+      // tile 0: no O update yet; kb2 takes tile 2
+      const TileAddr ta = tile_addr(min(2, n + 1));
+      lds_barrier();
+#pragma unroll
+      for (int j = 0; j < JA; ++j) issue_load(ta, kb2, j);
+      wait_all_but_last();
+      lds_barrier();
     }
-    if (s < nsteps_run) body(s, kb0, kb2);
-    if (s + 1 < nsteps_run) body(s + 1, kb1, kb0);
-    deferred_o();
-    const float m_row = xor16_32_max(m_top);
-    if (gq == 0) lds.mx[wave][col] = m_row;
-    if (!__syncthreads_or(m_top > m_run + kHeadroom)) break;
-    m_run = fmaxf(m_row, lds.mx[twin][col]);
-    m_set = true;
-    l_run = 0.0f;
-    l_lse = 0.0f;
+    int s = 1;
+#pragma unroll 1
+    for (; s + 2 <= n; s += 3) {
+      obody(s, kb0);
+      obody(s + 1, kb1);
+      obody(s + 2, kb2);
+    }
+    if (s <= n) obody(s, kb0);
+    if (s + 1 <= n) obody(s + 1, kb1);
+    const bool again = __syncthreads_or(false);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // every load to LDS has landed
+    if (!again) break;
   }
-  // no load to LDS may still be in flight when the workgroup ends
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();  // the S waves' row statistics
 
-  // publish this wave's half of its row tile, then write channels 64 w.. of
-  // all RT row tiles
-  l_run = xor16_32_sum(l_run);
-  l_lse = xor16_32_sum(l_lse);
-  if (gq == 0) {
-    lds.ml[own][mh][col][0] = m_run;
-    lds.ml[own][mh][col][1] = l_run;
-    lds.ml[own][mh][col][2] = l_lse;
-  }
-  __syncthreads();
   const int R_ = a.rows.n_rows;
-  const bool swp = gq & 1;
 #pragma unroll
   for (int q = 0; q < RT; ++q) {
     const int qr = qrow0 + 16 * q + col;
     if (qr >= Mq) continue;
     const int set = qr / G, h = g * G + qr % G;
     const int64_t orow = ((int64_t)set * R_ + r) * a.hq + h;
-    const float m_r = lds.ml[q][0][col][0];
-    const float l_r = lds.ml[q][0][col][1] + lds.ml[q][1][col][1];
-    const float lx = lds.ml[q][0][col][2] + lds.ml[q][1][col][2];
-    const int c0 = wave * 64 + 16 * gq;
-    // channels c0 + 8 c2 + [0, 8): t = 2 c2 and 2 c2 + 1, swapped on odd gq
-    f32x4 o8[2][2];
+    const float m_r = lds.ml[q][col][0], l_r = lds.ml[q][col][1], lx = lds.ml[q][col][2];
+    const int c0 = b * 128 + 32 * gq;
+    // channels c0 + 8 c2 + [0, 8): t = 2 c2 and 2 c2 + 1
+    f32x4 o8[4][2];
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      o8[c2][0] = swp ? O[q][2 * c2 + 1] : O[q][2 * c2];
-      o8[c2][1] = swp ? O[q][2 * c2] : O[q][2 * c2 + 1];
+    for (int c2 = 0; c2 < 4; ++c2) {
+      o8[c2][0] = O[q][2 * c2];
+      o8[c2][1] = O[q][2 * c2 + 1];
     }
     if (a.n_split == 1) {
       float lse;
       const float inv = finish_row(m_r, l_r, lx, sink_log2(a, set, h), lse);
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
+      for (int c2 = 0; c2 < 4; ++c2) {
         const f32x4 v0 = o8[c2][0] * inv, v1 = o8[c2][1] * inv;
         float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         apply_gate(a, orow * DV + c0 + 8 * c2, v);
         store8(a, orow * DV + c0 + 8 * c2, v);
       }
-      if (a.lse && wave == 0 && gq == 0) a.lse[orow] = lse;
+      if (a.lse && b == 0 && gq == 0) a.lse[orow] = lse;
     } else {
       const int64_t nrows = (int64_t)a.n_qsets * R_ * a.hq;
       float* po = a.part + ((int64_t)sp * nrows + orow) * DV + c0;
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
+      for (int c2 = 0; c2 < 4; ++c2) {
         reinterpret_cast<f32x4*>(po + 8 * c2)[0] = o8[c2][0];
         reinterpret_cast<f32x4*>(po + 8 * c2)[1] = o8[c2][1];
       }
-      if (wave == 0 && gq == 0) {
+      if (b == 0 && gq == 0) {
         float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 3;
         ml[0] = m_r;
         ml[1] = l_r;
@@ -1685,13 +1718,13 @@ hipError_t launch_mla(const AttnArgs& a, hipStream_t s) {
 }
 
 template <int DQK>
-hipError_t launch_mla8(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_mla_ws(const AttnArgs& a, hipStream_t s) {
   const int G = a.hq / a.hkv;
   const int groups = (a.n_qsets * G + 16 * kMlaRT - 1) / (16 * kMlaRT);
   const int per = ((a.max_entries + a.n_split - 1) / a.n_split + kTile - 1) / kTile * kTile;
   const int n_units = a.n_split * a.rows.n_rows * a.hkv;
   const int64_t nwg = (int64_t)(n_units + 7) / 8 * 8 * groups;
-  hipLaunchKernelGGL((attn_mla8<DQK>), dim3((unsigned)nwg), dim3(512), 0, s, a, per, n_units, groups);
+  hipLaunchKernelGGL((attn_mla_ws<DQK>), dim3((unsigned)nwg), dim3(512), 0, s, a, per, n_units, groups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   const int64_t nrows = (int64_t)a.n_qsets * a.rows.n_rows * a.hq;
@@ -1752,7 +1785,7 @@ hipError_t launch_attn_gather(const AttnArgs& a, hipStream_t s) {
   }
   // Rows of 512 or more channels with at least 64 query rows per KV head:
   // the kernels that split S by channel halves across their waves, so each
-  // K fragment read from LDS feeds two MFMAs (attn_mla8 for bf16 rows,
+  // K fragment read from LDS feeds two MFMAs (attn_mla_ws for bf16 rows,
   // attn_mla for FP4 rows).
   const bool many_rows = a.n_qsets * (a.hq / a.hkv) >= 16 * kMlaRT;
   if (a.kv_kind == KV_SEPARATE) {
@@ -1760,11 +1793,11 @@ hipError_t launch_attn_gather(const AttnArgs& a, hipStream_t s) {
     if (a.dqk == 256 && a.dv == 256) return launch_shaped<256, 256, KV_SEPARATE, 2>(a, s);
   } else if (a.kv_kind == KV_SHARED) {
     if (a.dqk == 576 && a.dv == 512) {
-      if (many_rows) return launch_mla8<576>(a, s);
+      if (many_rows) return launch_mla_ws<576>(a, s);
       return launch_shaped<576, 512, KV_SHARED, 2>(a, s);
     }
     if (a.dqk == 512 && a.dv == 512) {
-      if (many_rows) return launch_mla8<512>(a, s);
+      if (many_rows) return launch_mla_ws<512>(a, s);
       return launch_shaped<512, 512, KV_SHARED, 2>(a, s);
     }
     if (a.dqk == 128 && a.dv == 128) return launch_shaped<128, 128, KV_SHARED, 2>(a, s);
