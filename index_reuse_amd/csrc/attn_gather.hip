@@ -1112,12 +1112,14 @@ __device__ __forceinline__ void lds_barrier() {
 // on eight waves, two per SIMD, split by role so that the two waves of a
 // SIMD are in different phases and one's VALU and LDS work overlaps the
 // other's MFMAs:
-//   - S waves a = 0..3, (hp, dh) = (a & 1, a >> 1): partial logits of row
-//     tiles {2 hp, 2 hp + 1} over all 32 entries and the k-steps of channel
-//     half dh (every K fragment read from LDS feeds two MFMAs); the halves
-//     swap one row tile's partials through LDS, and wave a finishes row tile
-//     2 hp + dh: mask, softmax, its P^T operand.  A wave owns whole rows of
-//     the tile, so the reference max needs no exchange between waves.
+//   - S waves a = 0..3, (mt, dh) = (a & 1, a >> 1): partial logits of all
+//     four row tiles over entry half mt of the 32-entry tile and the k-steps
+//     of channel half dh, so every K fragment read from LDS feeds four MFMAs
+//     and each tile is read from LDS once; the channel halves swap two row
+//     tiles' partials through LDS, and wave a finishes row tiles 2 dh and
+//     2 dh + 1 over its entry half: mask, softmax, its half of their P^T
+//     operands.  The two entry halves of a row agree on the reference max
+//     at tile 0 and add their probability sums at the end.
 //   - O waves b = 0..3: channels [128 b, 128 b + 128) of all four row tiles,
 //     and every load of the tiles.
 // Two barriers per tile.  Before the first, tile s's logits (S waves)
@@ -1136,9 +1138,11 @@ __device__ __forceinline__ void lds_barrier() {
 template <int DQK>
 struct MlaWsLds {
   static constexpr int SLOTS = kMaxEntries + 3 * kTile;
-  float sx[4][8][64];         // S partials handed to the other channel half
-  u32x4 p[kMlaRT][64];        // P^T operand of each row tile
-  float ml[kMlaRT][16][3];    // per row tile: m, rounded and unrounded sums
+  float sx[4][8][64];          // S partials handed to the other channel half
+  float sxo[4][8][64];         // at the reference tile: the partials a wave keeps
+  u32x4 p[kMlaRT][64];         // P^T operand of each row tile: 8 bytes per entry half
+  float mx[4][2][16];          // row max of a wave's two row tiles over its entry half
+  float ml[kMlaRT][2][16][3];  // per row tile and entry half: m, rounded and unrounded sums
   int32_t wfirst[8];
   int32_t slot[SLOTS];
 };
@@ -1179,111 +1183,139 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
   const int n = rt.nsteps_run;
   constexpr float kHeadroom = 64.0f;
 
+  // The first tile with an entry (n if none; the same in every wave) fixes
+  // the reference max of the softmax (see the S waves).
+  int s_first = 0;
+  while (s_first < n && __builtin_amdgcn_ballot_w64(lds.slot[s_first * kTile + (lane & 31)] >= 0) == 0)
+    ++s_first;
+
   if (wave < 4) {
     // ------------------------------------------------------------ S waves
-    const int hp = wave & 1, dh = wave >> 1;
-    const int own = 2 * hp + dh;   // row tile this wave finishes
-    const int partner = wave ^ 2;  // same row tiles, other channel half
-    u32x4 qv[2][KH];  // [0] row tile own, [1] own ^ 1; k-steps [KH dh, KH dh + KH)
+    // wave (mt, dh): entries [16 mt, 16 mt + 16) of every tile, k-steps
+    // [KH dh, KH dh + KH), all four row tiles (every K fragment read from
+    // LDS feeds four MFMAs); it finishes row tiles 2 dh and 2 dh + 1 over
+    // its entry half
+    const int mt = wave & 1, dh = wave >> 1;
+    const int partner = wave ^ 2;  // same entries, other channel half
+    const int twin = wave ^ 1;     // same row tiles, other entry half
+    // qv[j]: row tile (2 dh + j) mod 4, so that j = 0, 1 are the tiles this
+    // wave finishes and j = 2, 3 its partner's (static register indices)
+    u32x4 qv[RT][KH];
 #pragma unroll
-    for (int ht = 0; ht < 2; ++ht) {
-      const int qr = qrow0 + 16 * (ht == 0 ? own : own ^ 1) + col;
+    for (int j = 0; j < RT; ++j) {
+      const int qr = qrow0 + 16 * ((2 * dh + j) & 3) + col;
       if (qr < Mq) {
         const int set = qr / G, h = g * G + qr % G;
         const u32x4* qp = reinterpret_cast<const u32x4*>(
             reinterpret_cast<const uint16_t*>(a.q) +
             (((int64_t)set * a.rows.n_rows + r) * a.hq + h) * DQK + gq * (DQK / 4));
 #pragma unroll
-        for (int i = 0; i < KH; ++i) qv[ht][i] = qp[KH * dh + i];
+        for (int i = 0; i < KH; ++i) qv[j][i] = qp[KH * dh + i];
       } else {
 #pragma unroll
-        for (int i = 0; i < KH; ++i) qv[ht][i] = u32x4{0, 0, 0, 0};
+        for (int i = 0; i < KH; ++i) qv[j][i] = u32x4{0, 0, 0, 0};
       }
     }
 
-    // softmax state of row tile `own` (lane col), per lane over its entries;
-    // m_run is fixed by the first tile with an entry (see attn_mfma)
-    float m_run = -__builtin_huge_valf(), m_top = -__builtin_huge_valf();
-    float l_run = 0.0f, l_lse = 0.0f;
+    // softmax state of row tiles 2 dh + h (lane col) over entry half mt, per
+    // lane over its entries; m_run is shared with the twin
+    float m_run[2], m_top[2], l_run[2], l_lse[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      m_run[h] = -__builtin_huge_valf();
+      m_top[h] = -__builtin_huge_valf();
+      l_run[h] = 0.0f;
+      l_lse[h] = 0.0f;
+    }
     bool m_set = false;
 
     auto body = [&](int s, const u32x4* cur) __attribute__((always_inline)) {
-      // S^T partials [ht][mt]: entries 16 mt + (M), query rows of tile ht (N)
-      f32x4 acc[2][2];
+      // S^T partials [j]: entries 16 mt + (M), query rows of tile
+      // (2 dh + j) mod 4 (N)
+      f32x4 acc[RT];
 #pragma unroll
-      for (int ht = 0; ht < 2; ++ht)
+      for (int j = 0; j < RT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const u32x4* krow = cur + (16 * mt + col) * PP + gq * (P / 4) + KH * dh;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) acc[ht][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < KH; ++i) {
+        const u32x4 av = krow[i];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const u32x4* krow = cur + (16 * mt + col) * PP + gq * (P / 4) + KH * dh;
-#pragma unroll
-        for (int i = 0; i < KH; ++i) {
-          const u32x4 av = krow[i];
-#pragma unroll
-          for (int ht = 0; ht < 2; ++ht)
-            acc[ht][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, qv[ht][i]), acc[ht][mt], 0,
-                0, 0);
-        }
+        for (int j = 0; j < RT; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, qv[j][i]), acc[j], 0, 0, 0);
       }
+      // hand the partner the row tiles it finishes
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds.sx[wave][4 * mt + i][lane] = acc[1][mt][i];
+        for (int i = 0; i < 4; ++i) lds.sx[wave][4 * h + i][lane] = acc[2 + h][i];
+      const bool ref = !m_set && s == s_first;  // the same in every S wave
+      if (ref) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lds.sxo[wave][4 * h + i][lane] = acc[h][i];
+      }
       // every logit MFMA before the barrier: after it the O waves' MFMAs run
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();  // (1) the partials
       float x[2][4];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[mt][i] = acc[0][mt][i] + lds.sx[partner][4 * mt + i][lane];
+        for (int i = 0; i < 4; ++i) x[h][i] = acc[h][i] + lds.sx[partner][4 * h + i][lane];
       // keeps the reads out of a branch on the mask
       asm volatile("" : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[1][0]),
                    "+v"(x[1][1]), "+v"(x[1][2]), "+v"(x[1][3]));
-      // which of the tile's 32 entries are real: bit e (and e + 32) of the
-      // ballot over lanes e = lane & 31
-      const uint64_t valid = __builtin_amdgcn_ballot_w64(lds.slot[s * kTile + (lane & 31)] >= 0);
+      // which of the half's 16 entries are real: bit e of the ballot over
+      // lanes e = lane & 15
+      const uint64_t valid =
+          __builtin_amdgcn_ballot_w64(lds.slot[s * kTile + 16 * mt + (lane & 15)] >= 0);
       // mask and scale: lane holds entries 16 mt + 4 gq + i for query row col
-      float tmax = -__builtin_huge_valf();
+      float tmax[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int h = 0; h < 2; ++h) {
+        tmax[h] = -__builtin_huge_valf();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool ok = (valid >> (16 * mt + 4 * gq + i)) & 1;
-          x[mt][i] = ok ? x[mt][i] * a.scale_log2 : -__builtin_huge_valf();
-          tmax = fmaxf(tmax, x[mt][i]);
+          const bool ok = (valid >> (4 * gq + i)) & 1;
+          x[h][i] = ok ? x[h][i] * a.scale_log2 : -__builtin_huge_valf();
+          tmax[h] = fmaxf(tmax[h], x[h][i]);
         }
+        m_top[h] = fmaxf(m_top[h], tmax[h]);
       }
-      m_top = fmaxf(m_top, tmax);
-      // the first tile with an entry (the same in every lane) fixes the
-      // reference
-      if (!m_set && valid != 0) {
-        m_run = xor16_32_max(tmax);
+      if (ref) {
+        // this tile fixes the reference: the max of the row over both entry
+        // halves, the other half's logits summed from the twin's partials
+        // and its partner's
+        const uint64_t ovalid =
+            __builtin_amdgcn_ballot_w64(lds.slot[s * kTile + 16 * (1 - mt) + (lane & 15)] >= 0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float om = tmax[h];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float y = lds.sxo[twin][4 * h + i][lane] + lds.sx[twin ^ 2][4 * h + i][lane];
+            if ((ovalid >> (4 * gq + i)) & 1) om = fmaxf(om, y * a.scale_log2);
+          }
+          m_run[h] = xor16_32_max(om);
+        }
         m_set = true;
       }
-      const float m_use = m_run == -__builtin_huge_valf() ? 0.0f : m_run;
-      float pr[2][4];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int h = 0; h < 2; ++h) {
+        const float m_use = m_run[h] == -__builtin_huge_valf() ? 0.0f : m_run[h];
+        float pr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[mt][i] = fast_exp2(x[mt][i] - m_use);
-      // P^T as the B operand: k-slot 8 gq + i <-> entry (i < 4 ? 4 gq + i : 16 + 4 gq + i - 4)
-      u32x4 pa;
-      pa[0] = pack_bf16x2(pr[0][0], pr[0][1]);
-      pa[1] = pack_bf16x2(pr[0][2], pr[0][3]);
-      pa[2] = pack_bf16x2(pr[1][0], pr[1][1]);
-      pa[3] = pack_bf16x2(pr[1][2], pr[1][3]);
-      float psum = 0.0f, xsum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        psum += __uint_as_float(pa[i] << 16) + __uint_as_float(pa[i] & 0xFFFF0000u);
-        xsum += pr[i >> 1][2 * (i & 1)] + pr[i >> 1][2 * (i & 1) + 1];
+        for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(x[h][i] - m_use);
+        // P^T k-slots 8 gq + j: entry 4 gq + j (half 0) in the low 8 bytes,
+        // 16 + 4 gq + j (half 1) in the high 8 bytes
+        const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
+        l_run[h] += (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u)) +
+                    (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xFFFF0000u));
+        l_lse[h] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        reinterpret_cast<uint2*>(&lds.p[2 * dh + h][lane])[mt] = uint2{p01, p23};
       }
-      l_run += psum;
-      l_lse += xsum;
-      lds.p[own][lane] = pa;
       lds_barrier();  // (2) P^T of tile s; tile s + 1 has landed
     };
 
@@ -1303,19 +1335,31 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
         lds_barrier();
         lds_barrier();
       }
-      const float m_row = xor16_32_max(m_top);
-      if (!__syncthreads_or(m_top > m_run + kHeadroom)) break;
-      m_run = m_row;
+      float m_row[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        m_row[h] = xor16_32_max(m_top[h]);
+        if (gq == 0) lds.mx[wave][h][col] = m_row[h];
+      }
+      if (!__syncthreads_or(m_top[0] > m_run[0] + kHeadroom || m_top[1] > m_run[1] + kHeadroom))
+        break;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        m_run[h] = fmaxf(m_row[h], lds.mx[twin][h][col]);
+        l_run[h] = 0.0f;
+        l_lse[h] = 0.0f;
+      }
       m_set = true;
-      l_run = 0.0f;
-      l_lse = 0.0f;
     }
-    l_run = xor16_32_sum(l_run);
-    l_lse = xor16_32_sum(l_lse);
-    if (gq == 0) {
-      lds.ml[own][col][0] = m_run;
-      lds.ml[own][col][1] = l_run;
-      lds.ml[own][col][2] = l_lse;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      l_run[h] = xor16_32_sum(l_run[h]);
+      l_lse[h] = xor16_32_sum(l_lse[h]);
+      if (gq == 0) {
+        lds.ml[2 * dh + h][mt][col][0] = m_run[h];
+        lds.ml[2 * dh + h][mt][col][1] = l_run[h];
+        lds.ml[2 * dh + h][mt][col][2] = l_lse[h];
+      }
     }
     __syncthreads();
     return;
@@ -1451,7 +1495,9 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
     if (qr >= Mq) continue;
     const int set = qr / G, h = g * G + qr % G;
     const int64_t orow = ((int64_t)set * R_ + r) * a.hq + h;
-    const float m_r = lds.ml[q][col][0], l_r = lds.ml[q][col][1], lx = lds.ml[q][col][2];
+    const float m_r = lds.ml[q][0][col][0];
+    const float l_r = lds.ml[q][0][col][1] + lds.ml[q][1][col][1];
+    const float lx = lds.ml[q][0][col][2] + lds.ml[q][1][col][2];
     const int c0 = b * 128 + 32 * gq;
     // channels c0 + 8 c2 + [0, 8): t = 2 c2 and 2 c2 + 1
     f32x4 o8[4][2];

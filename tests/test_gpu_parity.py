@@ -253,6 +253,34 @@ def test_attention_peaked_logits(shape, gain, dev):
                     what="%s gain %g" % (shape, gain))
 
 
+@pytest.mark.parametrize("dqk", [576, 512])
+def test_attention_leading_padding(dqk, dev):
+    """Index lists whose first entries are padding (-1 inside the count, which
+    the format allows): the first tiles of a row hold no entry, so the
+    reference max of the softmax comes from a later tile; 64 query heads per
+    KV head, so the latent kernel with split waves runs."""
+    # 24 decode rows: several tiles per split, so the padding covers whole
+    # tiles at the start of a split, part of one, or whole splits
+    lens = (3000, 1500, 777, 2100) * 6
+    wl = synth.HYSPARSE2.replace(n_seqs=len(lens), seq_lens_override=lens, window=0, dqk=dqk,
+                                 dv=512, kv_mode="shared", hq=64, hkv=1, n_qsets=1)
+    prob = synth.make_problem(wl, device="cpu")
+    _flush("case leading padding dqk %d" % dqk)
+    p, step = _step(prob, dev)
+    sc = H.oracle_scores(prob, 0)
+    idx, cnt = H.oracle_select(prob, sc, wl.k)
+    idx = idx.copy()
+    lead = (40, 70, 100, 500, 0)
+    for r in range(idx.shape[0]):
+        m = min(lead[r % len(lead)], int(cnt[r]))
+        idx[r, :m] = -1
+    step.run_attention(idx=[torch.from_numpy(idx).to(dev)], count=[torch.from_numpy(cnt).to(dev)])
+    torch.cuda.synchronize()
+    o_ref, l_ref = H.oracle_attention(prob, 0, idx, cnt)
+    H.check_outputs(step.o[0], o_ref, step.lse[0], l_ref, torch.bfloat16,
+                    what="leading padding %d" % dqk)
+
+
 def test_dsa_rows_fp8_latent(dev):
     """DSA-shaped prefill rows (FP8 indexer 64x128, top-2048, latent 576 with
     V = first 512, 128 heads) on a 4096-token sequence; rows straddle the
