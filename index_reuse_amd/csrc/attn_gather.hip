@@ -1089,6 +1089,9 @@ __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, in
 }
 
 // ---------------------------------------- load-to-LDS helpers (gfx950)
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+
 typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
@@ -1236,13 +1239,27 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
 #pragma unroll
       for (int j = 0; j < RT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       const u32x4* krow = cur + (16 * mt + col) * PP + gq * (P / 4) + KH * dh;
+      // the slot of entry 16 mt + (lane & 15): whether it is real (read here,
+      // beside the K reads, rather than after the barrier)
+      const int slot_e = lds.slot[s * kTile + 16 * mt + (lane & 15)];
+      u32x4 kf[KH];
+#pragma unroll
+      for (int i = 0; i < KH; ++i) kf[i] = krow[i];
 #pragma unroll
       for (int i = 0; i < KH; ++i) {
-        const u32x4 av = krow[i];
 #pragma unroll
         for (int j = 0; j < RT; ++j)
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, qv[j][i]), acc[j], 0, 0, 0);
+              __builtin_bit_cast(bf16x8, kf[i]), __builtin_bit_cast(bf16x8, qv[j][i]), acc[j], 0, 0, 0);
+      }
+      // the slot and five K fragments ahead, then one more read after each
+      // fragment's MFMAs (left to itself the scheduler keeps only two reads
+      // ahead; all nine at once would not fit the registers)
+      __builtin_amdgcn_sched_group_barrier(0x0100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < KH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, RT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
       }
       // hand the partner the row tiles it finishes
 #pragma unroll
@@ -1269,8 +1286,8 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
                    "+v"(x[1][1]), "+v"(x[1][2]), "+v"(x[1][3]));
       // which of the half's 16 entries are real: bit e of the ballot over
       // lanes e = lane & 15
-      const uint64_t valid =
-          __builtin_amdgcn_ballot_w64(lds.slot[s * kTile + 16 * mt + (lane & 15)] >= 0);
+      const uint64_t valid = __builtin_amdgcn_ballot_w64(slot_e >= 0);
+      const uint32_t vbits = (uint32_t)valid >> (4 * gq);  // bit i: entry 16 mt + 4 gq + i
       // mask and scale: lane holds entries 16 mt + 4 gq + i for query row col
       float tmax[2];
 #pragma unroll
@@ -1278,7 +1295,7 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
         tmax[h] = -__builtin_huge_valf();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool ok = (valid >> (4 * gq + i)) & 1;
+          const bool ok = (vbits >> i) & 1;
           x[h][i] = ok ? x[h][i] * a.scale_log2 : -__builtin_huge_valf();
           tmax[h] = fmaxf(tmax[h], x[h][i]);
         }
@@ -1311,8 +1328,12 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
         // P^T k-slots 8 gq + j: entry 4 gq + j (half 0) in the low 8 bytes,
         // 16 + 4 gq + j (half 1) in the high 8 bytes
         const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
-        l_run[h] += (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u)) +
-                    (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xFFFF0000u));
+        // the rounded probabilities' sum (the weights P.V uses), by two
+        // bf16 dot products with (1, 1)
+        l_run[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p01), kOnes2, l_run[h],
+                                                   false);
+        l_run[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p23), kOnes2, l_run[h],
+                                                   false);
         l_lse[h] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
         reinterpret_cast<uint2*>(&lds.p[2 * dh + h][lane])[mt] = uint2{p01, p23};
       }
