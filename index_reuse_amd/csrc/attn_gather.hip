@@ -1452,7 +1452,9 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
     lds_barrier();  // (1) every wave is past its reads of buf
     // the MFMAs run between the two barriers, while the S waves do their
     // softmax (the scheduling barriers keep the compiler from moving them
-    // across either barrier); the loads go out among them
+    // across either barrier); the loads go out among them.  (Issuing half
+    // of them before the first barrier instead, into the buffer that nothing
+    // reads then, made the kernel a fifth slower.)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -1460,10 +1462,16 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
       for (int q = 0; q < RT; ++q)
         O[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[t]), pb[q],
                                                           O[q][t], 0, 0, 0);
-      if (t < JA) issue_load(ta, buf, t);
     }
 #pragma unroll
-    for (int j = 8; j < JA; ++j) issue_load(ta, buf, j);
+    for (int j = 0; j < JA; ++j) issue_load(ta, buf, j);
+    // one load after every three MFMAs: the load unit takes a 1 KB load in
+    // about the time of three, and a burst would hold the wave's MFMAs back
+#pragma unroll
+    for (int j = 0; j < JA; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x0008, 3, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);  // load
+    }
     __builtin_amdgcn_sched_barrier(0);
     // tile s + 1 has landed (tile s + 2 may still be in flight)
     wait_all_but_last();
