@@ -1518,6 +1518,59 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
   __syncthreads();  // the S waves' row statistics
 
   const int R_ = a.rows.n_rows;
+  if (a.n_split > 1) {
+    // Split partials (fp32) go out through a wave-private transpose in the
+    // tile buffers, which nothing uses any more: each store instruction
+    // then writes two rows' 512-byte runs of the wave's 128 channels,
+    // instead of 16-byte pieces of 16 rows (every workgroup of a split call
+    // writes its partials at about the same time, and the scattered pieces
+    // took a third of a short call).  Rows are padded by 16 bytes, so the
+    // 16 lanes of a write fall on distinct banks; one wave's LDS accesses
+    // run in order, so no barrier is needed.  (The same transpose for the
+    // final bf16 rows of an unsplit call made the long prefill calls
+    // slower.)
+    constexpr int SROW = 128 + 4;  // floats per staged row
+    static_assert(2 * 2 * 16 * SROW * 4 <= NJ * 64 * 16, "two waves' stages per tile buffer");
+    float* stage = reinterpret_cast<float*>(b < 2 ? kb0 : kb1) + (b & 1) * (2 * 16 * SROW);
+    const int64_t nrows = (int64_t)a.n_qsets * R_ * a.hq;
+#pragma unroll
+    for (int q = 0; q < RT; ++q) {
+      // the row statistics of the lane's row of tile q
+      const int qr = qrow0 + 16 * q + col;
+      if (qr < Mq && b == 0 && gq == 0) {
+        const int set = qr / G, h = g * G + qr % G;
+        const int64_t orow = ((int64_t)set * R_ + r) * a.hq + h;
+        float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 3;
+        ml[0] = lds.ml[q][0][col][0];
+        ml[1] = lds.ml[q][0][col][1] + lds.ml[q][1][col][1];
+        ml[2] = lds.ml[q][0][col][2] + lds.ml[q][1][col][2];
+      }
+    }
+#pragma unroll
+    for (int pq = 0; pq < RT / 2; ++pq) {
+      // row tiles 2 pq and 2 pq + 1: staged row 16 h + col holds channels
+      // [128 b, 128 b + 128) of row col of tile 2 pq + h
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          *reinterpret_cast<f32x4*>(&stage[(16 * h + col) * SROW + 32 * gq + 4 * t]) = O[2 * pq + h][t];
+      // lane l stores 4 channels of staged row 2 k + (l >> 5)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int sr = 2 * k + (lane >> 5);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&stage[sr * SROW + 4 * (lane & 31)]);
+        const int qr = qrow0 + 16 * (2 * pq + (sr >> 4)) + (sr & 15);
+        if (qr < Mq) {
+          const int set = qr / G, h = g * G + qr % G;
+          const int64_t orow = ((int64_t)set * R_ + r) * a.hq + h;
+          *reinterpret_cast<f32x4*>(a.part + ((int64_t)sp * nrows + orow) * DV + 128 * b +
+                                    4 * (lane & 31)) = v;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < RT; ++q) {
     const int qr = qrow0 + 16 * q + col;
