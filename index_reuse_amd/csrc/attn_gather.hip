@@ -1049,6 +1049,43 @@ __global__ __launch_bounds__(256, 1) void attn_mla(AttnArgs a, int per_split, in
   }
   __syncthreads();
   const int R_ = a.rows.n_rows;
+  if (a.n_split > 1) {
+    // Split partials leave through a wave-private transpose in the tile
+    // buffers, one row tile at a time (see attn_mla_ws): each store writes
+    // two rows' 512-byte runs of the wave's 128 channels.
+    constexpr int SROW = 128 + 4;  // floats per staged row
+    static_assert(4 * 16 * SROW * 4 <= sizeof(lds.k), "four waves' stages");
+    float* stage = reinterpret_cast<float*>(&lds.k[0][0]) + wave * (16 * SROW);
+    const int64_t nrows = (int64_t)a.n_qsets * R_ * a.hq;
+#pragma unroll
+    for (int q = 0; q < RT; ++q) {
+      const int qr = qrow0 + 16 * q + col;
+      if (qr < Mq && wave == 0 && gq == 0) {
+        const int set = qr / G, h = g * G + qr % G;
+        const int64_t orow = ((int64_t)set * R_ + r) * a.hq + h;
+        float* ml = a.part + (int64_t)a.n_split * nrows * DV + ((int64_t)sp * nrows + orow) * 3;
+        ml[0] = lds.ml[q][col][0];
+        ml[1] = lds.ml[q][col][1];
+        ml[2] = lds.ml[q][col][2];
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        *reinterpret_cast<f32x4*>(&stage[col * SROW + 32 * gq + 4 * t]) = O[q][t];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int sr = 2 * k + (lane >> 5);  // staged row: row sr of tile q
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&stage[sr * SROW + 4 * (lane & 31)]);
+        const int qs = qrow0 + 16 * q + sr;
+        if (qs < Mq) {
+          const int set = qs / G, h = g * G + qs % G;
+          const int64_t orow = ((int64_t)set * R_ + r) * a.hq + h;
+          *reinterpret_cast<f32x4*>(a.part + ((int64_t)sp * nrows + orow) * DV + 128 * wave +
+                                    4 * (lane & 31)) = v;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < RT; ++q) {
     const int qr = qrow0 + 16 * q + col;
