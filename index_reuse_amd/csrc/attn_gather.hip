@@ -1473,19 +1473,26 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
   const int voff = (4 * gq + ((lane >> 2) & 3)) * (PP * 8) + 128 * b + 32 * vq;
   // Tile s: O update of tile s - 1 from buf, which then takes tile s + 2
   // (the table ends at tile n + 1: the last pass reloads that one).
-  auto obody = [&](int s, u32x4* buf) __attribute__((always_inline)) {
-    const TileAddr ta = tile_addr(min(s + 2, n + 1));
-    bf16x8 pb[RT];
+  // V fragments of the tile being applied: the first half (t < 4) is read
+  // during the previous tile's MFMAs, in place of the half they have just
+  // consumed, the second half before the tile's first barrier, so the read
+  // phase (where the S waves read K) carries half the transpose reads.
+  s16x8 vf[8];
+  auto read_v = [&](const u32x4* src, int t0) __attribute__((always_inline)) {
+    const uint16_t* kb = reinterpret_cast<const uint16_t*>(src);
 #pragma unroll
-    for (int q = 0; q < RT; ++q) pb[q] = __builtin_bit_cast(bf16x8, lds.p[q][lane]);
-    const uint16_t* kb = reinterpret_cast<const uint16_t*>(buf);
-    s16x8 vf[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = t0; t < t0 + 4; ++t) {
       const s16x4 lo = lds_read_tr16(kb + voff + 4 * t);
       const s16x4 hi = lds_read_tr16(kb + voff + 4 * t + 16 * PP * 8);
       vf[t] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+  };
+  auto obody = [&](int s, u32x4* buf, const u32x4* nbuf) __attribute__((always_inline)) {
+    const TileAddr ta = tile_addr(min(s + 2, n + 1));
+    bf16x8 pb[RT];
+#pragma unroll
+    for (int q = 0; q < RT; ++q) pb[q] = __builtin_bit_cast(bf16x8, lds.p[q][lane]);
+    read_v(buf, 4);  // the second half of tile s - 1's V (the first came earlier)
     lds_barrier();  // (1) every wave is past its reads of buf
     // the MFMAs run between the two barriers, while the S waves do their
     // softmax (the scheduling barriers keep the compiler from moving them
@@ -1494,7 +1501,16 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
     // reads then, made the kernel a fifth slower.)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int q = 0; q < RT; ++q)
+        O[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[t]), pb[q],
+                                                          O[q][t], 0, 0, 0);
+    }
+    if constexpr (DQK != 512) __builtin_amdgcn_sched_barrier(0);
+    read_v(nbuf, 0);  // the first half of tile s's V, in place of what just went in
+#pragma unroll
+    for (int t = 4; t < 8; ++t) {
 #pragma unroll
       for (int q = 0; q < RT; ++q)
         O[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[t]), pb[q],
@@ -1502,12 +1518,29 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
     }
 #pragma unroll
     for (int j = 0; j < JA; ++j) issue_load(ta, buf, j);
-    // one load after every three MFMAs: the load unit takes a 1 KB load in
-    // about the time of three, and a burst would hold the wave's MFMAs back
+    // The loads go out among the MFMAs, about one after every three: the
+    // load unit takes a 1 KB load in about the time of three, and a burst
+    // would hold the wave's MFMAs back.  With 512-wide rows the next tile's
+    // V reads are paced among them too (with 576-wide rows that spilled).
+    if constexpr (DQK == 512) {
+      __builtin_amdgcn_sched_group_barrier(0x0008, 16, 0);
 #pragma unroll
-    for (int j = 0; j < JA; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x0008, 3, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);  // load
+      for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);  // load
+      }
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);  // load
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 3, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);  // load
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     // tile s + 1 has landed (tile s + 2 may still be in flight)
@@ -1533,6 +1566,7 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
       // tile 0: no O update yet; kb2 takes tile 2
       const TileAddr ta = tile_addr(min(2, n + 1));
       lds_barrier();
+      read_v(kb0, 0);
 #pragma unroll
       for (int j = 0; j < JA; ++j) issue_load(ta, kb2, j);
       wait_all_but_last();
@@ -1541,12 +1575,12 @@ __global__ __launch_bounds__(512, 1) void attn_mla_ws(AttnArgs a, int per_split,
     int s = 1;
 #pragma unroll 1
     for (; s + 2 <= n; s += 3) {
-      obody(s, kb0);
-      obody(s + 1, kb1);
-      obody(s + 2, kb2);
+      obody(s, kb0, kb1);
+      obody(s + 1, kb1, kb2);
+      obody(s + 2, kb2, kb0);
     }
-    if (s <= n) obody(s, kb0);
-    if (s + 1 <= n) obody(s + 1, kb1);
+    if (s <= n) obody(s, kb0, kb1);
+    if (s + 1 <= n) obody(s + 1, kb1, kb2);
     const bool again = __syncthreads_or(false);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // every load to LDS has landed
