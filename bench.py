@@ -140,12 +140,15 @@ def source_hash(fam: str) -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(fam: str, workload: str):
+def recorded_traffic(call: str, workload: str):
     """HBM bytes per call from the committed counter summary
     profiles/<call>_<workload>_traffic.txt (FETCH_SIZE and WRITE_SIZE per
     dispatch, each scaled by the same counter's reading for a plain copy of
-    known size), or None when absent or taken on other kernel sources."""
-    path = os.path.join(PROFILES, "%s_%s_traffic.txt" % (fam, workload))
+    known size), or None when absent or taken on other kernel sources.  The
+    file is named for the call itself (a workload's FA attention call is not
+    its sparse attention call), the source check for the call's family."""
+    fam = call_family(call)
+    path = os.path.join(PROFILES, "%s_%s_traffic.txt" % (call, workload))
     if not os.path.exists(path):
         return None
     rec = {}
@@ -625,7 +628,7 @@ def run_decode(args, wl, fa: bool = False):
     step0 = steps[0]
     queries = step0.prob.n_rows * sum(q.shape[0] for q in step0.prob.q)
     dom = max(per_call, key=per_call.get)
-    traffic = recorded_traffic(call_family(dom), wl.name)
+    traffic = recorded_traffic(dom, wl.name)
     bytes_dom = algorithmic_bytes(step0, dom)
     achieved = bytes_dom / (per_call[dom] * 1e-3) / 1e9
     kernels = {}
