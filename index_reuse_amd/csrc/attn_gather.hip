@@ -405,8 +405,18 @@ __device__ __forceinline__ void fill_window_steps(const AttnArgs& a, const RowIn
   __syncthreads();
 }
 
+// Waves per SIMD that attn_mfma's register budget must leave room for.
+// Separate 128-wide rows with a one-step ring fit three (at most 168
+// VGPRs), so two 6-wave workgroups share a CU and each hides the other's
+// fixed costs and load waits; the others take what they need.
+template <int DQK, int KV, int W, int NG, int D>
+constexpr int attn_mfma_waves() {
+  return (DQK == 128 && KV == KV_SEPARATE && W * NG == 6 && D == 1) ? 3 : 1;
+}
+
 template <int DQK, int DV, int KV, int W, int NG, int D>
-__global__ __launch_bounds__(64 * W * NG, 1) void attn_mfma(AttnArgs a, int per_split) {
+__global__ __launch_bounds__(64 * W * NG, (attn_mfma_waves<DQK, KV, W, NG, D>())) void attn_mfma(
+    AttnArgs a, int per_split) {
   constexpr int NTH = 64 * W * NG;
   using L = AttnLds<DQK, DV, KV, W, NG, D>;
   using T = TileRegs<DQK, DV, KV, NTH, NG>;
@@ -1935,7 +1945,9 @@ template <int DQK, int DV, int KV, int D>
 hipError_t launch_shaped(const AttnArgs& a, hipStream_t s) {
   const AttnShape sh = attn_shape(a);
   if (sh.w == 3 && sh.ng == 2) {
-    if constexpr (DQK == 128) return launch_mfma_attn<DQK, DV, KV, 3, 2, D>(a, s);
+    // separate rows: a one-step ring at two workgroups per CU (1-3% faster
+    // than two steps at one workgroup per CU, alone or with steps in flight)
+    if constexpr (DQK == 128) return launch_mfma_attn<DQK, DV, KV, 3, 2, KV == KV_SEPARATE ? 1 : D>(a, s);
   } else if (sh.ng == 1) {
     if constexpr (DQK >= 256) return launch_mfma_attn<DQK, DV, KV, 4, 1, D>(a, s);
   } else {
