@@ -1971,10 +1971,12 @@ void attn_plan(AttnArgs& a) {
   int ns = (a.max_entries + kMaxEntries - 1) / kMaxEntries;
   // wide value rows make split partials expensive: stop at about 64
   // workgroups, but take at least 4 splits (measured on 8 and 16 rows of 64
-  // heads over 512 entries), and up to one split per 512 entries of a long
-  // range (the partials then cost at most half the rows they replace)
+  // heads over 512 entries), and up to one split per 1024 entries of a long
+  // range (the partials then cost at most a quarter of the rows they
+  // replace; one split per 512 entries is 3% faster for a call alone, but
+  // its partial traffic costs 30% of the throughput with calls in flight)
   const int cap = a.dv >= 512
-                      ? (int)max(max((int64_t)4, (64 + base - 1) / base), (int64_t)a.max_entries / 512)
+                      ? (int)max(max((int64_t)4, (64 + base - 1) / base), (int64_t)a.max_entries / 1024)
                       : max_split;
   while (ns < max_split && ns < cap && ns < kMaxSplits && base * ns < 256) ++ns;
   a.n_split = ns < 1 ? 1 : ns;
