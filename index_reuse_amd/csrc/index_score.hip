@@ -110,7 +110,7 @@ __device__ __forceinline__ void mfma_tiles(const LaneSlice<DIM, true> (&q)[NMT],
 }
 
 // grid = (ceil(n_slots / (64*kWaves*gpw)), R); wave w scores gpw groups of 64
-// consecutive slots of row blockIdx.y (gpw even), 16 entries per MFMA tile.
+// consecutive slots of row blockIdx.y, 16 entries per MFMA tile.
 // The query slices and head weights are loaded once per wave; key rows
 // stream through a two-deep register pipeline (the next group's rows load
 // while the current group is scored).  Loads are unconditional, with the
@@ -657,18 +657,52 @@ hipError_t launch_prefill(const IndexArgs& a, int nmt, int n_blocks, hipStream_t
   return hipGetLastError();
 }
 
+// Workgroups of `kernel` (64 kWaves threads) that the whole GPU holds at
+// once: the occupancy the registers and LDS allow per CU, times the CUs.
+// Taken once per kernel (on the device current at the first call).
+int resident_workgroups(const void* kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kWaves, 0) != hipSuccess)
+    return 0;
+  return max(cus, 1) * max(per_cu, 1);
+}
+
+// Groups per wave: each wave scores gpw 64-entry groups, one after another,
+// so a launch takes about ceil(workgroups / resident) * gpw group times.
+// Take the gpw in [2, 16] that minimises that (ties: the larger gpw, whose
+// fewer workgroups load the queries fewer times).  A last partial round of
+// long waves is what this avoids: 1024 workgroups of 8 groups per wave
+// where 768 fit made the CSA2 Full indexer 103 against 94 us.
+int pick_gpw(int groups, int rows, int resident) {
+  if (resident <= 0) resident = 1024;
+  int best = 2;
+  int64_t best_cost = -1;
+  for (int gpw = 2; gpw <= 16; ++gpw) {
+    const int64_t wgs = (int64_t)((groups + gpw - 1) / gpw) * rows;
+    const int64_t cost = (wgs + resident - 1) / resident * gpw;
+    if (best_cost < 0 || cost <= best_cost) {
+      best = gpw;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 template <int NMT, int DIM, bool FP8>
 hipError_t launch_mfma(const IndexArgs& a, hipStream_t s) {
-  // Enough workgroups to cover the 256 CUs several times; long rows give each
-  // wave more 64-entry groups, so the query load is amortised over them.
   const int per_group = 64 * kWaves;
   const int groups = (a.n_slots + per_group - 1) / per_group;
-  int gpw = 2;
-  while (gpw < 16 && (int64_t)((groups + 2 * gpw - 1) / (2 * gpw)) * a.rows.n_rows >= 1024) gpw *= 2;
-  dim3 grid((groups + gpw - 1) / gpw, a.rows.n_rows);
   constexpr int rowb = DIM * (FP8 ? 1 : 2);
   constexpr bool stageable = rowb == 128 || rowb == 256;
   const bool staged = stageable && a.cand == nullptr && a.k.page_shift >= 6 && a.k.row_stride == rowb;
+  static const int resident_staged =
+      resident_workgroups(reinterpret_cast<const void*>(&index_score_mfma<NMT, DIM, FP8, stageable>));
+  static const int resident_plain =
+      resident_workgroups(reinterpret_cast<const void*>(&index_score_mfma<NMT, DIM, FP8, false>));
+  const int gpw = pick_gpw(groups, a.rows.n_rows, staged ? resident_staged : resident_plain);
+  dim3 grid((groups + gpw - 1) / gpw, a.rows.n_rows);
   if (staged)
     hipLaunchKernelGGL((index_score_mfma<NMT, DIM, FP8, stageable>), grid, dim3(64 * kWaves), 0, s, a, gpw);
   else
