@@ -103,3 +103,19 @@ def test_dense_crossover():
     dense = lambda L: 1152 * L
     assert abs(sparse(2048) / dense(2048) - 1.111) < 0.001
     assert abs(dense(4096) / sparse(4096) - 1.64) < 0.005
+
+
+def test_traffic_records_keyed_by_call(tmp_path, monkeypatch):
+    """A counter record belongs to the call it names: the FA workload's
+    dense attention call must not take the sparse attention call's record,
+    and a record taken on other kernel sources is not used."""
+    fam_hash = bench.source_hash("attn_gather_fwd")
+    rec = "# test record\nsource_sha256: %s\ntraffic_bytes: 1234\n" % fam_hash
+    (tmp_path / "attn_gather_fwd_hysparse2_traffic.txt").write_text(rec)
+    (tmp_path / "index_score_hysparse2_traffic.txt").write_text(
+        "source_sha256: 0000\ntraffic_bytes: 99\n")
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.recorded_traffic("attn_gather_fwd", "hysparse2") == 1234.0
+    assert bench.recorded_traffic("attn_gather_fwd_fa", "hysparse2") is None
+    assert bench.recorded_traffic("index_score", "hysparse2") is None
+    assert bench.recorded_traffic("attn_gather_fwd", "csa") is None
